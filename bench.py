@@ -1,0 +1,243 @@
+"""Throughput of the fused MoE-LoRA layer on one MI355X.
+
+One step = one full layer call (route, align, LoRA shrink, gate_up GEMM with
+LoRA expand + SwiGLU, LoRA shrink, down GEMM with LoRA expand, combine) over
+one batch of seeded synthetic inputs already resident in HBM.  Prints ONE JSON
+line.  The default workload is the GPT-OSS-20B-shaped decode layer
+(T=64, H=I=2880, 32 experts top-4, 8 LoRA adapters of rank 16, 25% tokens
+without LoRA); the prefill layer (T=4096, 32 adapters of rank 32) is measured
+beside it and reported under "prefill".
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import lora_expert_gemm_topk_amd as ml
+from lora_expert_gemm_topk_amd import moe_lora as mm
+from lora_expert_gemm_topk_amd import synth
+
+METRIC = "MoE-LoRA layer tokens/s (decode T=64, prefill T=4096); % HBM/MFMA roofline"
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # FLOP/s, MI355X dense bf16
+
+
+# ------------------------------------------------------------ work counting
+
+def work(shape: synth.LayerShape, ids: np.ndarray, adapter_ids: np.ndarray) -> dict:
+    """Algorithmic bytes and FLOPs of one layer call, counted from the actual
+    routing: only touched experts and touched (adapter, expert) LoRA bins."""
+    s = shape
+    es = 2 if s.dtype == synth.BF16 else 4
+    touched = np.unique(ids.reshape(-1))
+    ad = np.repeat(adapter_ids.astype(np.int64), s.Kp) if s.lora else np.full(ids.size, -1)
+    lora_pairs = ad >= 0
+    bins = np.unique(ad[lora_pairs] * s.Ep + ids.reshape(-1)[lora_pairs]) if s.lora else np.array([])
+    P, P_lora = ids.size, int(lora_pairs.sum())
+    w13 = 2 * s.I * s.H * es
+    w2 = s.H * s.I * es
+    a13, b13, a2, b2 = (s.r * s.H * es, 2 * s.I * s.r * es, s.r * s.I * es, s.H * s.r * es) if s.lora else (0,) * 4
+    act = s.T * s.H * es * 2 + s.T * s.E * 4 + s.T * 4
+    flops_gu = 2.0 * P * 2 * s.I * s.H + 2.0 * P_lora * 2 * s.I * s.r
+    flops_dn = 2.0 * P * s.H * s.I + 2.0 * P_lora * s.H * s.r
+    flops_sh = 2.0 * P_lora * s.r * (s.H + s.I)
+    return dict(
+        experts=int(touched.size), bins=int(bins.size), P=P, P_lora=P_lora,
+        bytes_layer=float(touched.size * (w13 + w2) + bins.size * (a13 + b13 + a2 + b2) + act),
+        flops_layer=flops_gu + flops_dn + flops_sh,
+        bytes_gate_up=float(touched.size * w13 + bins.size * b13 + s.T * s.H * es),
+        flops_gate_up=flops_gu,
+        bytes_down=float(touched.size * w2 + bins.size * b2),
+        flops_down=flops_dn,
+    )
+
+
+# ------------------------------------------------------------ stage timing
+
+class StageEvents:
+    """2 x 7 HIP events per step, recorded by the library around each stage
+    on the stream the kernels run on."""
+
+    def __init__(self, steps: int):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        n = 2 * len(mm.STAGES)
+        self.arrays = []
+        for _ in range(steps):
+            arr = (ctypes.c_void_p * n)()
+            for i in range(n):
+                ev = ctypes.c_void_p()
+                rc = self.hip.hipEventCreate(ctypes.byref(ev))
+                if rc != 0:
+                    raise RuntimeError(f"hipEventCreate failed: {rc}")
+                arr[i] = ev
+            self.arrays.append(arr)
+
+    def stage_ms(self) -> dict:
+        out = {name: [] for name in mm.STAGES}
+        f = ctypes.c_float()
+        for arr in self.arrays:
+            for s, name in enumerate(mm.STAGES):
+                rc = self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(arr[2 * s]),
+                                                  ctypes.c_void_p(arr[2 * s + 1]))
+                if rc != 0:
+                    raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+                out[name].append(f.value)
+        return {k: float(np.mean(v)) for k, v in out.items()}
+
+    def close(self):
+        for arr in self.arrays:
+            for ev in arr:
+                self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+# ------------------------------------------------------------ measurement
+
+def measure(name: str, steps: int, warmup: int, seed: int = 0) -> dict:
+    shape, recipe = synth.workload(name)
+    inp = synth.make_inputs(shape, recipe, seed=seed, device="cuda")
+    dev = inp.x.device
+    out = torch.empty((shape.T, shape.H), dtype=inp.x.dtype, device=dev)
+    ws = ml.Workspace()
+    ids = torch.empty((shape.T, shape.Kp), dtype=torch.int32, device=dev)
+    wts = torch.empty((shape.T, shape.Kp), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        ml.forward_inputs(inp, out=out, workspace=ws, routing_out=(ids, wts), stage_events=ev)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+
+    # second timed pass with per-stage HIP events (kernel durations)
+    se = StageEvents(steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(se.arrays[i])
+    torch.cuda.synchronize()
+    stage = se.stage_ms()
+    se.close()
+
+    wk = work(shape, ids.cpu().numpy(), inp.adapter_ids.cpu().numpy())
+    plan = ml.moe_lora_plan_query(ml.make_dims(shape.T, shape.H, shape.I, shape.E, shape.K, shape.S, shape.L,
+                                               shape.r, shape.rsf, shape.renormalize, shape.dtype))
+    return dict(name=name, shape=shape, inp=inp, ms=ms, stage=stage, work=wk, plan=plan)
+
+
+def roofline_obj(m: dict, bound: str) -> dict:
+    st = m["stage"]["gate_up"] * 1e-3
+    if bound == "hbm":
+        ach = m["work"]["bytes_gate_up"] / st
+        return {"kernel": "gemm_stream gate_up (+LoRA expand13, SwiGLU)", "bound": "hbm",
+                "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": ach / HBM_PEAK,
+                "traffic": None, "kernel_us": st * 1e6,
+                "algorithmic_bytes": m["work"]["bytes_gate_up"]}
+    ach = m["work"]["flops_gate_up"] / st
+    return {"kernel": "gemm_stream gate_up (+LoRA expand13, SwiGLU)", "bound": "mfma",
+            "achieved": ach / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK,
+            "traffic": None, "kernel_us": st * 1e6, "algorithmic_flops": m["work"]["flops_gate_up"]}
+
+
+def layer_roofline(m: dict) -> dict:
+    wk = m["work"]
+    t = m["ms"] * 1e-3
+    t_roof = max(wk["bytes_layer"] / HBM_PEAK, wk["flops_layer"] / MFMA_BF16_PEAK)
+    return {"bytes": wk["bytes_layer"], "flops": wk["flops_layer"],
+            "hbm_frac": wk["bytes_layer"] / t / HBM_PEAK, "mfma_frac": wk["flops_layer"] / t / MFMA_BF16_PEAK,
+            "roofline_us": t_roof * 1e6, "frac_of_roofline": t_roof / t}
+
+
+def cpu_baseline(m: dict, budget_tokens: int) -> dict:
+    import oracle
+    s = m["shape"]
+    host = m["inp"].to("cpu")
+    n = min(s.T, budget_tokens)
+    tokens = np.arange(n)
+    threads = min(os.cpu_count() or 1, 16)
+    t0 = time.perf_counter()
+    oracle.forward_inputs(host, tokens=tokens, nthreads=threads)
+    wall = time.perf_counter() - t0
+    return {"value": n / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {s.T} tokens of one {m['name']} layer call (fp64 oracle, OpenMP)",
+            "wall_s": wall}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gptoss_decode_T64")
+    ap.add_argument("--prefill", default="gptoss_prefill_T4096", help="secondary workload ('' to skip)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this layer is built and measured on one GPU only; "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    m = measure(args.workload, args.steps, args.warmup)
+    s = m["shape"]
+    result = {
+        "metric": METRIC,
+        "value": s.T / (m["ms"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded)",
+        "config": {"workload": args.workload, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "K": s.K, "S": s.S,
+                   "L": s.L, "r": s.r, "block_m": m["plan"]["block_m"], "split_k": m["plan"]["split_k"]},
+        "roofline": roofline_obj(m, "hbm"),
+        "layer": layer_roofline(m),
+        "stage_us": {k: v * 1e3 for k, v in m["stage"].items()},
+        "work": m["work"],
+    }
+    if not args.no_cpu:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(m, args.cpu_tokens)
+    else:
+        result["cpu_baseline"] = None
+    del m
+    torch.cuda.empty_cache()
+    if args.prefill:
+        print(f"bench: {args.prefill}", file=sys.stderr, flush=True)
+        p = measure(args.prefill, max(5, args.steps // 5), max(2, args.warmup // 5))
+        ps = p["shape"]
+        result["prefill"] = {"workload": args.prefill, "tokens_per_s": ps.T / (p["ms"] * 1e-3),
+                             "ms_per_step": p["ms"], "roofline": roofline_obj(p, "mfma"),
+                             "layer": layer_roofline(p), "stage_us": {k: v * 1e3 for k, v in p["stage"].items()},
+                             "block_m": p["plan"]["block_m"]}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,205 @@
+/*
+ * moe_lora.h -- C ABI of the fused MoE-LoRA layer for MI355X (gfx950).
+ *
+ * One layer call computes, for T tokens with hidden size H:
+ *   1. top-K routing over E routed experts from fp32 router logits, softmax
+ *      weights over the selected logits, and S always-on shared experts
+ *      appended as extra slots after the routed ones (ids E..E+S-1, weight
+ *      1/routed_scaling_factor)                           [moe_lora_route]
+ *   2. alignment of the T*(K+S) (token, slot) pairs by expert over the
+ *      E+S stacked w13 rows, padded per expert to the GEMM block, with the
+ *      pairs of each expert grouped by adapter           [moe_lora_align]
+ *   3. per pair: g = W13[e] x (+ B13[a,e] A13[a,e] x), h = silu(g_gate) *
+ *      g_up, y = W2[e] h (+ B2[a,e] A2[a,e] h), and out = rsf * sum_j w_j y_j
+ *                                                       [moe_lora_forward]
+ * Sources of the method:
+ *   - aitrends.kr summary of the AWS post on multi-LoRA serving of MoE
+ *     models in vLLM, "section details": routing and adapter choice are two
+ *     sparsities at once; LoRA shrink and expand are fused into every expert
+ *     projection; layers without LoRA exit at once; skinny LoRA products use
+ *     split-K; the LoRA sum is folded into the expand step.  "Image
+ *     analysis", diagram: an adapter path on gate_up and on down.
+ *   - secrett2633 analysis of vLLM PR 46545 ("vLLM ROCm shared-expert
+ *     fusion"), "code analysis" parts 1-2: shared slots appended after the
+ *     routed top-k with ids from the routed expert count upward and one
+ *     constant weight; the alignment expert count is the number of stacked
+ *     w13 rows.  "Lessons" item 2: that weight is 1/routed_scaling_factor.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous,
+ *     16-byte aligned.  The caller owns every buffer; the library never
+ *     allocates or frees device memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; no call synchronises the host or copies device data back,
+ *     so a call can be captured into a HIP graph.  Inputs must stay alive
+ *     until the stream reaches the call.
+ *   - Return value: MOE_LORA_OK, or a negative code below.  Nothing is
+ *     enqueued when argument checking fails.  Preconditions NOT checked on
+ *     the device: router logits are finite; adapter ids lie in [-1, L).
+ *   - T may be 0: the call is a no-op returning MOE_LORA_OK.
+ *   - Concurrent calls are safe when they use distinct workspaces.
+ */
+#ifndef MOE_LORA_H
+#define MOE_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_LORA_OK 0
+#define MOE_LORA_EINVAL (-1)       /* null pointer, bad size, K > E, rsf <= 0, misaligned pointer */
+#define MOE_LORA_EUNSUPPORTED (-2) /* dtype, H or I not a multiple of 8, limits below exceeded */
+#define MOE_LORA_EWORKSPACE (-3)   /* workspace smaller than moe_lora_workspace_bytes() */
+#define MOE_LORA_EHIP (-4)         /* a HIP launch failed; moe_lora_strerror() has the text */
+
+#define MOE_LORA_F32 0
+#define MOE_LORA_BF16 1
+
+/* Stages of moe_lora_forward, in launch order (for moe_lora_args.stage_events). */
+#define MOE_LORA_STAGE_ROUTE 0
+#define MOE_LORA_STAGE_ALIGN 1
+#define MOE_LORA_STAGE_SHRINK13 2
+#define MOE_LORA_STAGE_GATE_UP 3
+#define MOE_LORA_STAGE_SHRINK2 4
+#define MOE_LORA_STAGE_DOWN 5
+#define MOE_LORA_STAGE_COMBINE 6
+#define MOE_LORA_NUM_STAGES 7
+
+/* Sizes and knobs of one layer call.
+ *   T  tokens (>= 0)             H  hidden size (multiple of 8)
+ *   I  expert intermediate size (multiple of 8); w13 holds 2I rows: gate
+ *      rows [0, I) then up rows [I, 2I)
+ *   E  routed experts (1..1024)  K  routed top-k (1..min(E, 64))
+ *   S  shared experts appended as slots K..K+S-1 (0..64)
+ *   L  LoRA adapters (>= 0)      r  LoRA rank (0..128); LoRA is active iff
+ *      L > 0 and r > 0
+ *   routed_scaling_factor  rsf > 0: shared slots get weight 1/rsf (fp32
+ *      division) and the whole combine is multiplied by rsf
+ *   renormalize  1: softmax over the K selected logits; 0: softmax over all
+ *      E logits, taken at the K selected ones
+ *   dtype  MOE_LORA_BF16 (bf16 tensors, fp32 accumulation) or MOE_LORA_F32
+ *   block_m  rows per expert block of the alignment and the GEMM tiles;
+ *      0 = library choice from the average rows per expert, else 16, 32 or 64
+ *   lora_block_m  rows per LoRA shrink work item; 0 = library choice, else
+ *      16 or 32 (32 needs r <= 64)
+ *   split_k  K-splits of the LoRA shrink; 0 = library choice, else 1..16
+ * Limits: (E+S) * (La+1) <= 16384 where La = L if LoRA is active else 0;
+ *   L <= 1024; T*(K+S) < 2^31 - 1. */
+typedef struct moe_lora_dims {
+    int64_t T, H, I, E, K, S, L, r;
+    float routed_scaling_factor;
+    int32_t renormalize;
+    int32_t dtype;
+    int32_t block_m;
+    int32_t lora_block_m;
+    int32_t split_k;
+} moe_lora_dims;
+
+/* What the library will do for a given moe_lora_dims (filled by
+ * moe_lora_plan_query).  block_m / lora_block_m / max_blocks /
+ * sorted_capacity / max_items also size the outputs of moe_lora_align. */
+typedef struct moe_lora_plan {
+    int32_t block_m;         /* expert block rows used by align and the GEMMs */
+    int32_t lora_block_m;    /* rows per LoRA work item */
+    int32_t split_k;         /* LoRA shrink K-splits */
+    int32_t gemm_kind;       /* 0 = fp32 path, 1 = bf16 streaming, 2 = bf16 LDS-tiled */
+    int64_t max_blocks;      /* ceil(P/block_m) + min(E+S, P), P = T*(K+S) */
+    int64_t sorted_capacity; /* max_blocks * block_m */
+    int64_t max_items;       /* ceil(P/lora_block_m) + min(P, L*(E+S)); 0 without LoRA */
+    size_t workspace_bytes;       /* for moe_lora_forward */
+    size_t align_workspace_bytes; /* for moe_lora_align */
+} moe_lora_plan;
+
+/* Device buffers of one layer call.
+ *   hidden [T,H] dtype;  router_logits [T,E] f32;  adapter_ids [T] i32
+ *     (-1 = no LoRA for that token; may be NULL when LoRA is inactive)
+ *   w13 [E+S, 2I, H] dtype;  w2 [E+S, H, I] dtype
+ *   a13 [L, E+S, r, H];  b13 [L, E+S, 2I, r];  a2 [L, E+S, r, I];
+ *   b2 [L, E+S, H, r]   (dtype; may all be NULL when LoRA is inactive)
+ *   out [T, H] dtype (written)
+ *   workspace: device scratch of at least moe_lora_workspace_bytes(),
+ *     256-byte aligned; contents on entry do not matter
+ *   topk_ids_out [T, K+S] i32, topk_weights_out [T, K+S] f32: optional
+ *     (NULL = not written) copies of the routing decisions
+ *   stage_events: optional (NULL = none) array of 2*MOE_LORA_NUM_STAGES
+ *     hipEvent_t handles created by the caller; the call records
+ *     stage_events[2s] on `stream` right before stage s and
+ *     stage_events[2s+1] right after it (both back to back for a stage that
+ *     launches nothing), so the caller can time each kernel on the stream it
+ *     runs on.  Stages: see MOE_LORA_STAGE_*. */
+typedef struct moe_lora_args {
+    const void *hidden;
+    const float *router_logits;
+    const int32_t *adapter_ids;
+    const void *w13;
+    const void *w2;
+    const void *a13;
+    const void *b13;
+    const void *a2;
+    const void *b2;
+    void *out;
+    void *workspace;
+    size_t workspace_bytes;
+    int32_t *topk_ids_out;
+    float *topk_weights_out;
+    void **stage_events;
+} moe_lora_args;
+
+/* Validate dims and describe the plan.  Pure host code: touches no device
+ * and may be called on a machine without a GPU.  Returns MOE_LORA_OK,
+ * MOE_LORA_EINVAL or MOE_LORA_EUNSUPPORTED; `plan` is written only on OK. */
+int moe_lora_plan_query(const moe_lora_dims *dims, moe_lora_plan *plan);
+
+/* Workspace bytes moe_lora_forward needs for `dims`; 0 when dims are
+ * invalid.  Pure host code. */
+size_t moe_lora_workspace_bytes(const moe_lora_dims *dims);
+
+/* Full argument check of a moe_lora_forward call (null pointers, sizes,
+ * alignment, workspace size).  Pure host code: dereferences no pointer and
+ * touches no device. */
+int moe_lora_check_args(const moe_lora_dims *dims, const moe_lora_args *args);
+
+/* Step 1 alone: top-K routing plus shared-slot append.
+ *   logits [T,E] f32 in; topk_ids [T,K+S] i32 and topk_weights [T,K+S] f32
+ *   out.  Selection order: larger logit first, lower expert index on an
+ *   exact tie (+0 == -0); slot order = selection order.  Weights: fp64
+ *   softmax rounded once to fp32.  Only T, E, K, S, routed_scaling_factor
+ *   and renormalize of `dims` are read. */
+int moe_lora_route(const moe_lora_dims *dims, const float *logits, int32_t *topk_ids,
+                   float *topk_weights, void *stream);
+
+/* Step 2 alone: alignment of the pairs f = t*(K+S) + j by expert.
+ *   topk_ids [T,K+S] i32 in (values in [0, E+S)); adapter_ids [T] i32 in
+ *   (ignored when LoRA is inactive).
+ *   sorted_ids [sorted_capacity]: pairs of expert 0, then expert 1, ...;
+ *     inside an expert ordered by adapter (no-LoRA first) then by f; each
+ *     expert group padded to a multiple of block_m with the sentinel
+ *     P = T*(K+S); the tail after num_post_pad also holds P.
+ *   block_expert [max_blocks]: expert of each block_m-row block, -1 after
+ *     the last used block.
+ *   num_post_pad [1]: padded row count.
+ *   lora_items [max_items][4] (start row, rows, adapter, expert): the
+ *     (adapter >= 0, expert) runs of sorted_ids in key order, cut into pieces
+ *     of at most lora_block_m rows; tail (0, 0, -1, -1).  May be NULL when
+ *     LoRA is inactive.  num_items [1]: item count (may be NULL likewise).
+ *   workspace: at least align_workspace_bytes of the plan. */
+int moe_lora_align(const moe_lora_dims *dims, const int32_t *topk_ids, const int32_t *adapter_ids,
+                   int32_t *sorted_ids, int32_t *block_expert, int32_t *num_post_pad,
+                   int32_t *lora_items, int32_t *num_items, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* The whole layer (steps 1-3), enqueued on `stream`. */
+int moe_lora_forward(const moe_lora_dims *dims, const moe_lora_args *args, void *stream);
+
+/* Text for a return code.  For MOE_LORA_EHIP it includes the HIP error of
+ * the failing call on this thread.  Never NULL. */
+const char *moe_lora_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LORA_H */

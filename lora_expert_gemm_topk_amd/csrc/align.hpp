@@ -1,0 +1,281 @@
+// Expert/adapter alignment of the (token, slot) pairs.
+//
+// The grouped GEMMs need the pairs of each expert contiguous and padded to
+// the expert block size; the alignment expert count is the number of
+// stacked w13 rows, shared experts included (secrett2633 analysis of vLLM
+// PR 46545, "code analysis" part 2).  The LoRA shrink/expand needs, in
+// addition, the pairs of one (adapter, expert) bin contiguous (aitrends.kr
+// summary of the AWS multi-LoRA MoE post, "section details": expert routing
+// and adapter choice are two sparsities at once).  Both come out of one
+// layout: pairs sorted by (expert, adapter+1, pair index), padded per expert.
+//
+// Layout produced (the contract with the GEMM and shrink kernels):
+//   sorted_ids[cap]         pair index f, or the sentinel P in the padding
+//   block_expert[maxb]      expert of each block of bm rows, -1 after the end
+//   *npp_out                padded row count (num_post_pad)
+//   *nitems_out             LoRA work item count
+//   items[max_items][4]     (start row, rows <= lbm, adapter, expert)
+//
+// Implementation: one workgroup of NW wavefronts, no host synchronisation
+// and no atomics on anything but LDS integer counters.  A stable sort by a
+// composite key is done as two stable counting passes (least significant
+// key first): by adapter+1 into `tmp`, then by expert into sorted_ids.  Each
+// pass gives every wave a contiguous segment of the input; a wave walks its
+// segment 64 pairs at a time in order, finds equal keys inside the wave with
+// bit-sliced ballots, and keeps one running cursor per key in LDS.  Per-wave
+// histograms plus a scan over (key, wave) make every position depend only on
+// the input, so the result is deterministic and stable.
+#pragma once
+
+#include "common.hpp"
+
+namespace moelora {
+
+struct AlignParams {
+    const int32_t *topk_ids;
+    const int32_t *adapter_ids;
+    int32_t *sorted_ids;
+    int32_t *block_expert;
+    int32_t *npp_out;
+    int32_t *nitems_out;
+    int32_t *items;
+    int32_t *tmp;
+    int P, Kp, Ep, La, bm, lbm;
+    int cap, max_blocks, max_items;
+    int nbits_a, nbits_e;
+};
+
+// Ids outside their documented ranges (a precondition) are clamped so that
+// they can never index memory out of bounds: an adapter outside [-1, La)
+// counts as "no LoRA", an expert outside [0, Ep) as the nearest valid one.
+__device__ __forceinline__ int adapter_key(const AlignParams &p, int f) {
+    const int a = p.adapter_ids[f / p.Kp];
+    return (a >= 0 && a < p.La) ? a + 1 : 0;
+}
+__device__ __forceinline__ int expert_of(const AlignParams &p, int f) {
+    return min(max(p.topk_ids[f], 0), p.Ep - 1);
+}
+
+// LDS ints used by align_kernel for a given shape and wave count.
+__host__ __device__ inline int64_t align_lds_ints(int NW, int Ep, int La) {
+    const int64_t nk = (int64_t)Ep * (La + 1);
+    const int64_t tk = (Ep > La + 1 ? Ep : La + 1) + 1;
+    int64_t n = (int64_t)NW * (La + 1) + (int64_t)NW * Ep + 2 * (int64_t)Ep + 1 + tk + 80;
+    if (La > 0) n += 2 * nk + 1;
+    return n;
+}
+
+// In-place exclusive scan of arr[0, n) in LDS by the whole workgroup.
+// Returns the total to every thread.  scr holds >= 17 ints.
+__device__ inline int block_excl_scan(int *arr, int n, int *scr) {
+    const int nt = (int)blockDim.x, tid = (int)threadIdx.x;
+    const int nw = nt >> 6, lane = tid & 63, w = tid >> 6;
+    const int per = (n + nt - 1) / nt;
+    const int b = tid * per;
+    const int e = min(n, b + per);
+    int local = 0;
+    for (int i = b; i < e; ++i) local += arr[i];
+    int x = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) scr[w] = x;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < nw; ++i) {
+            const int t = scr[i];
+            scr[i] = run;
+            run += t;
+        }
+        scr[nw] = run;
+    }
+    __syncthreads();
+    int run = scr[w] + x - local;
+    const int total = scr[nw];
+    for (int i = b; i < e; ++i) {
+        const int t = arr[i];
+        arr[i] = run;
+        run += t;
+    }
+    __syncthreads();
+    return total;
+}
+
+__global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
+    extern __shared__ int lds[];
+    const int NW = (int)(blockDim.x >> 6);
+    const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int La = p.La, Ep = p.Ep, A1 = La + 1;
+    const int NK = Ep * A1;
+    const int TK = (Ep > A1 ? Ep : A1) + 1;
+
+    int *histA = lds;                    // [NW][A1]
+    int *histB = histA + NW * A1;        // [NW][Ep]
+    int *offE = histB + NW * Ep;         // [Ep+1]
+    int *totE = offE + Ep + 1;           // [Ep]
+    int *tk = totE + Ep;                 // [TK]
+    int *scr = tk + TK;                  // [80]
+    int *cnt2 = scr + 80;                // [NK]      (La > 0)
+    int *itemOff = cnt2 + NK;            // [NK+1]    (La > 0)
+
+    const int nzero = NW * A1 + NW * Ep + (La > 0 ? NK : 0);
+    for (int i = tid; i < nzero; i += nt) {
+        if (i < NW * A1 + NW * Ep) lds[i] = 0;
+        else cnt2[i - NW * A1 - NW * Ep] = 0;
+    }
+    __syncthreads();
+
+    const int P = p.P;
+    const int seg = (P + NW - 1) / NW;
+    const int s0 = min(P, w * seg), s1 = min(P, s0 + seg);
+
+    // ---- pass A: stable counting sort by adapter+1 into tmp ------------
+    if (La > 0) {
+        for (int base = s0; base < s1; base += 64) {
+            const int f = base + lane;
+            const bool valid = f < s1;
+            const int a1 = valid ? adapter_key(p, f) : 0;
+            const uint64_t m = match_key((uint32_t)a1, valid, p.nbits_a);
+            if (valid) {
+                if ((m & lanemask_lt()) == 0) histA[w * A1 + a1] += __popcll(m);
+                atomicAdd(&cnt2[expert_of(p, f) * A1 + a1], 1);
+            }
+        }
+        __syncthreads();
+        for (int a = tid; a < A1; a += nt) {
+            int run = 0;
+            for (int v = 0; v < NW; ++v) {
+                const int c = histA[v * A1 + a];
+                histA[v * A1 + a] = run;
+                run += c;
+            }
+            tk[a] = run;
+        }
+        __syncthreads();
+        block_excl_scan(tk, A1, scr);
+        for (int i = tid; i < NW * A1; i += nt) histA[i] += tk[i % A1];
+        __syncthreads();
+        for (int base = s0; base < s1; base += 64) {
+            const int f = base + lane;
+            const bool valid = f < s1;
+            const int a1 = valid ? adapter_key(p, f) : 0;
+            const uint64_t m = match_key((uint32_t)a1, valid, p.nbits_a);
+            if (valid) {
+                const int pos = histA[w * A1 + a1] + __popcll(m & lanemask_lt());
+                p.tmp[pos] = f;
+                if ((m & lanemask_lt()) == 0) histA[w * A1 + a1] += __popcll(m);
+            }
+        }
+        __threadfence_block();
+        __syncthreads();
+    }
+
+    // ---- pass B: stable counting sort by expert, padded per expert --------
+    for (int base = s0; base < s1; base += 64) {
+        const int i = base + lane;
+        const bool valid = i < s1;
+        const int f = valid ? (La > 0 ? p.tmp[i] : i) : 0;
+        const int e = valid ? expert_of(p, f) : 0;
+        const uint64_t m = match_key((uint32_t)e, valid, p.nbits_e);
+        if (valid && (m & lanemask_lt()) == 0) histB[w * Ep + e] += __popcll(m);
+    }
+    __syncthreads();
+    for (int e = tid; e < Ep; e += nt) {
+        int run = 0;
+        for (int v = 0; v < NW; ++v) {
+            const int c = histB[v * Ep + e];
+            histB[v * Ep + e] = run;
+            run += c;
+        }
+        totE[e] = run;
+        tk[e] = (run + p.bm - 1) / p.bm * p.bm;
+    }
+    __syncthreads();
+    const int npp = block_excl_scan(tk, Ep, scr);
+    for (int e = tid; e < Ep; e += nt) offE[e] = tk[e];
+    if (tid == 0) offE[Ep] = npp;
+    __syncthreads();
+    for (int i = tid; i < NW * Ep; i += nt) histB[i] += offE[i % Ep];
+    __syncthreads();
+    for (int base = s0; base < s1; base += 64) {
+        const int i = base + lane;
+        const bool valid = i < s1;
+        const int f = valid ? (La > 0 ? p.tmp[i] : i) : 0;
+        const int e = valid ? expert_of(p, f) : 0;
+        const uint64_t m = match_key((uint32_t)e, valid, p.nbits_e);
+        if (valid) {
+            const int pos = histB[w * Ep + e] + __popcll(m & lanemask_lt());
+            p.sorted_ids[pos] = f;
+            if ((m & lanemask_lt()) == 0) histB[w * Ep + e] += __popcll(m);
+        }
+    }
+
+    // ---- padding, tail and block -> expert map ---------------------------
+    for (int e = w; e < Ep; e += NW) {
+        const int b = offE[e] + totE[e], end = offE[e + 1];
+        for (int q = b + lane; q < end; q += 64) p.sorted_ids[q] = P;
+    }
+    for (int q = npp + tid; q < p.cap; q += nt) p.sorted_ids[q] = P;
+    for (int b = tid; b < p.max_blocks; b += nt) {
+        const int pos = b * p.bm;
+        int ex = -1;
+        if (pos < npp) {
+            int lo = 0, hi = Ep - 1;  // last e with offE[e] <= pos
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (offE[mid] <= pos) lo = mid;
+                else hi = mid - 1;
+            }
+            ex = lo;
+        }
+        p.block_expert[b] = ex;
+    }
+
+    // ---- LoRA work items: (adapter >= 0, expert) runs cut to lbm rows ------
+    int nitems = 0;
+    if (La > 0 && p.items != nullptr) {
+        for (int k = tid; k < NK; k += nt) {
+            const int a1 = k % A1;
+            itemOff[k] = (a1 == 0) ? 0 : (cnt2[k] + p.lbm - 1) / p.lbm;
+        }
+        __syncthreads();
+        nitems = block_excl_scan(itemOff, NK, scr);
+        for (int e = tid; e < Ep; e += nt) {
+            int run = offE[e];
+            for (int a1 = 0; a1 < A1; ++a1) {
+                const int k = e * A1 + a1;
+                const int c = cnt2[k];
+                if (a1 > 0) {
+                    int it = itemOff[k];
+                    for (int q = 0; q < c; q += p.lbm) {
+                        int4 v;
+                        v.x = run + q;
+                        v.y = min(p.lbm, c - q);
+                        v.z = a1 - 1;
+                        v.w = e;
+                        reinterpret_cast<int4 *>(p.items)[it++] = v;
+                    }
+                }
+                run += c;
+            }
+        }
+        for (int q = nitems + tid; q < p.max_items; q += nt) {
+            int4 v;
+            v.x = 0;
+            v.y = 0;
+            v.z = -1;
+            v.w = -1;
+            reinterpret_cast<int4 *>(p.items)[q] = v;
+        }
+    }
+    if (tid == 0) {
+        *p.npp_out = npp;
+        *p.nitems_out = nitems;
+    }
+}
+
+}  // namespace moelora

@@ -1,0 +1,257 @@
+// Grouped expert GEMM for few rows per expert (decode), streaming the expert
+// weights once from HBM.
+//
+//   gate_up:  y13[p, n] = sum_h x[t(p), h] * W13[e, n, h]      n in the tile's
+//             gate columns [i0, i0+BW/2) and the matching up columns
+//             I + [i0, i0+BW/2); epilogue: + LoRA expand (s13 . B13[a,e]),
+//             h = silu(gate) * up, stored bf16 at the sorted row p.
+//   down:     y2[f, n]  = sum_i h[p, i] * W2[e, n, i]; epilogue: + LoRA
+//             expand (s2 . B2[a,e]), stored fp32 at the pair row f.
+// (aitrends.kr summary of the AWS multi-LoRA MoE post: LoRA shrink/expand
+// fused into each expert projection, "section details"; an adapter path on
+// gate_up and on down, "image analysis" diagram; the LoRA sum folded into
+// the expand step.)
+//
+// One workgroup = one expert block of BT sorted rows x one tile of BW weight
+// rows.  The weight tile is the MFMA M side (v_mfma_f32_16x16x32_bf16), the
+// BT tokens the N side, so a lane's accumulator holds 4 consecutive output
+// features of one token and gate/up pairs sit at the same register position.
+// The 4 wavefronts split the reduction into 64-wide chunks (chunk c goes to
+// wave c mod 4) and load their MFMA fragments straight from global memory,
+// double-buffered in registers, so each weight byte is read exactly once per
+// expert block and many loads are in flight per CU.  Partial tiles are summed
+// across waves in LDS in a fixed order, which keeps the result deterministic.
+// Blocks past the padded row count exit at once.
+#pragma once
+
+#include "common.hpp"
+
+namespace moelora {
+
+struct GemmParams {
+    const uint16_t *in;          // gate_up: x [T, Kdim]; down: h [cap, Kdim]
+    const int32_t *sorted_ids;   // [cap]
+    const int32_t *block_expert; // [max_blocks]
+    const int32_t *counters;     // [0] = padded row count
+    const int32_t *adapter_ids;  // [T]
+    const uint16_t *W;           // gate_up: w13 [Ep, 2*Nout, Kdim]; down: w2 [Ep, Nout, Kdim]
+    const uint16_t *B;           // gate_up: b13 [L, Ep, 2*Nout, r]; down: b2 [L, Ep, Nout, r]
+    const float *s_part;         // [split][cap][r]
+    void *out;                   // gate_up: h bf16 [cap, Nout]; down: y2 f32 [P, Nout]
+    int Kdim, Nout, Kp, P, cap, Ep, L, r, split, lora;
+};
+
+// Add the LoRA expand term sum_k s[p,k] * B[a,e,row,k] to `v` for NC output
+// rows starting at `rows[c]` (rows[c] < 0: skipped).  s is the fixed-order sum
+// of the split-K partials.  r is a multiple of 8.
+template <int NC>
+__device__ __forceinline__ void lora_expand_add(const GemmParams &p, int e, int a, int prow, const int *rows,
+                                                int rows_per_expert, float *v) {
+    const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r;
+    for (int k0 = 0; k0 < p.r; k0 += 8) {
+        float s[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] = 0.f;
+        for (int sp = 0; sp < p.split; ++sp) {
+            const float4 *sv = reinterpret_cast<const float4 *>(p.s_part + ((int64_t)sp * p.cap + prow) * p.r + k0);
+            const float4 lo = sv[0], hi = sv[1];
+            s[0] += lo.x; s[1] += lo.y; s[2] += lo.z; s[3] += lo.w;
+            s[4] += hi.x; s[5] += hi.y; s[6] += hi.z; s[7] += hi.w;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (rows[c] < 0) continue;
+            const u32x4 bv = *reinterpret_cast<const u32x4 *>(Bae + (int64_t)rows[c] * p.r + k0);
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc += s[2 * i] * bf16_to_f32((uint16_t)(bv[i] & 0xffffu));
+                acc += s[2 * i + 1] * bf16_to_f32((uint16_t)(bv[i] >> 16));
+            }
+            v[c] += acc;
+        }
+    }
+}
+
+template <int BW, int BT, bool GU>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
+    constexpr int MS = BW / 16, NS = BT / 16;
+    constexpr int LDW = BW + 4;
+    __shared__ float buf[2][BT][LDW];
+
+    const int b = blockIdx.y;
+    const int npp = p.counters[0];
+    if (b * BT >= npp) return;
+    const int e = p.block_expert[b];
+    const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+    const int64_t Kd = p.Kdim;
+    const int N = p.Nout;
+    const int i0 = blockIdx.x * (GU ? BW / 2 : BW);
+    const int rows_per_expert = GU ? 2 * N : N;
+
+    const uint16_t *wrow[MS];
+    bool wok[MS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+        int col, grow;
+        if (GU) {
+            const int half = ms / (MS / 2);
+            col = i0 + (ms % (MS / 2)) * 16 + l16;
+            grow = half ? N + col : col;
+        } else {
+            col = i0 + ms * 16 + l16;
+            grow = col;
+        }
+        wok[ms] = col < N;
+        wrow[ms] = p.W + ((int64_t)e * rows_per_expert + (wok[ms] ? grow : 0)) * Kd;
+    }
+    const uint16_t *xrow[NS];
+    bool xok[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+        const int prow = b * BT + ns * 16 + l16;
+        const int f = p.sorted_ids[prow];
+        xok[ns] = f < p.P;
+        int64_t row = 0;
+        if (xok[ns]) row = GU ? (f / p.Kp) : prow;
+        xrow[ns] = p.in + row * Kd;
+    }
+
+    f32x4 acc[MS][NS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nch = (int)((Kd + 63) / 64);
+    u32x4 wa[2][MS][2], xa[2][NS][2];
+    auto load = [&](int buf_i, int c) {
+        const int64_t k0 = (int64_t)c * 64 + g * 16;
+        const bool k_lo = k0 < Kd, k_hi = k0 + 8 < Kd;
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+            wa[buf_i][ms][0] = ld16(wrow[ms] + k0, wok[ms] && k_lo);
+            wa[buf_i][ms][1] = ld16(wrow[ms] + k0 + 8, wok[ms] && k_hi);
+        }
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+            xa[buf_i][ns][0] = ld16(xrow[ns] + k0, xok[ns] && k_lo);
+            xa[buf_i][ns][1] = ld16(xrow[ns] + k0 + 8, xok[ns] && k_hi);
+        }
+    };
+    auto compute = [&](int buf_i) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(wa[buf_i][ms][s]), as_bf16x8(xa[buf_i][ns][s]), acc[ms][ns], 0, 0, 0);
+    };
+    int c = w;
+    if (c < nch) load(0, c);
+    while (c < nch) {
+        if (c + 4 < nch) load(1, c + 4);
+        compute(0);
+        c += 4;
+        if (c >= nch) break;
+        if (c + 4 < nch) load(0, c + 4);
+        compute(1);
+        c += 4;
+    }
+
+    // Cross-wave reduction in fixed order: (w0 + w2) + (w1 + w3).
+    auto put = [&](int slot) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns)
+                *reinterpret_cast<f32x4 *>(&buf[slot][ns * 16 + l16][ms * 16 + g * 4]) = acc[ms][ns];
+    };
+    auto add = [&](int slot) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns)
+                acc[ms][ns] += *reinterpret_cast<const f32x4 *>(&buf[slot][ns * 16 + l16][ms * 16 + g * 4]);
+    };
+    if (w >= 2) put(w - 2);
+    __syncthreads();
+    if (w < 2) add(w);
+    __syncthreads();
+    if (w == 1) put(0);
+    __syncthreads();
+    if (w == 0) {
+        add(0);
+        put(1);
+    }
+    __syncthreads();
+
+    // Epilogue on the finished tile buf[1][token][feature].
+    if (GU) {
+        constexpr int CG = BW / 8;  // 4-column groups in the gate half
+        uint16_t *hout = reinterpret_cast<uint16_t *>(p.out);
+        for (int q = (int)threadIdx.x; q < BT * CG; q += 256) {
+            const int j = q / CG, cg = q % CG;
+            const int prow = b * BT + j;
+            const int col0 = i0 + cg * 4;
+            if (col0 >= N) continue;
+            const int f = p.sorted_ids[prow];
+            uint2 packed = make_uint2(0u, 0u);
+            if (f < p.P) {
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = buf[1][j][cg * 4 + i];
+                    v[4 + i] = buf[1][j][BW / 2 + cg * 4 + i];
+                }
+                if (p.lora) {
+                    const int a = p.adapter_ids[f / p.Kp];
+                    if (a >= 0 && a < p.L) {
+                        int rows[8];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            rows[i] = col0 + i;
+                            rows[4 + i] = N + col0 + i;
+                        }
+                        lora_expand_add<8>(p, e, a, prow, rows, rows_per_expert, v);
+                    }
+                }
+                float hv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hv[i] = silu(v[i]) * v[4 + i];
+                packed.x = pack_bf16x2(hv[0], hv[1]);
+                packed.y = pack_bf16x2(hv[2], hv[3]);
+            }
+            *reinterpret_cast<uint2 *>(hout + (int64_t)prow * N + col0) = packed;
+        }
+    } else {
+        constexpr int CG = BW / 4;
+        float *yout = reinterpret_cast<float *>(p.out);
+        for (int q = (int)threadIdx.x; q < BT * CG; q += 256) {
+            const int j = q / CG, cg = q % CG;
+            const int prow = b * BT + j;
+            const int col0 = i0 + cg * 4;
+            if (col0 >= N) continue;
+            const int f = p.sorted_ids[prow];
+            if (f >= p.P) continue;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = buf[1][j][cg * 4 + i];
+            if (p.lora) {
+                const int a = p.adapter_ids[f / p.Kp];
+                if (a >= 0 && a < p.L) {
+                    int rows[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rows[i] = col0 + i;
+                    lora_expand_add<4>(p, e, a, prow, rows, rows_per_expert, v);
+                }
+            }
+            *reinterpret_cast<float4 *>(yout + (int64_t)f * N + col0) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+}  // namespace moelora

@@ -1,0 +1,508 @@
+// Host side of the MoE-LoRA layer: argument checking, plan (tile and split
+// choice, workspace carving) and the launch sequence.  Every entry point is
+// declared and documented in include/moe_lora.h.
+//
+// Launch sequence of moe_lora_forward on the caller's stream (no host sync,
+// no allocation, grids sized for the worst case so nothing is read back):
+//   route -> align -> [shrink13] -> gate_up GEMM (+expand13, SwiGLU)
+//         -> [shrink2] -> down GEMM (+expand2) -> combine
+// The LoRA shrink launches are skipped on the host when the layer has no
+// LoRA (L = 0 or r = 0), and on the device every shrink workgroup exits at
+// once when no token of the call carries an adapter (aitrends.kr summary of
+// the AWS multi-LoRA MoE post, "section details": layers without LoRA exit
+// immediately).  No kernel is specialised on T: T is a runtime argument and
+// the code object is loaded once (same post: per-length recompilation made
+// the first version's time-to-first-token 10x the base model's).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "moe_lora.h"
+#include "align.hpp"
+#include "combine.hpp"
+#include "fp32_path.hpp"
+#include "gemm_stream.hpp"
+#include "route.hpp"
+#include "shrink.hpp"
+
+using namespace moelora;
+
+namespace {
+
+constexpr int64_t kLdsBytes = 160 * 1024;
+constexpr int kStreamBW = 64;
+
+thread_local char g_errbuf[320];
+
+struct Plan {
+    int bm = 0, lbm = 0, split = 1, kind = 0;
+    int64_t P = 0, Ep = 0, Kp = 0, La = 0;
+    int64_t max_blocks = 0, cap = 0, max_items = 0;
+    int align_nw = 16;
+    size_t align_lds = 0;
+    bool lora = false;
+    // workspace offsets (bytes)
+    size_t o_ids = 0, o_w = 0, o_sorted = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0;
+    size_t o_s13 = 0, o_s2 = 0, o_h = 0, o_y2 = 0, total = 0;
+    size_t align_total = 0;  // tmp + nothing else, for moe_lora_align
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int bits_for(int64_t n) {  // bits to hold values 0..n-1
+    int b = 0;
+    while ((int64_t(1) << b) < n) ++b;
+    return b;
+}
+
+int make_plan(const moe_lora_dims *d, Plan *pl) {
+    if (!d || !pl) return MOE_LORA_EINVAL;
+    if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->K <= 0 || d->K > d->E || d->S < 0 || d->L < 0 ||
+        d->r < 0)
+        return MOE_LORA_EINVAL;
+    if (!(std::isfinite(d->routed_scaling_factor) && d->routed_scaling_factor > 0.0f)) return MOE_LORA_EINVAL;
+    if (d->renormalize != 0 && d->renormalize != 1) return MOE_LORA_EINVAL;
+    if (d->dtype != MOE_LORA_F32 && d->dtype != MOE_LORA_BF16) return MOE_LORA_EUNSUPPORTED;
+    if (d->E > 1024 || d->K > 64 || d->S > 64) return MOE_LORA_EUNSUPPORTED;
+    if (d->H % 8 != 0 || d->I % 8 != 0) return MOE_LORA_EUNSUPPORTED;
+    if (d->H > (1 << 24) || d->I > (1 << 24)) return MOE_LORA_EUNSUPPORTED;
+    const bool lora = d->L > 0 && d->r > 0;
+    if (lora) {
+        if (d->r > 128 || d->L > 1024) return MOE_LORA_EUNSUPPORTED;
+        if (d->dtype == MOE_LORA_BF16 && d->r % 8 != 0) return MOE_LORA_EUNSUPPORTED;
+    }
+    Plan p;
+    p.lora = lora;
+    p.Kp = d->K + d->S;
+    p.Ep = d->E + d->S;
+    p.La = lora ? d->L : 0;
+    if (d->T > (int64_t(1) << 31) / p.Kp) return MOE_LORA_EUNSUPPORTED;
+    p.P = d->T * p.Kp;
+    if (p.Ep * (p.La + 1) > 16384) return MOE_LORA_EUNSUPPORTED;
+
+    // tile choice by the average rows per expert; never specialised on T itself
+    const int64_t rho = p.P / p.Ep;
+    if (d->block_m != 0 && d->block_m != 16 && d->block_m != 32 && d->block_m != 64) return MOE_LORA_EUNSUPPORTED;
+    if (d->lora_block_m != 0 && d->lora_block_m != 16 && d->lora_block_m != 32) return MOE_LORA_EUNSUPPORTED;
+    if (d->split_k < 0 || d->split_k > 16) return MOE_LORA_EINVAL;
+    if (d->dtype == MOE_LORA_F32) {
+        p.kind = 0;
+        p.bm = d->block_m ? d->block_m : 16;
+        p.lbm = d->lora_block_m ? d->lora_block_m : 16;
+        p.split = 1;
+    } else {
+        p.kind = 1;
+        p.bm = d->block_m ? d->block_m : (rho <= 12 ? 16 : (rho <= 40 ? 32 : 64));
+        p.lbm = d->lora_block_m ? d->lora_block_m : (rho <= 40 || d->r > 64 ? 16 : 32);
+        if (p.lbm == 32 && d->r > 64) return MOE_LORA_EUNSUPPORTED;
+        if (d->split_k) {
+            p.split = d->split_k;
+        } else {
+            const int64_t ch = (std::max(d->H, d->I) + 31) / 32;
+            p.split = (d->T <= 512) ? (int)std::min<int64_t>(4, std::max<int64_t>(1, ch / 16)) : 1;
+        }
+    }
+    if (!lora) p.split = 1;
+
+    const int64_t nz = std::min(p.Ep, p.P);
+    p.max_blocks = (p.P + p.bm - 1) / p.bm + nz;
+    p.cap = p.max_blocks * p.bm;
+    if (lora) {
+        const int64_t bins = std::min(p.La * p.Ep, p.P);
+        p.max_items = (p.P + p.lbm - 1) / p.lbm + bins;
+    }
+    if (p.cap >= (int64_t(1) << 31) - 1) return MOE_LORA_EUNSUPPORTED;
+
+    // align workgroup: as many waves as the LDS allows
+    p.align_nw = 0;
+    for (int nw = 16; nw >= 1; nw >>= 1) {
+        const int64_t bytes = align_lds_ints(nw, (int)p.Ep, (int)p.La) * 4;
+        if (bytes <= kLdsBytes) {
+            p.align_nw = nw;
+            p.align_lds = (size_t)bytes;
+            break;
+        }
+    }
+    if (p.align_nw == 0) return MOE_LORA_EUNSUPPORTED;
+
+    const size_t A = 256;
+    const size_t es = d->dtype == MOE_LORA_BF16 ? 2 : 4;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = round_up(o + std::max<size_t>(bytes, 1), A);
+        return at;
+    };
+    p.o_ids = take(sizeof(int32_t) * p.P);
+    p.o_w = take(sizeof(float) * p.P);
+    p.o_sorted = take(sizeof(int32_t) * p.cap);
+    p.o_bexp = take(sizeof(int32_t) * p.max_blocks);
+    p.o_cnt = take(sizeof(int32_t) * 16);
+    p.o_items = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_items, 1));
+    p.o_tmp = take(sizeof(int32_t) * p.P);
+    p.o_s13 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
+    p.o_s2 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
+    p.o_h = take(es * p.cap * d->I);
+    p.o_y2 = take(sizeof(float) * p.P * d->H);
+    p.total = o;
+    p.align_total = round_up(sizeof(int32_t) * std::max<int64_t>(p.P, 1), A) + round_up(sizeof(int32_t) * 16, A);
+    *pl = p;
+    return MOE_LORA_OK;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int hip_fail(hipError_t e, const char *what) {
+    snprintf(g_errbuf, sizeof g_errbuf, "HIP error in %s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return MOE_LORA_EHIP;
+}
+
+std::once_flag g_attr_once;
+hipError_t g_attr_err = hipSuccess;
+
+void set_kernel_attributes() {
+    g_attr_err = hipFuncSetAttribute((const void *)align_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)kLdsBytes);
+}
+
+int launch_route(const moe_lora_dims *d, const float *logits, int32_t *ids, float *w, hipStream_t st) {
+    const int T = (int)d->T, E = (int)d->E;
+    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+    const float shared_w = 1.0f / d->routed_scaling_factor;
+    const int K = (int)d->K, S = (int)d->S, rn = d->renormalize;
+    if (E <= 64) hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
+    else if (E <= 128) hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
+    else if (E <= 256) hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
+    else if (E <= 512) hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
+    else hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
+    return MOE_LORA_OK;
+}
+
+int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
+                 int32_t *sorted, int32_t *bexp, int32_t *npp, int32_t *items, int32_t *nitems, int32_t *tmp,
+                 hipStream_t st) {
+    std::call_once(g_attr_once, set_kernel_attributes);
+    if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
+    AlignParams ap;
+    ap.topk_ids = ids;
+    ap.adapter_ids = adapter_ids;
+    ap.sorted_ids = sorted;
+    ap.block_expert = bexp;
+    ap.npp_out = npp;
+    ap.nitems_out = nitems;
+    ap.items = pl.lora ? items : nullptr;
+    ap.tmp = tmp;
+    ap.P = (int)pl.P;
+    ap.Kp = (int)pl.Kp;
+    ap.Ep = (int)pl.Ep;
+    ap.La = (int)pl.La;
+    ap.bm = pl.bm;
+    ap.lbm = pl.lbm;
+    ap.cap = (int)pl.cap;
+    ap.max_blocks = (int)pl.max_blocks;
+    ap.max_items = (int)pl.max_items;
+    ap.nbits_a = bits_for(pl.La + 1);
+    ap.nbits_e = bits_for(pl.Ep);
+    (void)d;
+    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(pl.align_nw * 64), pl.align_lds, st, ap);
+    return MOE_LORA_OK;
+}
+
+template <int NT>
+void launch_shrink_nt(const ShrinkParams &sp, int r, int split, int max_items, hipStream_t st) {
+    const dim3 grid((unsigned)max_items, (unsigned)split), block(256);
+    if (r <= 16) hipLaunchKernelGGL((shrink_kernel<NT, 1, true>), grid, block, 0, st, sp);
+    else if (r <= 32) hipLaunchKernelGGL((shrink_kernel<NT, 2, true>), grid, block, 0, st, sp);
+    else if (r <= 64) hipLaunchKernelGGL((shrink_kernel<NT, 4, true>), grid, block, 0, st, sp);
+    else hipLaunchKernelGGL((shrink_kernel<NT, 8, true>), grid, block, 0, st, sp);
+}
+
+template <int NT>
+void launch_shrink_rows_nt(const ShrinkParams &sp, int r, int split, int max_items, hipStream_t st) {
+    const dim3 grid((unsigned)max_items, (unsigned)split), block(256);
+    if (r <= 16) hipLaunchKernelGGL((shrink_kernel<NT, 1, false>), grid, block, 0, st, sp);
+    else if (r <= 32) hipLaunchKernelGGL((shrink_kernel<NT, 2, false>), grid, block, 0, st, sp);
+    else if (r <= 64) hipLaunchKernelGGL((shrink_kernel<NT, 4, false>), grid, block, 0, st, sp);
+    else hipLaunchKernelGGL((shrink_kernel<NT, 8, false>), grid, block, 0, st, sp);
+}
+
+void launch_shrink(const Plan &pl, ShrinkParams sp, bool gather, int r, hipStream_t st) {
+    const int nch = (sp.Kdim + 31) / 32;
+    sp.chunks_per_split = (nch + pl.split - 1) / pl.split;
+    const int mi = (int)pl.max_items;
+    if (gather) {
+        if (pl.lbm == 16) launch_shrink_nt<1>(sp, r, pl.split, mi, st);
+        else launch_shrink_nt<2>(sp, r, pl.split, mi, st);
+    } else {
+        if (pl.lbm == 16) launch_shrink_rows_nt<1>(sp, r, pl.split, mi, st);
+        else launch_shrink_rows_nt<2>(sp, r, pl.split, mi, st);
+    }
+}
+
+template <bool GU>
+void launch_gemm_stream(const Plan &pl, const GemmParams &gp, hipStream_t st) {
+    const int tile = GU ? kStreamBW / 2 : kStreamBW;
+    const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
+    switch (pl.bm) {
+        case 16: hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU>), grid, block, 0, st, gp); break;
+        case 32: hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU>), grid, block, 0, st, gp); break;
+        default: hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 64, GU>), grid, block, 0, st, gp); break;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_lora_plan_query(const moe_lora_dims *dims, moe_lora_plan *plan) {
+    Plan p;
+    const int rc = make_plan(dims, &p);
+    if (rc != MOE_LORA_OK) return rc;
+    if (!plan) return MOE_LORA_EINVAL;
+    plan->block_m = p.bm;
+    plan->lora_block_m = p.lbm;
+    plan->split_k = p.split;
+    plan->gemm_kind = p.kind;
+    plan->max_blocks = p.max_blocks;
+    plan->sorted_capacity = p.cap;
+    plan->max_items = p.max_items;
+    plan->workspace_bytes = p.total;
+    plan->align_workspace_bytes = p.align_total;
+    return MOE_LORA_OK;
+}
+
+size_t moe_lora_workspace_bytes(const moe_lora_dims *dims) {
+    Plan p;
+    return make_plan(dims, &p) == MOE_LORA_OK ? p.total : 0;
+}
+
+int moe_lora_check_args(const moe_lora_dims *d, const moe_lora_args *a) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc != MOE_LORA_OK) return rc;
+    if (!a) return MOE_LORA_EINVAL;
+    if (d->T == 0) return MOE_LORA_OK;
+    if (!a->hidden || !a->router_logits || !a->w13 || !a->w2 || !a->out || !a->workspace) return MOE_LORA_EINVAL;
+    if (p.lora && (!a->adapter_ids || !a->a13 || !a->b13 || !a->a2 || !a->b2)) return MOE_LORA_EINVAL;
+    const void *v16[] = {a->hidden, a->w13, a->w2, a->out};
+    for (const void *ptr : v16)
+        if (!aligned(ptr, 16)) return MOE_LORA_EINVAL;
+    if (p.lora) {
+        const void *l16[] = {a->a13, a->b13, a->a2, a->b2};
+        for (const void *ptr : l16)
+            if (!aligned(ptr, 16)) return MOE_LORA_EINVAL;
+    }
+    if (!aligned(a->workspace, 256)) return MOE_LORA_EINVAL;
+    if (a->workspace_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    return MOE_LORA_OK;
+}
+
+int moe_lora_route(const moe_lora_dims *d, const float *logits, int32_t *topk_ids, float *topk_weights,
+                   void *stream) {
+    if (!d) return MOE_LORA_EINVAL;
+    if (d->T < 0 || d->E <= 0 || d->K <= 0 || d->K > d->E || d->S < 0) return MOE_LORA_EINVAL;
+    if (d->E > 1024 || d->K > 64 || d->S > 64) return MOE_LORA_EUNSUPPORTED;
+    if (!(std::isfinite(d->routed_scaling_factor) && d->routed_scaling_factor > 0.0f)) return MOE_LORA_EINVAL;
+    if (d->renormalize != 0 && d->renormalize != 1) return MOE_LORA_EINVAL;
+    if (d->T == 0) return MOE_LORA_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_LORA_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    launch_route(d, logits, topk_ids, topk_weights, st);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "route launch");
+}
+
+int moe_lora_align(const moe_lora_dims *d, const int32_t *topk_ids, const int32_t *adapter_ids,
+                   int32_t *sorted_ids, int32_t *block_expert, int32_t *num_post_pad, int32_t *lora_items,
+                   int32_t *num_items, void *workspace, size_t workspace_bytes, void *stream) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc != MOE_LORA_OK) return rc;
+    if (d->T == 0) return MOE_LORA_OK;
+    if (!topk_ids || !sorted_ids || !block_expert || !num_post_pad || !workspace) return MOE_LORA_EINVAL;
+    if (p.lora && (!adapter_ids || !lora_items || !num_items)) return MOE_LORA_EINVAL;
+    if (lora_items && !aligned(lora_items, 16)) return MOE_LORA_EINVAL;
+    if (!aligned(workspace, 256)) return MOE_LORA_EINVAL;
+    if (workspace_bytes < p.align_total) return MOE_LORA_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    int32_t *tmp = (int32_t *)ws;
+    int32_t *cnt = (int32_t *)(ws + round_up(sizeof(int32_t) * p.P, 256));
+    int r2 = launch_align(p, d, topk_ids, adapter_ids, sorted_ids, block_expert, num_post_pad, lora_items,
+                          num_items ? num_items : cnt + 1, tmp, st);
+    if (r2 != MOE_LORA_OK) return r2;
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "align launch");
+}
+
+int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *stream) {
+    const int rc = moe_lora_check_args(d, a);
+    if (rc != MOE_LORA_OK) return rc;
+    if (d->T == 0) return MOE_LORA_OK;
+    Plan p;
+    make_plan(d, &p);
+    hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)a->workspace;
+    int32_t *ids = a->topk_ids_out ? a->topk_ids_out : (int32_t *)(ws + p.o_ids);
+    float *wts = a->topk_weights_out ? a->topk_weights_out : (float *)(ws + p.o_w);
+    int32_t *sorted = (int32_t *)(ws + p.o_sorted);
+    int32_t *bexp = (int32_t *)(ws + p.o_bexp);
+    int32_t *cnt = (int32_t *)(ws + p.o_cnt);
+    int32_t *items = (int32_t *)(ws + p.o_items);
+    int32_t *tmp = (int32_t *)(ws + p.o_tmp);
+    float *s13 = (float *)(ws + p.o_s13);
+    float *s2 = (float *)(ws + p.o_s2);
+    void *h = (void *)(ws + p.o_h);
+    float *y2 = (float *)(ws + p.o_y2);
+    const int H = (int)d->H, I = (int)d->I, r = (int)d->r;
+
+    void **ev = a->stage_events;
+    auto mark = [&](int slot) {
+        if (ev) hipEventRecord((hipEvent_t)ev[slot], st);
+    };
+    mark(2 * MOE_LORA_STAGE_ROUTE);
+    launch_route(d, a->router_logits, ids, wts, st);
+    mark(2 * MOE_LORA_STAGE_ROUTE + 1);
+    mark(2 * MOE_LORA_STAGE_ALIGN);
+    int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, bexp, cnt, items, cnt + 1, tmp, st);
+    if (r2 != MOE_LORA_OK) return r2;
+    mark(2 * MOE_LORA_STAGE_ALIGN + 1);
+
+    if (p.kind == 0) {
+        // fp32 path
+        mark(2 * MOE_LORA_STAGE_SHRINK13);
+        if (p.lora)
+            hipLaunchKernelGGL(shrink_f32_kernel, dim3((unsigned)p.max_items), dim3(256), 0, st,
+                               (const float *)a->hidden, sorted, (const float *)a->a13, items, cnt, s13, H, r,
+                               (int)p.Ep, (int)p.Kp, 1);
+        mark(2 * MOE_LORA_STAGE_SHRINK13 + 1);
+        F32Params fp;
+        fp.sorted_ids = sorted;
+        fp.block_expert = bexp;
+        fp.counters = cnt;
+        fp.adapter_ids = a->adapter_ids;
+        fp.Kp = (int)p.Kp;
+        fp.P = (int)p.P;
+        fp.cap = (int)p.cap;
+        fp.Ep = (int)p.Ep;
+        fp.r = r;
+        fp.L = (int)p.La;
+        fp.lora = p.lora ? 1 : 0;
+        fp.bt = p.bm;
+        fp.in = (const float *)a->hidden;
+        fp.W = (const float *)a->w13;
+        fp.B = (const float *)a->b13;
+        fp.s = s13;
+        fp.out = (float *)h;
+        fp.Kdim = H;
+        fp.Nout = I;
+        mark(2 * MOE_LORA_STAGE_GATE_UP);
+        hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)((I + 63) / 64), (unsigned)p.max_blocks),
+                           dim3(256), 0, st, fp);
+        mark(2 * MOE_LORA_STAGE_GATE_UP + 1);
+        mark(2 * MOE_LORA_STAGE_SHRINK2);
+        if (p.lora)
+            hipLaunchKernelGGL(shrink_f32_kernel, dim3((unsigned)p.max_items), dim3(256), 0, st,
+                               (const float *)h, sorted, (const float *)a->a2, items, cnt, s2, I, r, (int)p.Ep,
+                               (int)p.Kp, 0);
+        mark(2 * MOE_LORA_STAGE_SHRINK2 + 1);
+        fp.in = (const float *)h;
+        fp.W = (const float *)a->w2;
+        fp.B = (const float *)a->b2;
+        fp.s = s2;
+        fp.out = y2;
+        fp.Kdim = I;
+        fp.Nout = H;
+        mark(2 * MOE_LORA_STAGE_DOWN);
+        hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3((unsigned)((H + 63) / 64), (unsigned)p.max_blocks),
+                           dim3(256), 0, st, fp);
+        mark(2 * MOE_LORA_STAGE_DOWN + 1);
+        mark(2 * MOE_LORA_STAGE_COMBINE);
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)d->T), dim3(256),
+                           0, st, y2, wts, a->out, (int)d->T, H, (int)p.Kp, d->routed_scaling_factor);
+        mark(2 * MOE_LORA_STAGE_COMBINE + 1);
+    } else {
+        ShrinkParams sp;
+        sp.sorted_ids = sorted;
+        sp.items = items;
+        sp.counters = cnt;
+        sp.r = r;
+        sp.Ep = (int)p.Ep;
+        sp.Kp = (int)p.Kp;
+        sp.P = (int)p.P;
+        sp.cap = (int)p.cap;
+        mark(2 * MOE_LORA_STAGE_SHRINK13);
+        if (p.lora) {
+            sp.in = (const uint16_t *)a->hidden;
+            sp.A = (const uint16_t *)a->a13;
+            sp.s_part = s13;
+            sp.Kdim = H;
+            launch_shrink(p, sp, true, r, st);
+        }
+        mark(2 * MOE_LORA_STAGE_SHRINK13 + 1);
+        GemmParams gp;
+        gp.sorted_ids = sorted;
+        gp.block_expert = bexp;
+        gp.counters = cnt;
+        gp.adapter_ids = a->adapter_ids;
+        gp.Kp = (int)p.Kp;
+        gp.P = (int)p.P;
+        gp.cap = (int)p.cap;
+        gp.Ep = (int)p.Ep;
+        gp.r = r;
+        gp.L = (int)p.La;
+        gp.split = p.split;
+        gp.lora = p.lora ? 1 : 0;
+        gp.in = (const uint16_t *)a->hidden;
+        gp.W = (const uint16_t *)a->w13;
+        gp.B = (const uint16_t *)a->b13;
+        gp.s_part = s13;
+        gp.out = h;
+        gp.Kdim = H;
+        gp.Nout = I;
+        mark(2 * MOE_LORA_STAGE_GATE_UP);
+        launch_gemm_stream<true>(p, gp, st);
+        mark(2 * MOE_LORA_STAGE_GATE_UP + 1);
+        mark(2 * MOE_LORA_STAGE_SHRINK2);
+        if (p.lora) {
+            sp.in = (const uint16_t *)h;
+            sp.A = (const uint16_t *)a->a2;
+            sp.s_part = s2;
+            sp.Kdim = I;
+            launch_shrink(p, sp, false, r, st);
+        }
+        mark(2 * MOE_LORA_STAGE_SHRINK2 + 1);
+        gp.in = (const uint16_t *)h;
+        gp.W = (const uint16_t *)a->w2;
+        gp.B = (const uint16_t *)a->b2;
+        gp.s_part = s2;
+        gp.out = y2;
+        gp.Kdim = I;
+        gp.Nout = H;
+        mark(2 * MOE_LORA_STAGE_DOWN);
+        launch_gemm_stream<false>(p, gp, st);
+        mark(2 * MOE_LORA_STAGE_DOWN + 1);
+        mark(2 * MOE_LORA_STAGE_COMBINE);
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)d->T), dim3(256),
+                           0, st, y2, wts, a->out, (int)d->T, H, (int)p.Kp, d->routed_scaling_factor);
+        mark(2 * MOE_LORA_STAGE_COMBINE + 1);
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "forward launch");
+}
+
+const char *moe_lora_strerror(int code) {
+    switch (code) {
+        case MOE_LORA_OK: return "ok";
+        case MOE_LORA_EINVAL: return "invalid argument (null pointer, bad size, K > E, rsf <= 0 or misaligned pointer)";
+        case MOE_LORA_EUNSUPPORTED: return "unsupported configuration (dtype, H or I not a multiple of 8, or a size limit)";
+        case MOE_LORA_EWORKSPACE: return "workspace too small";
+        case MOE_LORA_EHIP: return g_errbuf[0] ? g_errbuf : "HIP error";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

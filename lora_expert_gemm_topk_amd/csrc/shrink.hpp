@@ -1,0 +1,114 @@
+// LoRA shrink: s[p, k] = sum_c in[p, c] * A[a, e, k, c] for the rows p of one
+// (adapter, expert) work item.
+//
+// The shrink is the skinny side of LoRA: r (16..64) output columns against a
+// reduction over H or I.  Following the split-K idea for skinny LoRA
+// products (aitrends.kr summary of the AWS multi-LoRA MoE post, "section
+// details" and "practical takeaways"), the reduction is split twice: across
+// `split` workgroups (grid.y) and, inside a workgroup, across its 4
+// wavefronts.  Partials go to s_part[split][row][r] in fp32 and are summed
+// in fixed order by the consumer (the expand in the next GEMM's epilogue), so
+// the result does not depend on scheduling.  Items past the item count exit
+// at once: a layer call whose tokens carry no adapter does no shrink work.
+//
+// Matrix-core mapping (v_mfma_f32_16x16x32_bf16): the MFMA M side is the
+// rank index k (A rows), the N side is the item's rows (tokens), K is the
+// reduction.  Rows k >= r and tokens past the item length load zeros.
+#pragma once
+
+#include "common.hpp"
+
+namespace moelora {
+
+struct ShrinkParams {
+    const uint16_t *in;        // gate_up: x [T, H]; down: h [cap, I] (row = sorted position)
+    const int32_t *sorted_ids; // gate_up only: pair index per sorted position
+    const uint16_t *A;         // [L, Ep, r, Kdim]
+    const int32_t *items;      // [max_items][4]
+    const int32_t *counters;   // [1] = item count
+    float *s_part;             // [split][cap][r]
+    int Kdim, r, Ep, Kp, P, cap;
+    int chunks_per_split;      // in units of 32 along Kdim
+};
+
+// NT: 16-row token subtiles per item (lora_block_m = 16*NT); MT: 16-row
+// rank subtiles (r <= 16*MT); GATHER: rows come from x through sorted_ids.
+template <int NT, int MT, bool GATHER>
+__global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
+    __shared__ float red[4][16 * NT][16 * MT + 4];
+    const int item = blockIdx.x;
+    if (item >= p.counters[1]) return;
+    const int4 it = reinterpret_cast<const int4 *>(p.items)[item];
+    const int p0 = it.x, len = it.y, a = it.z, e = it.w;
+    const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+    const int64_t Kd = p.Kdim;
+
+    // per-lane row pointers for the N side (tokens) and the M side (rank rows)
+    const uint16_t *xrow[NT];
+    bool xok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int j = nt * 16 + l16;
+        xok[nt] = j < len;
+        int64_t row = 0;
+        if (xok[nt]) {
+            if (GATHER) row = p.sorted_ids[p0 + j] / p.Kp;
+            else row = p0 + j;
+        }
+        xrow[nt] = p.in + row * Kd;
+    }
+    const uint16_t *arow[MT];
+    bool aok[MT];
+    const uint16_t *Abase = p.A + ((int64_t)a * p.Ep + e) * p.r * Kd;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int k = mt * 16 + l16;
+        aok[mt] = k < p.r;
+        arow[mt] = Abase + (int64_t)(aok[mt] ? k : 0) * Kd;
+    }
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nch = (int)((Kd + 31) / 32);
+    const int c_beg = blockIdx.y * p.chunks_per_split;
+    const int c_end = min(nch, c_beg + p.chunks_per_split);
+    for (int c = c_beg + w; c < c_end; c += 4) {
+        const int64_t k0 = (int64_t)c * 32 + g * 8;
+        const bool kin = k0 < Kd;  // Kdim is a multiple of 8
+        u32x4 av[MT], xv[NT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) av[mt] = ld16(arow[mt] + k0, aok[mt] && kin);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) xv[nt] = ld16(xrow[nt] + k0, xok[nt] && kin);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[mt]), as_bf16x8(xv[nt]),
+                                                                      acc[mt][nt], 0, 0, 0);
+    }
+    // D layout: lane holds rank rows 4*g .. 4*g+3 of column (token) l16.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[w][nt * 16 + l16][mt * 16 + g * 4 + i] = acc[mt][nt][i];
+    __syncthreads();
+    const int R4 = (p.r + 3) / 4;
+    float *dst = p.s_part + ((int64_t)blockIdx.y * p.cap + p0) * p.r;
+    for (int q = (int)threadIdx.x; q < len * R4; q += 256) {
+        const int j = q / R4, k = (q % R4) * 4;
+        for (int i = 0; i < 4 && k + i < p.r; ++i) {
+            const float v = ((red[0][j][k + i] + red[1][j][k + i]) + red[2][j][k + i]) + red[3][j][k + i];
+            dst[(int64_t)j * p.r + k + i] = v;
+        }
+    }
+}
+
+}  // namespace moelora

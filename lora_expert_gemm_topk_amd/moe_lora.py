@@ -1,0 +1,246 @@
+"""Python binding of libmoelora.so (see include/moe_lora.h for the contract).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoelora.so.  PyTorch supplies device memory and the current stream.  When
+the library has not been built this module raises instead of falling back to
+anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libmoelora.so"
+_lib = None
+
+MOE_LORA_OK = 0
+MOE_LORA_EINVAL = -1
+MOE_LORA_EUNSUPPORTED = -2
+MOE_LORA_EWORKSPACE = -3
+MOE_LORA_EHIP = -4
+MOE_LORA_F32 = 0
+MOE_LORA_BF16 = 1
+STAGES = ("route", "align", "shrink13", "gate_up", "shrink2", "down", "combine")
+
+EXPORTED = ("moe_lora_plan_query", "moe_lora_workspace_bytes", "moe_lora_check_args", "moe_lora_route",
+            "moe_lora_align", "moe_lora_forward", "moe_lora_strerror")
+
+
+class MoeLoraDims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64), ("E", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("S", ctypes.c_int64), ("L", ctypes.c_int64), ("r", ctypes.c_int64),
+                ("routed_scaling_factor", ctypes.c_float), ("renormalize", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("block_m", ctypes.c_int32), ("lora_block_m", ctypes.c_int32),
+                ("split_k", ctypes.c_int32)]
+
+
+class MoeLoraPlan(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int32), ("lora_block_m", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("gemm_kind", ctypes.c_int32), ("max_blocks", ctypes.c_int64),
+                ("sorted_capacity", ctypes.c_int64), ("max_items", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t), ("align_workspace_bytes", ctypes.c_size_t)]
+
+
+class MoeLoraArgs(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_void_p), ("router_logits", ctypes.c_void_p),
+                ("adapter_ids", ctypes.c_void_p), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("a13", ctypes.c_void_p), ("b13", ctypes.c_void_p), ("a2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("topk_ids_out", ctypes.c_void_p),
+                ("topk_weights_out", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+
+
+class MoeLoraError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {moe_lora_strerror(code)} (code {code})")
+        self.code = code
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmoelora.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(f"HIP library {_LIB_PATH} is missing; build it with "
+                           "`python -m lora_expert_gemm_topk_amd.build`")
+    L = ctypes.CDLL(str(_LIB_PATH))
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    L.moe_lora_plan_query.argtypes = [P(MoeLoraDims), P(MoeLoraPlan)]
+    L.moe_lora_plan_query.restype = ctypes.c_int
+    L.moe_lora_workspace_bytes.argtypes = [P(MoeLoraDims)]
+    L.moe_lora_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_lora_check_args.argtypes = [P(MoeLoraDims), P(MoeLoraArgs)]
+    L.moe_lora_check_args.restype = ctypes.c_int
+    L.moe_lora_route.argtypes = [P(MoeLoraDims), vp, vp, vp, vp]
+    L.moe_lora_route.restype = ctypes.c_int
+    L.moe_lora_align.argtypes = [P(MoeLoraDims), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.moe_lora_align.restype = ctypes.c_int
+    L.moe_lora_forward.argtypes = [P(MoeLoraDims), P(MoeLoraArgs), vp]
+    L.moe_lora_forward.restype = ctypes.c_int
+    L.moe_lora_strerror.argtypes = [ctypes.c_int]
+    L.moe_lora_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def make_dims(T, H, I, E, K, S=0, L=0, r=0, rsf=1.0, renormalize=1, dtype="bf16", block_m=0,
+              lora_block_m=0, split_k=0) -> MoeLoraDims:
+    dt = {"bf16": MOE_LORA_BF16, "f32": MOE_LORA_F32, torch.bfloat16: MOE_LORA_BF16,
+          torch.float32: MOE_LORA_F32}.get(dtype, dtype)
+    return MoeLoraDims(int(T), int(H), int(I), int(E), int(K), int(S), int(L), int(r), float(rsf),
+                       int(renormalize), int(dt), int(block_m), int(lora_block_m), int(split_k))
+
+
+def moe_lora_strerror(code: int) -> str:
+    return lib().moe_lora_strerror(int(code)).decode()
+
+
+def moe_lora_plan_query(dims: MoeLoraDims) -> dict:
+    p = MoeLoraPlan()
+    rc = lib().moe_lora_plan_query(ctypes.byref(dims), ctypes.byref(p))
+    if rc != MOE_LORA_OK:
+        raise MoeLoraError(rc, "moe_lora_plan_query")
+    return {name: getattr(p, name) for name, _ in MoeLoraPlan._fields_}
+
+
+def moe_lora_workspace_bytes(dims: MoeLoraDims) -> int:
+    return int(lib().moe_lora_workspace_bytes(ctypes.byref(dims)))
+
+
+def moe_lora_check_args(dims: MoeLoraDims, args: MoeLoraArgs) -> int:
+    return int(lib().moe_lora_check_args(ctypes.byref(dims), ctypes.byref(args)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dev_tensor(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def moe_lora_route(logits: torch.Tensor, K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1):
+    """Top-K routing + shared-slot append on the GPU -> (topk_ids int32, topk_weights f32)."""
+    _dev_tensor(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dims = make_dims(T, 8, 8, E, K, S, 0, 0, rsf, renormalize)
+    ids = torch.empty((T, K + S), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, K + S), dtype=torch.float32, device=logits.device)
+    with torch.cuda.device(logits.device):
+        rc = lib().moe_lora_route(ctypes.byref(dims), _ptr(logits), _ptr(ids), _ptr(w), _stream(logits.device))
+    if rc != MOE_LORA_OK:
+        raise MoeLoraError(rc, "moe_lora_route")
+    return ids, w
+
+
+def moe_lora_align(topk_ids: torch.Tensor, adapter_ids: Optional[torch.Tensor], dims: MoeLoraDims) -> dict:
+    """Alignment on the GPU.  Returns sorted_ids, block_expert, num_post_pad [1],
+    lora_items [max_items, 4], num_items [1] and the plan, all device tensors."""
+    _dev_tensor(topk_ids, "topk_ids", torch.int32)
+    _dev_tensor(adapter_ids, "adapter_ids", torch.int32)
+    plan = moe_lora_plan_query(dims)
+    dev = topk_ids.device
+    sorted_ids = torch.empty(plan["sorted_capacity"], dtype=torch.int32, device=dev)
+    block_expert = torch.empty(plan["max_blocks"], dtype=torch.int32, device=dev)
+    npp = torch.zeros(1, dtype=torch.int32, device=dev)
+    items = torch.empty((max(plan["max_items"], 1), 4), dtype=torch.int32, device=dev)
+    nitems = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(plan["align_workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().moe_lora_align(ctypes.byref(dims), _ptr(topk_ids), _ptr(adapter_ids), _ptr(sorted_ids),
+                                  _ptr(block_expert), _ptr(npp), _ptr(items), _ptr(nitems), _ptr(ws),
+                                  ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != MOE_LORA_OK:
+        raise MoeLoraError(rc, "moe_lora_align")
+    return dict(sorted_ids=sorted_ids, block_expert=block_expert, num_post_pad=npp,
+                lora_items=items[:plan["max_items"]], num_items=nitems, plan=plan)
+
+
+class Workspace:
+    """A reusable device workspace: grows on demand, never shrinks."""
+
+    def __init__(self):
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self.buf
+
+
+def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optional[torch.Tensor],
+                     w13: torch.Tensor, w2: torch.Tensor, a13=None, b13=None, a2=None, b2=None, *,
+                     K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
+                     block_m: int = 0, lora_block_m: int = 0, split_k: int = 0,
+                     routing_out: Optional[tuple] = None, stage_events=None) -> torch.Tensor:
+    """The fused MoE-LoRA layer on the GPU (enqueued on the current stream).
+
+    Shapes: x [T,H], logits [T,E] f32, adapter_ids [T] i32 (-1 = none),
+    w13 [E+S,2I,H], w2 [E+S,H,I], a13 [L,E+S,r,H], b13 [L,E+S,2I,r],
+    a2 [L,E+S,r,I], b2 [L,E+S,H,r]; x, weights and out share one dtype
+    (bf16 or f32).  routing_out = (ids [T,K+S] i32, weights [T,K+S] f32)
+    receives the routing decisions when given.  stage_events: optional
+    ctypes array of 2*len(STAGES) hipEvent_t handles recorded around each
+    stage on the launch stream."""
+    dt = x.dtype
+    for name, t in (("x", x), ("w13", w13), ("w2", w2), ("a13", a13), ("b13", b13), ("a2", a2), ("b2", b2)):
+        _dev_tensor(t, name, dt)
+    _dev_tensor(logits, "logits", torch.float32)
+    _dev_tensor(adapter_ids, "adapter_ids", torch.int32)
+    T, H = x.shape
+    Ep, twoI, _ = w13.shape
+    I = twoI // 2
+    E = logits.shape[1]
+    L, r = (a13.shape[0], a13.shape[2]) if a13 is not None else (0, 0)
+    dims = make_dims(T, H, I, E, K, S, L, r, rsf, renormalize, dt, block_m, lora_block_m, split_k)
+    if out is None:
+        out = torch.empty((T, H), dtype=dt, device=x.device)
+    _dev_tensor(out, "out", dt)
+    nbytes = moe_lora_workspace_bytes(dims)
+    ws = (workspace or Workspace()).get(nbytes, x.device)
+    ids_out, w_out = routing_out if routing_out is not None else (None, None)
+    args = MoeLoraArgs(x.data_ptr(), logits.data_ptr(), adapter_ids.data_ptr() if adapter_ids is not None else None,
+                       w13.data_ptr(), w2.data_ptr(),
+                       *(t.data_ptr() if t is not None else None for t in (a13, b13, a2, b2)),
+                       out.data_ptr(), ws.data_ptr(), ws.numel(),
+                       ids_out.data_ptr() if ids_out is not None else None,
+                       w_out.data_ptr() if w_out is not None else None,
+                       ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None)
+    with torch.cuda.device(x.device):
+        rc = lib().moe_lora_forward(ctypes.byref(dims), ctypes.byref(args), _stream(x.device))
+    if rc != MOE_LORA_OK:
+        raise MoeLoraError(rc, "moe_lora_forward")
+    return out
+
+
+def forward_inputs(inp, *, lora: bool = True, **kw) -> torch.Tensor:
+    """moe_lora_forward over a synth.LayerInputs bundle already on the GPU."""
+    s = inp.shape
+    use = lora and s.lora
+    return moe_lora_forward(inp.x, inp.logits, inp.adapter_ids if use else None, inp.w13, inp.w2,
+                            inp.a13 if use else None, inp.b13 if use else None,
+                            inp.a2 if use else None, inp.b2 if use else None,
+                            K=s.K, S=s.S, rsf=s.rsf, renormalize=s.renormalize, **kw)

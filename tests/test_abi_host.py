@@ -1,0 +1,106 @@
+"""Host-only checks of the C ABI: the library loads without a GPU, exports every
+symbol the header declares, and rejects bad arguments with the documented
+codes before touching any device."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import lora_expert_gemm_topk_amd as ml
+from lora_expert_gemm_topk_amd import moe_lora as mm
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "moe_lora.h"
+
+
+def _declared():
+    txt = HEADER.read_text()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char \*)\s*(moe_lora_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(mm.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(mm.library_path()))
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_never_null():
+    for c in (0, -1, -2, -3, -4, 17):
+        assert isinstance(ml.moe_lora_strerror(c), str) and ml.moe_lora_strerror(c)
+
+
+def _dims(**kw):
+    base = dict(T=64, H=2880, I=2880, E=32, K=4, S=0, L=8, r=16)
+    base.update(kw)
+    return ml.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=33), ml.MOE_LORA_EINVAL),            # K > E
+    (dict(K=0), ml.MOE_LORA_EINVAL),
+    (dict(T=-1), ml.MOE_LORA_EINVAL),
+    (dict(H=0), ml.MOE_LORA_EINVAL),
+    (dict(rsf=0.0), ml.MOE_LORA_EINVAL),
+    (dict(rsf=float("nan")), ml.MOE_LORA_EINVAL),
+    (dict(renormalize=2), ml.MOE_LORA_EINVAL),
+    (dict(H=2884), ml.MOE_LORA_EUNSUPPORTED),    # H not a multiple of 8
+    (dict(I=100), ml.MOE_LORA_EUNSUPPORTED),
+    (dict(dtype=7), ml.MOE_LORA_EUNSUPPORTED),
+    (dict(r=12), ml.MOE_LORA_EUNSUPPORTED),      # bf16 rank must be a multiple of 8
+    (dict(r=256), ml.MOE_LORA_EUNSUPPORTED),
+    (dict(E=2048, K=4), ml.MOE_LORA_EUNSUPPORTED),
+    (dict(block_m=24), ml.MOE_LORA_EUNSUPPORTED),
+    (dict(E=256, L=128), ml.MOE_LORA_EUNSUPPORTED),  # (E+S)*(L+1) over the align limit
+])
+def test_plan_rejects(kw, code):
+    d = _dims(**kw)
+    with pytest.raises(ml.MoeLoraError) as ei:
+        ml.moe_lora_plan_query(d)
+    assert ei.value.code == code
+    assert ml.moe_lora_workspace_bytes(d) == 0
+
+
+def test_plan_sizes_follow_the_bounds():
+    for T, E, K, S, L, r in [(64, 32, 4, 0, 8, 16), (4096, 32, 4, 0, 32, 32), (1, 64, 8, 1, 0, 0),
+                             (8192, 128, 8, 0, 64, 64), (16, 4, 2, 0, 2, 8)]:
+        d = _dims(T=T, E=E, K=K, S=S, L=L, r=r)
+        p = ml.moe_lora_plan_query(d)
+        P, Ep = T * (K + S), E + S
+        assert p["max_blocks"] == -(-P // p["block_m"]) + min(Ep, P)
+        assert p["sorted_capacity"] == p["max_blocks"] * p["block_m"]
+        if L and r:
+            assert p["max_items"] == -(-P // p["lora_block_m"]) + min(P, L * Ep)
+        else:
+            assert p["max_items"] == 0
+        assert p["workspace_bytes"] == ml.moe_lora_workspace_bytes(d) > 0
+
+
+def _args(**kw):
+    a = ml.MoeLoraArgs()
+    fields = dict(hidden=0x1000, router_logits=0x2000, adapter_ids=0x3000, w13=0x4000, w2=0x5000,
+                  a13=0x6000, b13=0x7000, a2=0x8000, b2=0x9000, out=0xa000, workspace=0x10000,
+                  workspace_bytes=1 << 40)
+    fields.update(kw)
+    for k, v in fields.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_check_args_codes_without_device():
+    d = _dims()
+    need = ml.moe_lora_workspace_bytes(d)
+    assert ml.moe_lora_check_args(d, _args(workspace_bytes=need)) == ml.MOE_LORA_OK
+    assert ml.moe_lora_check_args(d, _args(workspace_bytes=need - 1)) == ml.MOE_LORA_EWORKSPACE
+    for name in ("hidden", "router_logits", "w13", "w2", "out", "workspace", "adapter_ids", "a13", "b2"):
+        assert ml.moe_lora_check_args(d, _args(**{name: None})) == ml.MOE_LORA_EINVAL, name
+    assert ml.moe_lora_check_args(d, _args(hidden=0x1008)) == ml.MOE_LORA_EINVAL     # misaligned
+    assert ml.moe_lora_check_args(d, _args(workspace=0x10010)) == ml.MOE_LORA_EINVAL
+    # without LoRA the adapter and LoRA pointers may be NULL
+    d0 = _dims(L=0, r=0)
+    assert ml.moe_lora_check_args(d0, _args(adapter_ids=None, a13=None, b13=None, a2=None, b2=None)) == 0
+    # T = 0 is a no-op and needs no buffers
+    assert ml.moe_lora_check_args(_dims(T=0), _args(hidden=None, out=None, workspace=None)) == 0

@@ -1,0 +1,276 @@
+"""GPU parity of the HIP path against the fp64 oracle, called through the C ABI.
+
+Routing and alignment must match the oracle bit for bit; the layer output must
+match within max-abs 2e-2 and relative L2 1e-2 (bf16) or 1e-5 (fp32); the
+LoRA delta (output minus the no-LoRA output) is checked on its own so that a
+missing LoRA term cannot hide inside the absolute tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import lora_expert_gemm_topk_amd as ml
+from lora_expert_gemm_topk_amd import synth
+from tests.gpu_util import LORA_DELTA_RELL2, assert_close, errs, inputs, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int32).numpy()
+
+
+# --------------------------------------------------------------------- route
+
+ROUTE_CASES = [
+    dict(T=16, E=4, K=2), dict(T=64, E=32, K=4), dict(T=4096, E=32, K=4),
+    dict(T=128, E=64, K=8, S=1, rsf=2.5), dict(T=33, E=300, K=5), dict(T=3, E=1000, K=64, S=2),
+    dict(T=50, E=12, K=3, renorm=0), dict(T=1, E=1, K=1), dict(T=8192, E=128, K=8, zipf=True),
+]
+
+
+@pytest.mark.parametrize("c", ROUTE_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_route_bitexact(c):
+    T, E, K, S = c["T"], c["E"], c["K"], c.get("S", 0)
+    rsf, rn = c.get("rsf", 1.0), c.get("renorm", 1)
+    g = torch.Generator().manual_seed(T * 7 + E)
+    lg = torch.randn(T, E, generator=g)
+    if c.get("zipf"):
+        lg += -1.1 * torch.log(torch.randperm(E, generator=g).float() + 1.0)
+    say("route", c)
+    ids, w = ml.moe_lora_route(lg.to(DEV), K, S, rsf, rn)
+    torch.cuda.synchronize()
+    oids, ow = oracle.route(lg.numpy(), K, S, rsf, rn)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.array_equal(_bits(w), ow.view(np.int32))
+
+
+def test_route_ties_bitexact():
+    g = torch.Generator().manual_seed(5)
+    lg = (torch.randint(-3, 4, (300, 40), generator=g).float() * 0.5)
+    lg[::7] = 0.0
+    lg[1::7] = -0.0
+    say("route ties")
+    ids, w = ml.moe_lora_route(lg.to(DEV), 6)
+    torch.cuda.synchronize()
+    oids, ow = oracle.route(lg.numpy(), 6)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.array_equal(_bits(w), ow.view(np.int32))
+
+
+# --------------------------------------------------------------------- align
+
+def _align_case(T, E, K, S, L, r, seed, bm=0, lbm=0, adapters="uniform_all", logits="normal", one_expert=False):
+    shape = synth.LayerShape(T=T, H=64, I=64, E=E, K=K, S=S, L=L, r=r)
+    inp = synth.make_inputs(shape, synth.Recipe(adapters=adapters, logits=logits), seed=seed)
+    ids, _ = oracle.route(inp.logits.numpy(), K, S)
+    if one_expert:
+        ids[:, 0] = 0
+    dims = ml.make_dims(T, 64, 64, E, K, S, L, r, block_m=bm, lora_block_m=lbm)
+    return ids, inp.adapter_ids, dims
+
+
+ALIGN_CASES = [
+    dict(T=16, E=4, K=2, S=0, L=2, r=8), dict(T=64, E=32, K=4, S=0, L=8, r=16),
+    dict(T=4096, E=32, K=4, S=0, L=32, r=32, adapters="runs"), dict(T=128, E=64, K=8, S=1, L=0, r=0),
+    dict(T=1, E=64, K=8, S=1, L=0, r=0), dict(T=500, E=6, K=2, S=1, L=3, r=8, bm=32, lbm=32),
+    dict(T=300, E=8, K=3, S=0, L=5, r=8, one_expert=True), dict(T=77, E=5, K=5, S=2, L=1, r=8, bm=16),
+    dict(T=8192, E=128, K=8, S=0, L=64, r=64, adapters="zipf", logits="zipf_bias"),
+    dict(T=200, E=16, K=2, S=0, L=4, r=16, adapters="none"),
+]
+
+
+@pytest.mark.parametrize("c", ALIGN_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_align_bitexact(c):
+    c = dict(c)
+    T, E, K, S, L, r = (c.pop(k) for k in ("T", "E", "K", "S", "L", "r"))
+    ids, ad, dims = _align_case(T, E, K, S, L, r, seed=T + E, **c)
+    say("align", T, E, K, S, L, r, c)
+    g = ml.moe_lora_align(torch.from_numpy(ids).to(DEV), ad.to(DEV), dims)
+    torch.cuda.synchronize()
+    plan = g["plan"]
+    La = L if (L > 0 and r > 0) else 0
+    o = oracle.align(ids, ad.numpy(), E + S, La, plan["block_m"], plan["lora_block_m"])
+    assert int(g["num_post_pad"].item()) == o["num_post_pad"]
+    assert np.array_equal(g["sorted_ids"].cpu().numpy(), o["sorted_ids"])
+    assert np.array_equal(g["block_expert"].cpu().numpy(), o["block_expert"])
+    if La:
+        assert int(g["num_items"].item()) == o["num_items"]
+        assert np.array_equal(g["lora_items"].cpu().numpy(), o["items"])
+
+
+# ------------------------------------------------------------ small forwards
+
+SMALL = [
+    # ragged K (H=200), ragged gate tiles (I=72), several experts/blocks
+    dict(T=40, H=200, I=72, E=6, K=2, S=0, L=3, r=16, dtype="bf16"),
+    dict(T=100, H=256, I=128, E=8, K=3, S=1, L=4, r=32, rsf=2.5, dtype="bf16"),
+    dict(T=300, H=128, I=96, E=4, K=2, S=0, L=2, r=8, dtype="bf16", block_m=64),
+    dict(T=64, H=192, I=160, E=16, K=4, S=0, L=5, r=64, dtype="bf16", block_m=32, lbm=32),
+    dict(T=24, H=136, I=72, E=5, K=2, S=1, L=3, r=16, dtype="bf16", split=3),
+    dict(T=40, H=200, I=72, E=6, K=2, S=0, L=3, r=4, dtype="f32"),
+    dict(T=33, H=64, I=40, E=3, K=3, S=2, L=2, r=5, rsf=2.0, dtype="f32", block_m=32),
+    dict(T=50, H=96, I=64, E=7, K=1, S=0, L=0, r=0, dtype="bf16"),
+]
+
+
+def _shape(c):
+    return synth.LayerShape(T=c["T"], H=c["H"], I=c["I"], E=c["E"], K=c["K"], S=c["S"], L=c["L"], r=c["r"],
+                            rsf=c.get("rsf", 1.0), dtype=c["dtype"])
+
+
+def _kw(c):
+    return dict(block_m=c.get("block_m", 0), lora_block_m=c.get("lbm", 0), split_k=c.get("split", 0))
+
+
+@pytest.mark.parametrize("c", SMALL, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_forward_small_parity(c):
+    shape = _shape(c)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=c["T"])
+    say("forward", c)
+    ids = torch.empty((shape.T, shape.Kp), dtype=torch.int32, device=DEV)
+    w = torch.empty((shape.T, shape.Kp), dtype=torch.float32, device=DEV)
+    out = ml.forward_inputs(inp, routing_out=(ids, w), **_kw(c))
+    torch.cuda.synchronize()
+    ref = oracle.forward_inputs(inp)
+    assert_close(out, ref, shape.dtype, f"forward {c}")
+    oids, ow = oracle.route(inp.logits.cpu().numpy(), shape.K, shape.S, shape.rsf)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.array_equal(_bits(w), ow.view(np.int32))
+    if shape.lora:
+        base = ml.forward_inputs(inp, lora=False, **_kw(c))
+        torch.cuda.synchronize()
+        ref0 = oracle.forward_inputs(inp, lora=False)
+        d_gpu = out.double() - base.double()
+        _, rel = errs(d_gpu, ref - ref0)
+        assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"
+
+
+def test_lora_off_is_bitwise_base():
+    """Zero B or every adapter -1 gives exactly the base layer (compared with ==)."""
+    shape = synth.LayerShape(T=96, H=256, I=128, E=8, K=2, L=4, r=16)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=3)
+    say("lora-off bitwise")
+    base = ml.forward_inputs(inp, lora=False).clone()
+    zb = ml.moe_lora_forward(inp.x, inp.logits, inp.adapter_ids, inp.w13, inp.w2, inp.a13,
+                             torch.zeros_like(inp.b13), inp.a2, torch.zeros_like(inp.b2), K=2).clone()
+    none = ml.moe_lora_forward(inp.x, inp.logits, torch.full_like(inp.adapter_ids, -1), inp.w13, inp.w2,
+                               inp.a13, inp.b13, inp.a2, inp.b2, K=2).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(zb, base)
+    assert torch.equal(none, base)
+
+
+def test_run_to_run_bitwise():
+    shape = synth.LayerShape(T=256, H=512, I=256, E=16, K=4, S=1, L=6, r=16, rsf=2.5)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=9)
+    say("determinism")
+    a = ml.forward_inputs(inp).clone()
+    b = ml.forward_inputs(inp).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_and_single_token():
+    shape = synth.LayerShape(T=0, H=64, I=64, E=4, K=2, L=2, r=8)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"))
+    say("T=0")
+    out = ml.forward_inputs(inp)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+    shape = synth.LayerShape(T=1, H=64, I=64, E=4, K=2, S=1, L=2, r=8, rsf=2.0)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=1)
+    inp.adapter_ids.fill_(1)
+    say("T=1")
+    out = ml.forward_inputs(inp)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.forward_inputs(inp), synth.BF16, "T=1")
+
+
+def test_all_tokens_one_expert():
+    """Degenerate routing: every token's top-1 is expert 0 (one huge expert group)."""
+    shape = synth.LayerShape(T=700, H=128, I=64, E=8, K=2, L=3, r=8)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=4)
+    inp.logits[:, 0] += 100.0
+    say("one expert")
+    out = ml.forward_inputs(inp)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.forward_inputs(inp), synth.BF16, "one expert")
+
+
+# -------------------------------------------------------- named workloads
+
+def test_tiny_fp32_workload_full():
+    inp = inputs("tiny_fp32_T16")
+    say("tiny_fp32_T16")
+    out = ml.forward_inputs(inp)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.forward_inputs(inp), synth.F32, "tiny_fp32_T16")
+
+
+def _sample_tokens(T, n, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    return np.sort(np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), n - 2, replace=False)]))
+
+
+@pytest.mark.parametrize("name,nsample", [("gptoss_decode_T64", 64), ("gptoss_prefill_T4096", 48),
+                                          ("shared_fused_T1", 1), ("shared_fused_T32", 32),
+                                          ("shared_fused_T128", 32)])
+def test_workload_full_size(name, nsample):
+    """Full-size workload on the GPU: routing and alignment bit-exact over every
+    token, layer output element by element on sampled tokens."""
+    inp = inputs(name)
+    s = inp.shape
+    say("workload", name)
+    ids = torch.empty((s.T, s.Kp), dtype=torch.int32, device=DEV)
+    w = torch.empty((s.T, s.Kp), dtype=torch.float32, device=DEV)
+    out = ml.forward_inputs(inp, routing_out=(ids, w))
+    torch.cuda.synchronize()
+    oids, ow = oracle.route(inp.logits.cpu().numpy(), s.K, s.S, s.rsf)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.array_equal(_bits(w), ow.view(np.int32))
+    dims = ml.make_dims(s.T, s.H, s.I, s.E, s.K, s.S, s.L, s.r, s.rsf)
+    g = ml.moe_lora_align(ids, inp.adapter_ids, dims)
+    torch.cuda.synchronize()
+    La = s.L if s.lora else 0
+    o = oracle.align(oids, inp.adapter_ids.cpu().numpy(), s.Ep, La, g["plan"]["block_m"],
+                     g["plan"]["lora_block_m"])
+    assert np.array_equal(g["sorted_ids"].cpu().numpy(), o["sorted_ids"])
+    assert np.array_equal(g["block_expert"].cpu().numpy(), o["block_expert"])
+    tok = _sample_tokens(s.T, nsample)
+    host = inp.to("cpu")
+    ref = oracle.forward_inputs(host, tokens=tok)
+    assert_close(out[torch.from_numpy(tok).to(DEV)], ref, s.dtype, name)
+    if s.lora:
+        base = ml.forward_inputs(inp, lora=False)
+        torch.cuda.synchronize()
+        ref0 = oracle.forward_inputs(host, tokens=tok, lora=False)
+        sel = torch.from_numpy(tok).to(DEV)
+        _, rel = errs(out[sel].double() - base[sel].double(), ref - ref0)
+        assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"
+
+
+def test_shared_fused_equals_unfused_on_gpu():
+    """Shared slot fused into the grouped GEMM (weight 1/rsf, output x rsf) equals
+    the routed layer times rsf plus a separate dense shared MLP, both on the GPU."""
+    inp = inputs("shared_fused_T32")
+    s = inp.shape
+    say("shared fused vs unfused")
+    fused = ml.forward_inputs(inp)
+    routed = ml.moe_lora_forward(inp.x, inp.logits, None, inp.w13[:s.E].contiguous(), inp.w2[:s.E].contiguous(),
+                                 K=s.K, S=0, rsf=s.rsf)
+    ones = torch.zeros((s.T, 1), dtype=torch.float32, device=DEV)
+    shared = ml.moe_lora_forward(inp.x, ones, None, inp.w13[s.E:].contiguous(), inp.w2[s.E:].contiguous(),
+                                 K=1, S=0, rsf=1.0)
+    torch.cuda.synchronize()
+    host = inp.to("cpu")
+    ref = oracle.forward_inputs(host)
+    assert_close(fused, ref, s.dtype, "fused")
+    unfused = routed.double() + shared.double()
+    maxabs, rel = errs(unfused, ref)
+    assert maxabs <= 2 * 2e-2 and rel <= 1e-2, (maxabs, rel)
