@@ -163,19 +163,37 @@ def layer_roofline(m: dict) -> dict:
             "roofline_us": t_roof * 1e6, "frac_of_roofline": t_roof / t}
 
 
-def cpu_baseline(m: dict, budget_tokens: int) -> dict:
+def cpu_baseline(m: dict, budget_tokens: int, min_wall_s: float = 10.0, max_reps: int = 200) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same layer call:
+    the first `budget_tokens` tokens, repeated until about `min_wall_s` of wall time."""
     import oracle
     s = m["shape"]
     host = m["inp"].to("cpu")
     n = min(s.T, budget_tokens)
     tokens = np.arange(n)
     threads = min(os.cpu_count() or 1, 16)
-    t0 = time.perf_counter()
-    oracle.forward_inputs(host, tokens=tokens, nthreads=threads)
-    wall = time.perf_counter() - t0
-    return {"value": n / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {s.T} tokens of one {m['name']} layer call (fp64 oracle, OpenMP)",
-            "wall_s": wall}
+    reps, wall = 0, 0.0
+    while reps < max_reps and (reps == 0 or wall < min_wall_s):
+        t0 = time.perf_counter()
+        oracle.forward_inputs(host, tokens=tokens, nthreads=threads)
+        wall += time.perf_counter() - t0
+        reps += 1
+    return {"value": n * reps / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {s.T} tokens of one {m['name']} layer call, {reps} repetitions "
+                      f"(fp64 oracle, OpenMP)", "wall_s": wall}
+
+
+def copy_calibration(mib: int, reps: int) -> None:
+    """A plain device-to-device copy of `mib` MiB, `reps` times: the reference
+    kernel whose FETCH_SIZE / WRITE_SIZE counters scale the layer's counters."""
+    n = mib * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reps": reps}), flush=True)
 
 
 def main() -> int:
@@ -187,6 +205,8 @@ def main() -> int:
     ap.add_argument("--prefill", default="gptoss_prefill_T4096", help="secondary workload ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -197,6 +217,9 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
+    if args.copy_calib_mib:
+        copy_calibration(args.copy_calib_mib, args.steps)
+        return 0
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     m = measure(args.workload, args.steps, args.warmup)
     s = m["shape"]

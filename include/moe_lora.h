@@ -82,7 +82,8 @@ extern "C" {
  *      E logits, taken at the K selected ones
  *   dtype  MOE_LORA_BF16 (bf16 tensors, fp32 accumulation) or MOE_LORA_F32
  *   block_m  rows per expert block of the alignment and the GEMM tiles;
- *      0 = library choice from the average rows per expert, else 16, 32 or 64
+ *      0 = library choice from the average rows per expert, else 16 or 32
+ *      (streaming GEMM) or 64 or 128 (LDS-tiled GEMM; bf16 only)
  *   lora_block_m  rows per LoRA shrink work item; 0 = library choice, else
  *      16 or 32 (32 needs r <= 64)
  *   split_k  K-splits of the LoRA shrink; 0 = library choice, else 1..16

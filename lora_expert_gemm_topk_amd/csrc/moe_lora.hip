@@ -25,6 +25,7 @@
 #include "combine.hpp"
 #include "fp32_path.hpp"
 #include "gemm_stream.hpp"
+#include "gemm_tiled.hpp"
 #include "route.hpp"
 #include "shrink.hpp"
 
@@ -85,17 +86,19 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
 
     // tile choice by the average rows per expert; never specialised on T itself
     const int64_t rho = p.P / p.Ep;
-    if (d->block_m != 0 && d->block_m != 16 && d->block_m != 32 && d->block_m != 64) return MOE_LORA_EUNSUPPORTED;
+    if (d->block_m != 0 && d->block_m != 16 && d->block_m != 32 && d->block_m != 64 && d->block_m != 128)
+        return MOE_LORA_EUNSUPPORTED;
     if (d->lora_block_m != 0 && d->lora_block_m != 16 && d->lora_block_m != 32) return MOE_LORA_EUNSUPPORTED;
     if (d->split_k < 0 || d->split_k > 16) return MOE_LORA_EINVAL;
     if (d->dtype == MOE_LORA_F32) {
         p.kind = 0;
         p.bm = d->block_m ? d->block_m : 16;
+        if (p.bm > 64) return MOE_LORA_EUNSUPPORTED;
         p.lbm = d->lora_block_m ? d->lora_block_m : 16;
         p.split = 1;
     } else {
-        p.kind = 1;
-        p.bm = d->block_m ? d->block_m : (rho <= 12 ? 16 : (rho <= 40 ? 32 : 64));
+        p.bm = d->block_m ? d->block_m : (rho <= 12 ? 16 : (rho <= 40 ? 32 : 128));
+        p.kind = p.bm <= 32 ? 1 : 2;
         p.lbm = d->lora_block_m ? d->lora_block_m : (rho <= 40 || d->r > 64 ? 16 : 32);
         if (p.lbm == 32 && d->r > 64) return MOE_LORA_EUNSUPPORTED;
         if (d->split_k) {
@@ -242,14 +245,41 @@ void launch_shrink(const Plan &pl, ShrinkParams sp, bool gather, int r, hipStrea
     }
 }
 
+// Weight rows per tile of the LDS-tiled kernel: the widest of 256 / 192 / 128
+// whose feature count divides N (gate_up tiles hold BW/2 features), else 256.
+int tiled_bw(int N, bool gu) {
+    const int opts[3] = {256, 192, 128};
+    for (int bw : opts)
+        if (N % (gu ? bw / 2 : bw) == 0) return bw;
+    return 256;
+}
+
+template <int BW, int BT, bool GU>
+void launch_tiled(const Plan &pl, const GemmParams &gp, hipStream_t st) {
+    const int n_wt = (gp.Nout + (GU ? BW / 2 : BW) - 1) / (GU ? BW / 2 : BW);
+    const unsigned total = (unsigned)(n_wt * pl.max_blocks);
+    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU>), dim3(total), dim3(256), 0, st, gp, n_wt,
+                       (int)pl.max_blocks);
+}
+
 template <bool GU>
-void launch_gemm_stream(const Plan &pl, const GemmParams &gp, hipStream_t st) {
-    const int tile = GU ? kStreamBW / 2 : kStreamBW;
-    const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
-    switch (pl.bm) {
-        case 16: hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU>), grid, block, 0, st, gp); break;
-        case 32: hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU>), grid, block, 0, st, gp); break;
-        default: hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 64, GU>), grid, block, 0, st, gp); break;
+void launch_gemm(const Plan &pl, const GemmParams &gp, hipStream_t st) {
+    if (pl.kind == 1) {
+        const int tile = GU ? kStreamBW / 2 : kStreamBW;
+        const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
+        if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU>), grid, block, 0, st, gp);
+        else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU>), grid, block, 0, st, gp);
+        return;
+    }
+    const int bw = tiled_bw(gp.Nout, GU);
+    if (pl.bm == 64) {
+        if (bw == 256) launch_tiled<256, 64, GU>(pl, gp, st);
+        else if (bw == 192) launch_tiled<192, 64, GU>(pl, gp, st);
+        else launch_tiled<128, 64, GU>(pl, gp, st);
+    } else {
+        if (bw == 256) launch_tiled<256, 128, GU>(pl, gp, st);
+        else if (bw == 192) launch_tiled<192, 128, GU>(pl, gp, st);
+        else launch_tiled<128, 128, GU>(pl, gp, st);
     }
 }
 
@@ -361,7 +391,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
 
     void **ev = a->stage_events;
     auto mark = [&](int slot) {
-        if (ev) hipEventRecord((hipEvent_t)ev[slot], st);
+        if (ev) (void)hipEventRecord((hipEvent_t)ev[slot], st);
     };
     mark(2 * MOE_LORA_STAGE_ROUTE);
     launch_route(d, a->router_logits, ids, wts, st);
@@ -464,7 +494,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.Kdim = H;
         gp.Nout = I;
         mark(2 * MOE_LORA_STAGE_GATE_UP);
-        launch_gemm_stream<true>(p, gp, st);
+        launch_gemm<true>(p, gp, st);
         mark(2 * MOE_LORA_STAGE_GATE_UP + 1);
         mark(2 * MOE_LORA_STAGE_SHRINK2);
         if (p.lora) {
@@ -483,7 +513,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.Kdim = I;
         gp.Nout = H;
         mark(2 * MOE_LORA_STAGE_DOWN);
-        launch_gemm_stream<false>(p, gp, st);
+        launch_gemm<false>(p, gp, st);
         mark(2 * MOE_LORA_STAGE_DOWN + 1);
         mark(2 * MOE_LORA_STAGE_COMBINE);
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)d->T), dim3(256),

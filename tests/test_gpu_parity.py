@@ -114,6 +114,11 @@ SMALL = [
     dict(T=40, H=200, I=72, E=6, K=2, S=0, L=3, r=4, dtype="f32"),
     dict(T=33, H=64, I=40, E=3, K=3, S=2, L=2, r=5, rsf=2.0, dtype="f32", block_m=32),
     dict(T=50, H=96, I=64, E=7, K=1, S=0, L=0, r=0, dtype="bf16"),
+    # LDS-tiled MFMA kernel: ragged K (200 = 3*64 + 8), ragged weight tiles, r=24 (partial k-step)
+    dict(T=300, H=200, I=200, E=4, K=2, S=0, L=3, r=24, dtype="bf16", block_m=128),
+    dict(T=500, H=256, I=384, E=6, K=2, S=1, L=4, r=32, rsf=2.5, dtype="bf16", block_m=128),
+    dict(T=260, H=192, I=96, E=3, K=2, S=0, L=2, r=16, dtype="bf16", block_m=64, split=2),
+    dict(T=200, H=128, I=128, E=5, K=3, S=0, L=0, r=0, dtype="bf16", block_m=128),
 ]
 
 
@@ -149,27 +154,30 @@ def test_forward_small_parity(c):
         assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"
 
 
-def test_lora_off_is_bitwise_base():
+@pytest.mark.parametrize("bm", [0, 128])
+def test_lora_off_is_bitwise_base(bm):
     """Zero B or every adapter -1 gives exactly the base layer (compared with ==)."""
     shape = synth.LayerShape(T=96, H=256, I=128, E=8, K=2, L=4, r=16)
     inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=3)
-    say("lora-off bitwise")
-    base = ml.forward_inputs(inp, lora=False).clone()
+    say("lora-off bitwise", bm)
+    base = ml.forward_inputs(inp, lora=False, block_m=bm).clone()
     zb = ml.moe_lora_forward(inp.x, inp.logits, inp.adapter_ids, inp.w13, inp.w2, inp.a13,
-                             torch.zeros_like(inp.b13), inp.a2, torch.zeros_like(inp.b2), K=2).clone()
+                             torch.zeros_like(inp.b13), inp.a2, torch.zeros_like(inp.b2), K=2,
+                             block_m=bm).clone()
     none = ml.moe_lora_forward(inp.x, inp.logits, torch.full_like(inp.adapter_ids, -1), inp.w13, inp.w2,
-                               inp.a13, inp.b13, inp.a2, inp.b2, K=2).clone()
+                               inp.a13, inp.b13, inp.a2, inp.b2, K=2, block_m=bm).clone()
     torch.cuda.synchronize()
     assert torch.equal(zb, base)
     assert torch.equal(none, base)
 
 
-def test_run_to_run_bitwise():
+@pytest.mark.parametrize("bm", [0, 128])
+def test_run_to_run_bitwise(bm):
     shape = synth.LayerShape(T=256, H=512, I=256, E=16, K=4, S=1, L=6, r=16, rsf=2.5)
     inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=9)
-    say("determinism")
-    a = ml.forward_inputs(inp).clone()
-    b = ml.forward_inputs(inp).clone()
+    say("determinism", bm)
+    a = ml.forward_inputs(inp, block_m=bm).clone()
+    b = ml.forward_inputs(inp, block_m=bm).clone()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
