@@ -81,9 +81,10 @@ extern "C" {
  *   renormalize  1: softmax over the K selected logits; 0: softmax over all
  *      E logits, taken at the K selected ones
  *   dtype  MOE_LORA_BF16 (bf16 tensors, fp32 accumulation) or MOE_LORA_F32
- *   block_m  rows per expert block of the alignment and the GEMM tiles;
- *      0 = library choice from the average rows per expert, else 16 or 32
- *      (streaming GEMM) or 64 or 128 (LDS-tiled GEMM; bf16 only)
+ *   block_m  token rows per GEMM tile; 0 = library choice from the
+ *      average rows per expert.  16 or 32: streaming GEMM, experts padded to
+ *      block_m rows.  128 or 256 (bf16 only): LDS-tiled GEMM, experts padded
+ *      to 32 rows and cut into tiles of at most block_m rows
  *   lora_block_m  rows per LoRA shrink work item; 0 = library choice, else
  *      16 or 32 (32 needs r <= 64)
  *   split_k  K-splits of the LoRA shrink; 0 = library choice, else 1..16
@@ -103,7 +104,8 @@ typedef struct moe_lora_dims {
  * moe_lora_plan_query).  block_m / lora_block_m / max_blocks /
  * sorted_capacity / max_items also size the outputs of moe_lora_align. */
 typedef struct moe_lora_plan {
-    int32_t block_m;         /* expert block rows used by align and the GEMMs */
+    int32_t block_m;         /* alignment block: each expert group is padded to a multiple of it */
+    int32_t tile_m;          /* token rows per GEMM tile */
     int32_t lora_block_m;    /* rows per LoRA work item */
     int32_t split_k;         /* LoRA shrink K-splits */
     int32_t gemm_kind;       /* 0 = fp32 path, 1 = bf16 streaming, 2 = bf16 LDS-tiled */

@@ -15,6 +15,10 @@
 //   *npp_out                padded row count (num_post_pad)
 //   *nitems_out             LoRA work item count
 //   items[max_items][4]     (start row, rows <= lbm, adapter, expert)
+//   tiles[][4]              optional token tiles for the LDS-tiled GEMM: each
+//                           expert's padded rows cut into runs of at most
+//                           tile_rows rows: (start row, rows | tiles of the
+//                           expert << 16, expert, first tile of the expert)
 //
 // Implementation: one workgroup of NW wavefronts, no host synchronisation
 // and no atomics on anything but LDS integer counters.  A stable sort by a
@@ -40,8 +44,11 @@ struct AlignParams {
     int32_t *nitems_out;
     int32_t *items;
     int32_t *tmp;
+    int32_t *tiles;       // optional GEMM token tiles [max_tiles][4]
+    int32_t *ntiles_out;  // tile count (when tiles != nullptr)
     int P, Kp, Ep, La, bm, lbm;
     int cap, max_blocks, max_items;
+    int tile_rows;
     int nbits_a, nbits_e;
 };
 
@@ -233,6 +240,28 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
             ex = lo;
         }
         p.block_expert[b] = ex;
+    }
+
+    // ---- token tiles of the LDS-tiled GEMM ---------------------------------
+    if (p.tiles != nullptr) {
+        __syncthreads();
+        for (int e = tid; e < Ep; e += nt) tk[e] = (offE[e + 1] - offE[e] + p.tile_rows - 1) / p.tile_rows;
+        __syncthreads();
+        const int ntiles = block_excl_scan(tk, Ep, scr);
+        for (int e = tid; e < Ep; e += nt) {
+            const int pad = offE[e + 1] - offE[e];
+            int it = tk[e];
+            const int t0 = it, nt_e = (pad + p.tile_rows - 1) / p.tile_rows;
+            for (int q = 0; q < pad; q += p.tile_rows) {
+                int4 v;
+                v.x = offE[e] + q;
+                v.y = min(p.tile_rows, pad - q) | (nt_e << 16);
+                v.z = e;
+                v.w = t0;
+                reinterpret_cast<int4 *>(p.tiles)[it++] = v;
+            }
+        }
+        if (tid == 0) *p.ntiles_out = ntiles;
     }
 
     // ---- LoRA work items: (adapter >= 0, expert) runs cut to lbm rows ------

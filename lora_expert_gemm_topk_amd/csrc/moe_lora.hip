@@ -39,14 +39,14 @@ constexpr int kStreamBW = 64;
 thread_local char g_errbuf[320];
 
 struct Plan {
-    int bm = 0, lbm = 0, split = 1, kind = 0;
+    int bm = 0, lbm = 0, split = 1, kind = 0, tile = 0;
     int64_t P = 0, Ep = 0, Kp = 0, La = 0;
-    int64_t max_blocks = 0, cap = 0, max_items = 0;
+    int64_t max_blocks = 0, cap = 0, max_items = 0, max_tiles = 0;
     int align_nw = 16;
     size_t align_lds = 0;
     bool lora = false;
     // workspace offsets (bytes)
-    size_t o_ids = 0, o_w = 0, o_sorted = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0;
+    size_t o_ids = 0, o_w = 0, o_sorted = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0, o_tiles = 0;
     size_t o_s13 = 0, o_s2 = 0, o_h = 0, o_y2 = 0, total = 0;
     size_t align_total = 0;  // tmp + nothing else, for moe_lora_align
 };
@@ -86,19 +86,22 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
 
     // tile choice by the average rows per expert; never specialised on T itself
     const int64_t rho = p.P / p.Ep;
-    if (d->block_m != 0 && d->block_m != 16 && d->block_m != 32 && d->block_m != 64 && d->block_m != 128)
+    if (d->block_m != 0 && d->block_m != 16 && d->block_m != 32 && d->block_m != 128 && d->block_m != 256)
         return MOE_LORA_EUNSUPPORTED;
     if (d->lora_block_m != 0 && d->lora_block_m != 16 && d->lora_block_m != 32) return MOE_LORA_EUNSUPPORTED;
     if (d->split_k < 0 || d->split_k > 16) return MOE_LORA_EINVAL;
     if (d->dtype == MOE_LORA_F32) {
         p.kind = 0;
         p.bm = d->block_m ? d->block_m : 16;
-        if (p.bm > 64) return MOE_LORA_EUNSUPPORTED;
+        if (p.bm > 32) return MOE_LORA_EUNSUPPORTED;
+        p.tile = p.bm;
         p.lbm = d->lora_block_m ? d->lora_block_m : 16;
         p.split = 1;
     } else {
-        p.bm = d->block_m ? d->block_m : (rho <= 12 ? 16 : (rho <= 40 ? 32 : 128));
-        p.kind = p.bm <= 32 ? 1 : 2;
+        const int tm = d->block_m ? d->block_m : (rho <= 12 ? 16 : (rho <= 40 ? 32 : (rho < 192 ? 128 : 256)));
+        p.kind = tm <= 32 ? 1 : 2;
+        p.bm = tm <= 32 ? tm : 32;  // the tiled GEMM pads experts to 32 rows and cuts tiles of tm rows
+        p.tile = tm;
         p.lbm = d->lora_block_m ? d->lora_block_m : (rho <= 40 || d->r > 64 ? 16 : 32);
         if (p.lbm == 32 && d->r > 64) return MOE_LORA_EUNSUPPORTED;
         if (d->split_k) {
@@ -117,6 +120,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
         const int64_t bins = std::min(p.La * p.Ep, p.P);
         p.max_items = (p.P + p.lbm - 1) / p.lbm + bins;
     }
+    if (p.kind == 2) p.max_tiles = (p.P + p.tile - 1) / p.tile + 2 * nz;
     if (p.cap >= (int64_t(1) << 31) - 1) return MOE_LORA_EUNSUPPORTED;
 
     // align workgroup: as many waves as the LDS allows
@@ -146,6 +150,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     p.o_cnt = take(sizeof(int32_t) * 16);
     p.o_items = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_items, 1));
     p.o_tmp = take(sizeof(int32_t) * p.P);
+    p.o_tiles = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_tiles, 1));
     p.o_s13 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
     p.o_s2 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
     p.o_h = take(es * p.cap * d->I);
@@ -186,7 +191,7 @@ int launch_route(const moe_lora_dims *d, const float *logits, int32_t *ids, floa
 
 int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
                  int32_t *sorted, int32_t *bexp, int32_t *npp, int32_t *items, int32_t *nitems, int32_t *tmp,
-                 hipStream_t st) {
+                 int32_t *tiles, int32_t *ntiles, hipStream_t st) {
     std::call_once(g_attr_once, set_kernel_attributes);
     if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
     AlignParams ap;
@@ -198,6 +203,9 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
     ap.nitems_out = nitems;
     ap.items = pl.lora ? items : nullptr;
     ap.tmp = tmp;
+    ap.tiles = tiles;
+    ap.ntiles_out = ntiles;
+    ap.tile_rows = pl.tile;
     ap.P = (int)pl.P;
     ap.Kp = (int)pl.Kp;
     ap.Ep = (int)pl.Ep;
@@ -245,25 +253,31 @@ void launch_shrink(const Plan &pl, ShrinkParams sp, bool gather, int r, hipStrea
     }
 }
 
-// Weight rows per tile of the LDS-tiled kernel: the widest of 256 / 192 / 128
-// whose feature count divides N (gate_up tiles hold BW/2 features), else 256.
+// Weight rows per tile of the LDS-tiled kernel.  256 (16 MFMAs per 8
+// fragment reads per wave) measured fastest for both projections of the
+// GPT-OSS-20B prefill layer even where N is not a multiple of the tile; 128
+// only when N is too small to fill wider tiles.
 int tiled_bw(int N, bool gu) {
-    const int opts[3] = {256, 192, 128};
-    for (int bw : opts)
-        if (N % (gu ? bw / 2 : bw) == 0) return bw;
-    return 256;
+#ifdef MOELORA_TILED_BW
+    (void)N;
+    (void)gu;
+    return MOELORA_TILED_BW;
+#endif
+    const int feats = gu ? N * 2 : N;
+    return feats <= 128 ? 128 : 256;
 }
 
 template <int BW, int BT, bool GU>
-void launch_tiled(const Plan &pl, const GemmParams &gp, hipStream_t st) {
+void launch_tiled(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
+                  hipStream_t st) {
     const int n_wt = (gp.Nout + (GU ? BW / 2 : BW) - 1) / (GU ? BW / 2 : BW);
-    const unsigned total = (unsigned)(n_wt * pl.max_blocks);
-    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU>), dim3(total), dim3(256), 0, st, gp, n_wt,
-                       (int)pl.max_blocks);
+    const unsigned total = (unsigned)(n_wt * pl.max_tiles);
+    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU>), dim3(total), dim3(256), 0, st, gp, tiles, ntiles, n_wt);
 }
 
 template <bool GU>
-void launch_gemm(const Plan &pl, const GemmParams &gp, hipStream_t st) {
+void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
+                 hipStream_t st) {
     if (pl.kind == 1) {
         const int tile = GU ? kStreamBW / 2 : kStreamBW;
         const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
@@ -272,14 +286,14 @@ void launch_gemm(const Plan &pl, const GemmParams &gp, hipStream_t st) {
         return;
     }
     const int bw = tiled_bw(gp.Nout, GU);
-    if (pl.bm == 64) {
-        if (bw == 256) launch_tiled<256, 64, GU>(pl, gp, st);
-        else if (bw == 192) launch_tiled<192, 64, GU>(pl, gp, st);
-        else launch_tiled<128, 64, GU>(pl, gp, st);
+    if (pl.tile == 128) {
+        if (bw == 256) launch_tiled<256, 128, GU>(pl, gp, tiles, ntiles, st);
+        else if (bw == 192) launch_tiled<192, 128, GU>(pl, gp, tiles, ntiles, st);
+        else launch_tiled<128, 128, GU>(pl, gp, tiles, ntiles, st);
     } else {
-        if (bw == 256) launch_tiled<256, 128, GU>(pl, gp, st);
-        else if (bw == 192) launch_tiled<192, 128, GU>(pl, gp, st);
-        else launch_tiled<128, 128, GU>(pl, gp, st);
+        if (bw == 256) launch_tiled<256, 256, GU>(pl, gp, tiles, ntiles, st);
+        else if (bw == 192) launch_tiled<192, 256, GU>(pl, gp, tiles, ntiles, st);
+        else launch_tiled<128, 256, GU>(pl, gp, tiles, ntiles, st);
     }
 }
 
@@ -293,6 +307,7 @@ int moe_lora_plan_query(const moe_lora_dims *dims, moe_lora_plan *plan) {
     if (rc != MOE_LORA_OK) return rc;
     if (!plan) return MOE_LORA_EINVAL;
     plan->block_m = p.bm;
+    plan->tile_m = p.tile;
     plan->lora_block_m = p.lbm;
     plan->split_k = p.split;
     plan->gemm_kind = p.kind;
@@ -362,7 +377,7 @@ int moe_lora_align(const moe_lora_dims *d, const int32_t *topk_ids, const int32_
     int32_t *tmp = (int32_t *)ws;
     int32_t *cnt = (int32_t *)(ws + round_up(sizeof(int32_t) * p.P, 256));
     int r2 = launch_align(p, d, topk_ids, adapter_ids, sorted_ids, block_expert, num_post_pad, lora_items,
-                          num_items ? num_items : cnt + 1, tmp, st);
+                          num_items ? num_items : cnt + 1, tmp, nullptr, nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "align launch");
@@ -397,7 +412,9 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     launch_route(d, a->router_logits, ids, wts, st);
     mark(2 * MOE_LORA_STAGE_ROUTE + 1);
     mark(2 * MOE_LORA_STAGE_ALIGN);
-    int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, bexp, cnt, items, cnt + 1, tmp, st);
+    int32_t *tiles = (int32_t *)(ws + p.o_tiles);
+    int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, bexp, cnt, items, cnt + 1, tmp,
+                          p.kind == 2 ? tiles : nullptr, cnt + 2, st);
     if (r2 != MOE_LORA_OK) return r2;
     mark(2 * MOE_LORA_STAGE_ALIGN + 1);
 
@@ -494,7 +511,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.Kdim = H;
         gp.Nout = I;
         mark(2 * MOE_LORA_STAGE_GATE_UP);
-        launch_gemm<true>(p, gp, st);
+        launch_gemm<true>(p, gp, tiles, cnt + 2, st);
         mark(2 * MOE_LORA_STAGE_GATE_UP + 1);
         mark(2 * MOE_LORA_STAGE_SHRINK2);
         if (p.lora) {
@@ -513,7 +530,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.Kdim = I;
         gp.Nout = H;
         mark(2 * MOE_LORA_STAGE_DOWN);
-        launch_gemm<false>(p, gp, st);
+        launch_gemm<false>(p, gp, tiles, cnt + 2, st);
         mark(2 * MOE_LORA_STAGE_DOWN + 1);
         mark(2 * MOE_LORA_STAGE_COMBINE);
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)d->T), dim3(256),

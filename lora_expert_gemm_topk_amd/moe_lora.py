@@ -38,8 +38,8 @@ class MoeLoraDims(ctypes.Structure):
 
 
 class MoeLoraPlan(ctypes.Structure):
-    _fields_ = [("block_m", ctypes.c_int32), ("lora_block_m", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("gemm_kind", ctypes.c_int32), ("max_blocks", ctypes.c_int64),
+    _fields_ = [("block_m", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("lora_block_m", ctypes.c_int32),
+                ("split_k", ctypes.c_int32), ("gemm_kind", ctypes.c_int32), ("max_blocks", ctypes.c_int64),
                 ("sorted_capacity", ctypes.c_int64), ("max_items", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t), ("align_workspace_bytes", ctypes.c_size_t)]
 

@@ -108,7 +108,7 @@ SMALL = [
     # ragged K (H=200), ragged gate tiles (I=72), several experts/blocks
     dict(T=40, H=200, I=72, E=6, K=2, S=0, L=3, r=16, dtype="bf16"),
     dict(T=100, H=256, I=128, E=8, K=3, S=1, L=4, r=32, rsf=2.5, dtype="bf16"),
-    dict(T=300, H=128, I=96, E=4, K=2, S=0, L=2, r=8, dtype="bf16", block_m=64),
+    dict(T=300, H=128, I=96, E=4, K=2, S=0, L=2, r=8, dtype="bf16", block_m=256),
     dict(T=64, H=192, I=160, E=16, K=4, S=0, L=5, r=64, dtype="bf16", block_m=32, lbm=32),
     dict(T=24, H=136, I=72, E=5, K=2, S=1, L=3, r=16, dtype="bf16", split=3),
     dict(T=40, H=200, I=72, E=6, K=2, S=0, L=3, r=4, dtype="f32"),
@@ -117,7 +117,7 @@ SMALL = [
     # LDS-tiled MFMA kernel: ragged K (200 = 3*64 + 8), ragged weight tiles, r=24 (partial k-step)
     dict(T=300, H=200, I=200, E=4, K=2, S=0, L=3, r=24, dtype="bf16", block_m=128),
     dict(T=500, H=256, I=384, E=6, K=2, S=1, L=4, r=32, rsf=2.5, dtype="bf16", block_m=128),
-    dict(T=260, H=192, I=96, E=3, K=2, S=0, L=2, r=16, dtype="bf16", block_m=64, split=2),
+    dict(T=260, H=192, I=96, E=3, K=2, S=0, L=2, r=16, dtype="bf16", block_m=256, split=2),
     dict(T=200, H=128, I=128, E=5, K=3, S=0, L=0, r=0, dtype="bf16", block_m=128),
 ]
 
