@@ -23,15 +23,18 @@
 // Implementation: one workgroup of NW wavefronts, no host synchronisation
 // and no atomics on anything but LDS integer counters.  A stable sort by a
 // composite key is done as two stable counting passes (least significant
-// key first): by adapter+1 into `tmp`, then by expert into sorted_ids.  Each
-// pass gives every wave a contiguous segment of the input; a wave walks its
-// segment 64 pairs at a time in order, finds equal keys inside the wave with
-// bit-sliced ballots, and keeps one running cursor per key in LDS.  Per-wave
-// histograms plus a scan over (key, wave) make every position depend only on
-// the input, so the result is deterministic and stable.
+// key first): by adapter+1, then by expert.  Each pass gives every wave a
+// contiguous segment of the input; a wave walks its segment 64 pairs at a
+// time in order, finds equal keys inside the wave with bit-sliced ballots,
+// and keeps one running cursor per key in LDS.  Per-wave histograms plus a
+// scan over (key, wave) make every position depend only on the input, so the
+// result is deterministic and stable.  When the pairs fit, the per-pair
+// expert and adapter keys and the intermediate order live in LDS as 16-bit
+// values (one bulk load instead of four passes of dependent global loads).
 #pragma once
 
 #include "common.hpp"
+#include "route.hpp"
 
 namespace moelora {
 
@@ -43,32 +46,37 @@ struct AlignParams {
     int32_t *npp_out;
     int32_t *nitems_out;
     int32_t *items;
-    int32_t *tmp;
+    int32_t *tmp;         // [P] global scratch (used when the keys do not fit in LDS)
     int32_t *tiles;       // optional GEMM token tiles [max_tiles][4]
     int32_t *ntiles_out;  // tile count (when tiles != nullptr)
-    int P, Kp, Ep, La, bm, lbm;
+    int T, P, Kp, Ep, La, bm, lbm;
     int cap, max_blocks, max_items;
     int tile_rows;
     int nbits_a, nbits_e;
+    int lds_keys;         // 1: stage keys and the intermediate order in LDS
 };
 
 // Ids outside their documented ranges (a precondition) are clamped so that
 // they can never index memory out of bounds: an adapter outside [-1, La)
 // counts as "no LoRA", an expert outside [0, Ep) as the nearest valid one.
-__device__ __forceinline__ int adapter_key(const AlignParams &p, int f) {
-    const int a = p.adapter_ids[f / p.Kp];
-    return (a >= 0 && a < p.La) ? a + 1 : 0;
-}
-__device__ __forceinline__ int expert_of(const AlignParams &p, int f) {
-    return min(max(p.topk_ids[f], 0), p.Ep - 1);
-}
+__device__ __forceinline__ int adapter_key_of(int a, int La) { return (a >= 0 && a < La) ? a + 1 : 0; }
+__device__ __forceinline__ int clamp_expert(int e, int Ep) { return min(max(e, 0), Ep - 1); }
 
-// LDS ints used by align_kernel for a given shape and wave count.
-__host__ __device__ inline int64_t align_lds_ints(int NW, int Ep, int La) {
+// ints of LDS before the staged keys (histograms, offsets, scan scratch, LoRA counts)
+__host__ __device__ inline int64_t align_lds_fixed_ints(int NW, int Ep, int La) {
     const int64_t nk = (int64_t)Ep * (La + 1);
     const int64_t tk = (Ep > La + 1 ? Ep : La + 1) + 1;
     int64_t n = (int64_t)NW * (La + 1) + (int64_t)NW * Ep + 2 * (int64_t)Ep + 1 + tk + 80;
     if (La > 0) n += 2 * nk + 1;
+    return n;
+}
+
+// LDS ints of the alignment; with lds_keys the 16-bit keys follow:
+// expert of each pair [P], order after the adapter pass [P], adapter+1 of
+// each token [T].
+__host__ __device__ inline int64_t align_lds_ints(int NW, int Ep, int La, int64_t T, int64_t P, bool lds_keys) {
+    int64_t n = align_lds_fixed_ints(NW, Ep, La);
+    if (lds_keys) n += (2 * P + T + 1) / 2 + 1;
     return n;
 }
 
@@ -111,14 +119,23 @@ __device__ inline int block_excl_scan(int *arr, int n, int *scr) {
     return total;
 }
 
-__global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
-    extern __shared__ int lds[];
+// Where the staged 16-bit keys start inside the alignment's LDS.
+__device__ __forceinline__ uint16_t *align_keys(int *lds, int NW, int Ep, int La) {
+    return reinterpret_cast<uint16_t *>(lds + align_lds_fixed_ints(NW, Ep, La));
+}
+
+// The alignment proper, run by one whole workgroup.  With p.lds_keys the
+// keys are bulk-loaded into LDS first unless `keys_ready` says the caller
+// already put them there.
+__device__ void align_body(const AlignParams &p, int *lds, bool keys_ready) {
     const int NW = (int)(blockDim.x >> 6);
     const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
     const int lane = tid & 63, w = tid >> 6;
     const int La = p.La, Ep = p.Ep, A1 = La + 1;
     const int NK = Ep * A1;
     const int TK = (Ep > A1 ? Ep : A1) + 1;
+    const int P = p.P;
+    const bool lk = p.lds_keys != 0;
 
     int *histA = lds;                    // [NW][A1]
     int *histB = histA + NW * A1;        // [NW][Ep]
@@ -128,6 +145,19 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
     int *scr = tk + TK;                  // [80]
     int *cnt2 = scr + 80;                // [NK]      (La > 0)
     int *itemOff = cnt2 + NK;            // [NK+1]    (La > 0)
+    uint16_t *eL = align_keys(lds, NW, Ep, La);  // [P] expert of pair f
+    uint16_t *oL = eL + P;                       // [P] order after the adapter pass
+    uint16_t *aL = oL + P;                       // [T] adapter+1 of token t
+
+    if (lk && !keys_ready) {
+        for (int f = tid; f < P; f += nt) eL[f] = (uint16_t)clamp_expert(p.topk_ids[f], Ep);
+        for (int t = tid; t < p.T; t += nt) aL[t] = (uint16_t)(La > 0 ? adapter_key_of(p.adapter_ids[t], La) : 0);
+    }
+    auto get_e = [&](int f) -> int { return lk ? (int)eL[f] : clamp_expert(p.topk_ids[f], Ep); };
+    auto get_a1 = [&](int f) -> int {
+        return lk ? (int)aL[f / p.Kp] : adapter_key_of(p.adapter_ids[f / p.Kp], La);
+    };
+    auto get_order = [&](int i) -> int { return La > 0 ? (lk ? (int)oL[i] : p.tmp[i]) : i; };
 
     const int nzero = NW * A1 + NW * Ep + (La > 0 ? NK : 0);
     for (int i = tid; i < nzero; i += nt) {
@@ -136,20 +166,19 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
     }
     __syncthreads();
 
-    const int P = p.P;
     const int seg = (P + NW - 1) / NW;
     const int s0 = min(P, w * seg), s1 = min(P, s0 + seg);
 
-    // ---- pass A: stable counting sort by adapter+1 into tmp ------------
+    // ---- pass A: stable counting sort by adapter+1 ------------------------
     if (La > 0) {
         for (int base = s0; base < s1; base += 64) {
             const int f = base + lane;
             const bool valid = f < s1;
-            const int a1 = valid ? adapter_key(p, f) : 0;
+            const int a1 = valid ? get_a1(f) : 0;
             const uint64_t m = match_key((uint32_t)a1, valid, p.nbits_a);
             if (valid) {
                 if ((m & lanemask_lt()) == 0) histA[w * A1 + a1] += __popcll(m);
-                atomicAdd(&cnt2[expert_of(p, f) * A1 + a1], 1);
+                atomicAdd(&cnt2[get_e(f) * A1 + a1], 1);
             }
         }
         __syncthreads();
@@ -169,11 +198,12 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
         for (int base = s0; base < s1; base += 64) {
             const int f = base + lane;
             const bool valid = f < s1;
-            const int a1 = valid ? adapter_key(p, f) : 0;
+            const int a1 = valid ? get_a1(f) : 0;
             const uint64_t m = match_key((uint32_t)a1, valid, p.nbits_a);
             if (valid) {
                 const int pos = histA[w * A1 + a1] + __popcll(m & lanemask_lt());
-                p.tmp[pos] = f;
+                if (lk) oL[pos] = (uint16_t)f;
+                else p.tmp[pos] = f;
                 if ((m & lanemask_lt()) == 0) histA[w * A1 + a1] += __popcll(m);
             }
         }
@@ -185,8 +215,8 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
     for (int base = s0; base < s1; base += 64) {
         const int i = base + lane;
         const bool valid = i < s1;
-        const int f = valid ? (La > 0 ? p.tmp[i] : i) : 0;
-        const int e = valid ? expert_of(p, f) : 0;
+        const int f = valid ? get_order(i) : 0;
+        const int e = valid ? get_e(f) : 0;
         const uint64_t m = match_key((uint32_t)e, valid, p.nbits_e);
         if (valid && (m & lanemask_lt()) == 0) histB[w * Ep + e] += __popcll(m);
     }
@@ -211,8 +241,8 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
     for (int base = s0; base < s1; base += 64) {
         const int i = base + lane;
         const bool valid = i < s1;
-        const int f = valid ? (La > 0 ? p.tmp[i] : i) : 0;
-        const int e = valid ? expert_of(p, f) : 0;
+        const int f = valid ? get_order(i) : 0;
+        const int e = valid ? get_e(f) : 0;
         const uint64_t m = match_key((uint32_t)e, valid, p.nbits_e);
         if (valid) {
             const int pos = histB[w * Ep + e] + __popcll(m & lanemask_lt());
@@ -305,6 +335,33 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
         *p.npp_out = npp;
         *p.nitems_out = nitems;
     }
+}
+
+__global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
+    extern __shared__ int lds[];
+    align_body(p, lds, false);
+}
+
+// Routing and alignment in one workgroup, for calls small enough that one
+// launch is cheaper than two: every wave routes tokens w, w+NW, ... (the
+// routing rule of route.hpp), writes ids and weights to global memory and
+// the per-pair expert keys straight into LDS, then the workgroup aligns.
+// Needs p.lds_keys.
+template <int VPL>
+__global__ __launch_bounds__(1024) void route_align_kernel(RouteParams rp, AlignParams p) {
+    extern __shared__ int lds[];
+    const int NW = (int)(blockDim.x >> 6);
+    const int w = (int)(threadIdx.x >> 6), lane = lane_id();
+    uint16_t *eL = align_keys(lds, NW, p.Ep, p.La);
+    uint16_t *aL = eL + 2 * p.P;
+    for (int t = w; t < rp.T; t += NW) {
+        const int id = route_one_token<VPL>(rp, t);
+        if (lane < p.Kp) eL[t * p.Kp + lane] = (uint16_t)clamp_expert(id, p.Ep);
+    }
+    for (int t = (int)threadIdx.x; t < p.T; t += (int)blockDim.x)
+        aL[t] = (uint16_t)(p.La > 0 ? adapter_key_of(p.adapter_ids[t], p.La) : 0);
+    __syncthreads();
+    align_body(p, lds, true);
 }
 
 }  // namespace moelora

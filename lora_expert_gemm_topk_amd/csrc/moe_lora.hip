@@ -34,7 +34,10 @@ using namespace moelora;
 namespace {
 
 constexpr int64_t kLdsBytes = 160 * 1024;
-constexpr int kStreamBW = 64;
+#ifndef MOELORA_STREAM_BW
+#define MOELORA_STREAM_BW 64
+#endif
+constexpr int kStreamBW = MOELORA_STREAM_BW;  // weight rows per streaming-GEMM workgroup
 
 thread_local char g_errbuf[320];
 
@@ -44,6 +47,8 @@ struct Plan {
     int64_t max_blocks = 0, cap = 0, max_items = 0, max_tiles = 0;
     int align_nw = 16;
     size_t align_lds = 0;
+    bool lds_keys = false;   // alignment keys staged in LDS
+    bool fuse_route = false; // route + align in one launch
     bool lora = false;
     // workspace offsets (bytes)
     size_t o_ids = 0, o_w = 0, o_sorted = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0, o_tiles = 0;
@@ -108,7 +113,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
             p.split = d->split_k;
         } else {
             const int64_t ch = (std::max(d->H, d->I) + 31) / 32;
-            p.split = (d->T <= 512) ? (int)std::min<int64_t>(4, std::max<int64_t>(1, ch / 16)) : 1;
+            p.split = (d->T <= 512) ? (int)std::min<int64_t>(2, std::max<int64_t>(1, ch / 16)) : 1;
         }
     }
     if (!lora) p.split = 1;
@@ -123,17 +128,30 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     if (p.kind == 2) p.max_tiles = (p.P + p.tile - 1) / p.tile + 2 * nz;
     if (p.cap >= (int64_t(1) << 31) - 1) return MOE_LORA_EUNSUPPORTED;
 
-    // align workgroup: as many waves as the LDS allows
+    // align workgroup: as many waves as the LDS allows, keys staged in LDS
+    // when they fit (16-bit pair indices need P < 65536)
+    // a small call needs few waves: one 64-pair step per wave and pass
+#ifndef MOELORA_ALIGN_MAXNW
+#define MOELORA_ALIGN_MAXNW 16
+#endif
+    int nw_max = MOELORA_ALIGN_MAXNW;
+    while (nw_max > 4 && (int64_t)(nw_max / 2) * 64 >= p.P) nw_max /= 2;
     p.align_nw = 0;
-    for (int nw = 16; nw >= 1; nw >>= 1) {
-        const int64_t bytes = align_lds_ints(nw, (int)p.Ep, (int)p.La) * 4;
-        if (bytes <= kLdsBytes) {
-            p.align_nw = nw;
-            p.align_lds = (size_t)bytes;
-            break;
+    for (int pass = 0; pass < 2 && p.align_nw == 0; ++pass) {
+        const bool lk = pass == 0;
+        if (lk && p.P >= 65536) continue;
+        for (int nw = nw_max; nw >= (lk ? 4 : 1); nw >>= 1) {
+            const int64_t bytes = align_lds_ints(nw, (int)p.Ep, (int)p.La, d->T, p.P, lk) * 4;
+            if (bytes <= kLdsBytes) {
+                p.align_nw = nw;
+                p.align_lds = (size_t)bytes;
+                p.lds_keys = lk;
+                break;
+            }
         }
     }
     if (p.align_nw == 0) return MOE_LORA_EUNSUPPORTED;
+    p.fuse_route = false;  // measured slower than two launches: one workgroup routes tokens serially
 
     const size_t A = 256;
     const size_t es = d->dtype == MOE_LORA_BF16 ? 2 : 4;
@@ -172,29 +190,50 @@ std::once_flag g_attr_once;
 hipError_t g_attr_err = hipSuccess;
 
 void set_kernel_attributes() {
-    g_attr_err = hipFuncSetAttribute((const void *)align_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kLdsBytes);
+    const void *fns[] = {(const void *)align_kernel, (const void *)route_align_kernel<1>,
+                         (const void *)route_align_kernel<2>, (const void *)route_align_kernel<4>,
+                         (const void *)route_align_kernel<8>, (const void *)route_align_kernel<16>};
+    for (const void *fn : fns) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        if (e != hipSuccess) g_attr_err = e;
+    }
+}
+
+RouteParams route_params(const moe_lora_dims *d, const float *logits, int32_t *ids, float *w) {
+    RouteParams rp;
+    rp.logits = logits;
+    rp.T = (int)d->T;
+    rp.E = (int)d->E;
+    rp.K = (int)d->K;
+    rp.S = (int)d->S;
+    rp.shared_w = 1.0f / d->routed_scaling_factor;
+    rp.renorm = d->renormalize;
+    rp.ids = ids;
+    rp.wts = w;
+    return rp;
 }
 
 int launch_route(const moe_lora_dims *d, const float *logits, int32_t *ids, float *w, hipStream_t st) {
-    const int T = (int)d->T, E = (int)d->E;
-    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
-    const float shared_w = 1.0f / d->routed_scaling_factor;
-    const int K = (int)d->K, S = (int)d->S, rn = d->renormalize;
-    if (E <= 64) hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
-    else if (E <= 128) hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
-    else if (E <= 256) hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
-    else if (E <= 512) hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
-    else hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, st, logits, T, E, K, S, shared_w, rn, ids, w);
+    const RouteParams rp = route_params(d, logits, ids, w);
+    const dim3 grid((unsigned)((rp.T + 3) / 4)), block(256);
+    const int E = rp.E;
+    if (E <= 64) hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, st, rp);
+    else if (E <= 128) hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, st, rp);
+    else if (E <= 256) hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, st, rp);
+    else if (E <= 512) hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, st, rp);
+    else hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, st, rp);
     return MOE_LORA_OK;
 }
 
+// Alignment (and, with `route` non-null, the routing in the same launch).
 int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
                  int32_t *sorted, int32_t *bexp, int32_t *npp, int32_t *items, int32_t *nitems, int32_t *tmp,
-                 int32_t *tiles, int32_t *ntiles, hipStream_t st) {
+                 int32_t *tiles, int32_t *ntiles, const RouteParams *route, hipStream_t st) {
     std::call_once(g_attr_once, set_kernel_attributes);
     if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
     AlignParams ap;
+    ap.T = (int)d->T;
+    ap.lds_keys = pl.lds_keys ? 1 : 0;
     ap.topk_ids = ids;
     ap.adapter_ids = adapter_ids;
     ap.sorted_ids = sorted;
@@ -217,8 +256,17 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
     ap.max_items = (int)pl.max_items;
     ap.nbits_a = bits_for(pl.La + 1);
     ap.nbits_e = bits_for(pl.Ep);
-    (void)d;
-    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(pl.align_nw * 64), pl.align_lds, st, ap);
+    const dim3 grid(1), block((unsigned)(pl.align_nw * 64));
+    if (route != nullptr) {
+        const int E = route->E;
+        if (E <= 64) hipLaunchKernelGGL(route_align_kernel<1>, grid, block, pl.align_lds, st, *route, ap);
+        else if (E <= 128) hipLaunchKernelGGL(route_align_kernel<2>, grid, block, pl.align_lds, st, *route, ap);
+        else if (E <= 256) hipLaunchKernelGGL(route_align_kernel<4>, grid, block, pl.align_lds, st, *route, ap);
+        else if (E <= 512) hipLaunchKernelGGL(route_align_kernel<8>, grid, block, pl.align_lds, st, *route, ap);
+        else hipLaunchKernelGGL(route_align_kernel<16>, grid, block, pl.align_lds, st, *route, ap);
+    } else {
+        hipLaunchKernelGGL(align_kernel, grid, block, pl.align_lds, st, ap);
+    }
     return MOE_LORA_OK;
 }
 
@@ -377,7 +425,7 @@ int moe_lora_align(const moe_lora_dims *d, const int32_t *topk_ids, const int32_
     int32_t *tmp = (int32_t *)ws;
     int32_t *cnt = (int32_t *)(ws + round_up(sizeof(int32_t) * p.P, 256));
     int r2 = launch_align(p, d, topk_ids, adapter_ids, sorted_ids, block_expert, num_post_pad, lora_items,
-                          num_items ? num_items : cnt + 1, tmp, nullptr, nullptr, st);
+                          num_items ? num_items : cnt + 1, tmp, nullptr, nullptr, nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "align launch");
@@ -408,13 +456,14 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     auto mark = [&](int slot) {
         if (ev) (void)hipEventRecord((hipEvent_t)ev[slot], st);
     };
+    int32_t *tiles = (int32_t *)(ws + p.o_tiles);
+    const RouteParams rp = route_params(d, a->router_logits, ids, wts);
     mark(2 * MOE_LORA_STAGE_ROUTE);
-    launch_route(d, a->router_logits, ids, wts, st);
+    if (!p.fuse_route) launch_route(d, a->router_logits, ids, wts, st);
     mark(2 * MOE_LORA_STAGE_ROUTE + 1);
     mark(2 * MOE_LORA_STAGE_ALIGN);
-    int32_t *tiles = (int32_t *)(ws + p.o_tiles);
     int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, bexp, cnt, items, cnt + 1, tmp,
-                          p.kind == 2 ? tiles : nullptr, cnt + 2, st);
+                          p.kind == 2 ? tiles : nullptr, cnt + 2, p.fuse_route ? &rp : nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;
     mark(2 * MOE_LORA_STAGE_ALIGN + 1);
 

@@ -14,6 +14,15 @@
 
 namespace moelora {
 
+struct RouteParams {
+    const float *logits;  // [T, E]
+    int T, E, K, S;
+    float shared_w;       // fl32(1/rsf)
+    int renorm;
+    int32_t *ids;         // [T, K+S]
+    float *wts;           // [T, K+S]
+};
+
 struct Cand {
     float v;
     int i;  // expert index; INT_MAX = none
@@ -25,14 +34,14 @@ __device__ __forceinline__ bool better(const Cand &a, const Cand &b) {
     return a.v > b.v || (a.v == b.v && a.i < b.i);
 }
 
+// Route token t with the whole wavefront; writes ids and weights of its K+S
+// slots and returns to lane j the expert id of slot j (-1 for j >= K+S; slots
+// beyond lane 63 are written but not returned).
 template <int VPL>
-__global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int T, int E, int K,
-                                                    int S, float shared_w, int renorm,
-                                                    int32_t *__restrict__ ids, float *__restrict__ wts) {
+__device__ int route_one_token(const RouteParams &rp, int t) {
     const int lane = lane_id();
-    const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (t >= T) return;
-    const float *l = logits + (int64_t)t * E;
+    const int E = rp.E, K = rp.K, S = rp.S;
+    const float *l = rp.logits + (int64_t)t * E;
     float v[VPL];
     bool live[VPL];
 #pragma unroll
@@ -42,7 +51,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
         v[j] = live[j] ? l[e] : 0.0f;
     }
     float myv = 0.0f;
-    int myi = 0;
+    int myi = -1;
     for (int s = 0; s < K; ++s) {
         Cand c{0.0f, 0x7fffffff};
 #pragma unroll
@@ -69,20 +78,29 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
     const double m = (double)__shfl(myv, 0, 64);
     const double ex = (lane < K) ? exp((double)myv - m) : 0.0;
     double sum = 0.0;
-    if (renorm) {
+    if (rp.renorm) {
         for (int j = 0; j < K; ++j) sum += __shfl(ex, j, 64);
     } else {
         for (int e = 0; e < E; ++e) sum += exp((double)l[e] - m);
     }
     const int Kp = K + S;
     if (lane < K) {
-        ids[(int64_t)t * Kp + lane] = myi;
-        wts[(int64_t)t * Kp + lane] = (float)(ex / sum);
+        rp.ids[(int64_t)t * Kp + lane] = myi;
+        rp.wts[(int64_t)t * Kp + lane] = (float)(ex / sum);
     }
     if (lane < S) {
-        ids[(int64_t)t * Kp + K + lane] = E + lane;
-        wts[(int64_t)t * Kp + K + lane] = shared_w;
+        rp.ids[(int64_t)t * Kp + K + lane] = E + lane;
+        rp.wts[(int64_t)t * Kp + K + lane] = rp.shared_w;
     }
+    if (lane >= K) myi = (lane < Kp) ? E + (lane - K) : -1;
+    return myi;
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_kernel(RouteParams rp) {
+    const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (t >= rp.T) return;
+    route_one_token<VPL>(rp, t);
 }
 
 }  // namespace moelora

@@ -77,20 +77,30 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
     const int nch = (int)((Kd + 31) / 32);
     const int c_beg = blockIdx.y * p.chunks_per_split;
     const int c_end = min(nch, c_beg + p.chunks_per_split);
-    for (int c = c_beg + w; c < c_end; c += 4) {
-        const int64_t k0 = (int64_t)c * 32 + g * 8;
-        const bool kin = k0 < Kd;  // Kdim is a multiple of 8
-        u32x4 av[MT], xv[NT];
+    // Chunks c_beg + w, +4, +8, ... go to wave w; a wave issues the loads of
+    // kBatch chunks before their MFMAs so its memory requests overlap (chunks
+    // past the end load zeros, whose products add exact zeros).
+    constexpr int kBatch = 4;
+    for (int c = c_beg + w; c < c_end; c += 4 * kBatch) {
+        u32x4 av[kBatch][MT], xv[kBatch][NT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) av[mt] = ld16(arow[mt] + k0, aok[mt] && kin);
+        for (int u = 0; u < kBatch; ++u) {
+            const int cc = c + 4 * u;
+            const int64_t k0 = (int64_t)cc * 32 + g * 8;
+            const bool kin = cc < c_end && k0 < Kd;  // Kdim is a multiple of 8
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) xv[nt] = ld16(xrow[nt] + k0, xok[nt] && kin);
+            for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16(arow[mt] + k0, aok[mt] && kin);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int nt = 0; nt < NT; ++nt) xv[u][nt] = ld16(xrow[nt] + k0, xok[nt] && kin);
+        }
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[mt]), as_bf16x8(xv[nt]),
-                                                                      acc[mt][nt], 0, 0, 0);
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][mt]), as_bf16x8(xv[u][nt]),
+                                                                          acc[mt][nt], 0, 0, 0);
     }
     // D layout: lane holds rank rows 4*g .. 4*g+3 of column (token) l16.
 #pragma unroll
