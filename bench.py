@@ -14,10 +14,13 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
+from pathlib import Path
 
 import numpy as np
 import torch
@@ -29,6 +32,34 @@ from lora_expert_gemm_topk_amd import synth
 METRIC = "MoE-LoRA layer tokens/s (decode T=64, prefill T=4096); % HBM/MFMA roofline"
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # FLOP/s, MI355X dense bf16
+
+ROOT = Path(__file__).resolve().parent
+CSRC = ROOT / "lora_expert_gemm_topk_amd" / "csrc"
+# the dominant kernels' sources and their launch code: a recorded counter
+# reading stays valid only while these are unchanged
+KERNEL_SOURCES = ("common.hpp", "gemm_stream.hpp", "gemm_tiled.hpp", "moe_lora.hip")
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(name.encode())
+        h.update((CSRC / name).read_bytes())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str, kernel: str) -> float | None:
+    """HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE) recorded in the
+    counter summary under profiles/, or None if there is none or the kernel's
+    sources have changed since it was taken."""
+    path = ROOT / "profiles" / f"hbm_counters_{workload}.md"
+    if not path.exists():
+        return None
+    m = re.search(rf"^traffic {re.escape(workload)} {kernel} bytes=(\d+) sources_sha256=([0-9a-f]+)$",
+                  path.read_text(), re.M)
+    if not m or m.group(2) != kernel_sources_sha256():
+        return None
+    return float(m.group(1))
 
 
 # ------------------------------------------------------------ work counting
@@ -142,16 +173,20 @@ def measure(name: str, steps: int, warmup: int, seed: int = 0) -> dict:
 
 def roofline_obj(m: dict, bound: str) -> dict:
     st = m["stage"]["gate_up"] * 1e-3
+    kern = ("gemm_stream" if m["plan"]["block_m"] <= 32 else "gemm_tiled") + \
+        " gate_up (+LoRA expand13, SwiGLU)"
+    traffic = recorded_traffic(m["name"], "gate_up")
     if bound == "hbm":
         ach = m["work"]["bytes_gate_up"] / st
-        return {"kernel": "gemm_stream gate_up (+LoRA expand13, SwiGLU)", "bound": "hbm",
+        return {"kernel": kern, "bound": "hbm",
                 "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": ach / HBM_PEAK,
-                "traffic": None, "kernel_us": st * 1e6,
+                "traffic": traffic, "kernel_us": st * 1e6,
                 "algorithmic_bytes": m["work"]["bytes_gate_up"]}
     ach = m["work"]["flops_gate_up"] / st
-    return {"kernel": "gemm_stream gate_up (+LoRA expand13, SwiGLU)", "bound": "mfma",
+    return {"kernel": kern, "bound": "mfma",
             "achieved": ach / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK,
-            "traffic": None, "kernel_us": st * 1e6, "algorithmic_flops": m["work"]["flops_gate_up"]}
+            "traffic": traffic, "kernel_us": st * 1e6, "algorithmic_flops": m["work"]["flops_gate_up"],
+            "algorithmic_bytes": m["work"]["bytes_gate_up"]}
 
 
 def layer_roofline(m: dict) -> dict:
@@ -257,7 +292,7 @@ def main() -> int:
         result["prefill"] = {"workload": args.prefill, "tokens_per_s": ps.T / (p["ms"] * 1e-3),
                              "ms_per_step": p["ms"], "roofline": roofline_obj(p, "mfma"),
                              "layer": layer_roofline(p), "stage_us": {k: v * 1e3 for k, v in p["stage"].items()},
-                             "block_m": p["plan"]["block_m"]}
+                             "block_m": p["plan"]["block_m"], "work": p["work"]}
     print(json.dumps(result), flush=True)
     return 0
 
