@@ -87,7 +87,9 @@ extern "C" {
  *      to 32 rows and cut into tiles of at most block_m rows
  *   lora_block_m  rows per LoRA shrink work item; 0 = library choice, else
  *      16 or 32 (32 needs r <= 64)
- *   split_k  K-splits of the LoRA shrink; 0 = library choice, else 1..16
+ *   split_k  K-splits of the LoRA shrink; 0 = library choice, else 1..16.
+ *      Applies to the streaming GEMM only: with the LDS-tiled GEMM the
+ *      shrink runs unsplit (the plan reports 1)
  * Limits: (E+S) * (La+1) <= 16384 where La = L if LoRA is active else 0;
  *   L <= 1024; T*(K+S) < 2^31 - 1. */
 typedef struct moe_lora_dims {

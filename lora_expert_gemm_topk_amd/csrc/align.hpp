@@ -11,6 +11,8 @@
 //
 // Layout produced (the contract with the GEMM and shrink kernels):
 //   sorted_ids[cap]         pair index f, or the sentinel P in the padding
+//   sorted_adapter[cap]     optional: adapter of each sorted row, -1 for
+//                           no LoRA and in the padding
 //   block_expert[maxb]      expert of each block of bm rows, -1 after the end
 //   *npp_out                padded row count (num_post_pad)
 //   *nitems_out             LoRA work item count
@@ -42,6 +44,7 @@ struct AlignParams {
     const int32_t *topk_ids;
     const int32_t *adapter_ids;
     int32_t *sorted_ids;
+    int32_t *sorted_adapter;  // optional [cap]
     int32_t *block_expert;
     int32_t *npp_out;
     int32_t *nitems_out;
@@ -247,6 +250,7 @@ __device__ void align_body(const AlignParams &p, int *lds, bool keys_ready) {
         if (valid) {
             const int pos = histB[w * Ep + e] + __popcll(m & lanemask_lt());
             p.sorted_ids[pos] = f;
+            if (p.sorted_adapter) p.sorted_adapter[pos] = get_a1(f) - 1;
             if ((m & lanemask_lt()) == 0) histB[w * Ep + e] += __popcll(m);
         }
     }
@@ -254,9 +258,15 @@ __device__ void align_body(const AlignParams &p, int *lds, bool keys_ready) {
     // ---- padding, tail and block -> expert map ---------------------------
     for (int e = w; e < Ep; e += NW) {
         const int b = offE[e] + totE[e], end = offE[e + 1];
-        for (int q = b + lane; q < end; q += 64) p.sorted_ids[q] = P;
+        for (int q = b + lane; q < end; q += 64) {
+            p.sorted_ids[q] = P;
+            if (p.sorted_adapter) p.sorted_adapter[q] = -1;
+        }
     }
-    for (int q = npp + tid; q < p.cap; q += nt) p.sorted_ids[q] = P;
+    for (int q = npp + tid; q < p.cap; q += nt) {
+        p.sorted_ids[q] = P;
+        if (p.sorted_adapter) p.sorted_adapter[q] = -1;
+    }
     for (int b = tid; b < p.max_blocks; b += nt) {
         const int pos = b * p.bm;
         int ex = -1;

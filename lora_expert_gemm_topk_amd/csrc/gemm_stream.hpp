@@ -31,12 +31,13 @@ namespace moelora {
 struct GemmParams {
     const uint16_t *in;          // gate_up: x [T, Kdim]; down: h [cap, Kdim]
     const int32_t *sorted_ids;   // [cap]
+    const int32_t *sorted_adapter; // [cap] adapter per sorted row (LDS-tiled kernel only)
     const int32_t *block_expert; // [max_blocks]
     const int32_t *counters;     // [0] = padded row count
     const int32_t *adapter_ids;  // [T]
     const uint16_t *W;           // gate_up: w13 [Ep, 2*Nout, Kdim]; down: w2 [Ep, Nout, Kdim]
     const uint16_t *B;           // gate_up: b13 [L, Ep, 2*Nout, r]; down: b2 [L, Ep, Nout, r]
-    const float *s_part;         // [split][cap][r]
+    const float *s_part;         // [split][cap][r] fp32; LDS-tiled kernel: bf16 [cap][r]
     void *out;                   // gate_up: h bf16 [cap, Nout]; down: y2 f32 [P, Nout]
     int Kdim, Nout, Kp, P, cap, Ep, L, r, split, lora;
 };

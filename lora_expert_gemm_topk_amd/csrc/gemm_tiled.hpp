@@ -1,5 +1,5 @@
 // Grouped expert GEMM for many rows per expert (prefill): LDS-tiled, matrix
-// cores (v_mfma_f32_32x32x16_bf16), LoRA expand and SwiGLU in the epilogue.
+// cores (v_mfma_f32_32x32x16_bf16); LoRA expand as extra K slabs, SwiGLU in the epilogue.
 //
 // Same contract as the streaming kernel (gemm_stream.hpp): weights are the
 // MFMA M side, the expert's tokens the N side, y13 -> SwiGLU -> h (bf16,
@@ -36,13 +36,11 @@
 // accumulator gives each lane 4 consecutive rows, so every lane holds whole
 // (gate, up) pairs and SwiGLU needs no data exchange.
 //
-// LoRA expand (aitrends.kr summary of the AWS multi-LoRA MoE post, "section
-// details": LoRA sum folded into the expand step) runs as extra MFMA k-steps
-// on the same accumulators after the main loop: for each adapter present in a
-// 32-token column tile, A = B13/B2 rows of (adapter, expert), B = the shrink
-// result of that tile's tokens carrying the adapter (others zero).  The
-// alignment groups an expert's tokens by adapter, so a column tile usually
-// sees one or two adapters.
+// LoRA expand runs as extra K slabs of the same ring and MFMAs, one per
+// adapter present in the token tile and 32 rank columns (see `issue`), so it
+// costs a few slabs of the main loop's kind and no separate epilogue pass.
+// This needs, per sorted row, the adapter (written by the alignment) and the
+// shrink result in bf16 (written by an unsplit shrink).
 //
 // Workgroups are numbered so that each XCD (8 per MI355X, dispatched round
 // robin) receives one contiguous range of work in expert-major order (expert,
@@ -100,6 +98,12 @@ __device__ __forceinline__ int swz(int row, int c) { return row * 64 + (swz_slot
 
 // Wait until at most N direct-to-LDS loads of this wave are still in flight,
 // then barrier; the memory clobber pins every LDS access to its side.
+// Barrier for LDS data only: waits for this wave's LDS accesses, not for its
+// loads in flight.  (__syncthreads also waits for every outstanding global
+// load, and placed before the K loop it leads the compiler to drain all slab
+// loads before each fragment read of the loop.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -139,6 +143,15 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // MFMA column tiles of this wave that hold at least one sorted row
     const int nt_live = max(0, min(NT, (nrows - wn * (BT / 2) + 31) / 32));
 
+    // ---- token metadata and the tile's adapter list ----------------------
+    // tok_f / tok_a: pair index and adapter of each tile row (P / -1 past the
+    // tile's rows); alist: the adapters present, ascending (the alignment
+    // sorts an expert's rows by adapter, so each is one run of rows).
+    __shared__ int tok_f[BT], tok_a[BT], alist[BT], wcnt[5];
+    const int my_row = row0 + min(tid, nrows - 1);
+    const int f_row = (tid < BT) ? p.sorted_ids[my_row] : p.P;
+    const int a_row = (p.lora && tid < BT) ? p.sorted_adapter[my_row] : -1;
+
     // ---- direct-to-LDS stage loads ----------------------------------------
     // One wave instruction fills 16 rows x 64 bytes (1 KiB) of a stage; wave w
     // owns instructions w, w+4, ...  Lane l writes row R0 + l/4, slot l&3,
@@ -168,17 +181,52 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         }
         src[j] = row + c * 8;
     }
+    const int nk = (int)((Kd + kTileBK - 1) / kTileBK);
+    const int rs = (p.r + kTileBK - 1) / kTileBK;  // LoRA slabs per adapter
     typedef __attribute__((address_space(3))) unsigned char lds_t;
     lds_t *lds_base = (lds_t *)lds;
+    auto dma = [&](const void *g, lds_t *stage, int j) {
+        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(stage + (w + 4 * j) * 1024),
+                                         16, 0, 0);
+    };
+    // Slab kt < nk: K columns [32 kt, 32 kt + 32) of the weights and tokens.
+    // Slab nk + q (LoRA expand, aitrends.kr summary of the AWS multi-LoRA MoE
+    // post, "section details": the LoRA sum folded into the expand step):
+    // rank columns [32 rc, 32 rc + 32) of adapter alist[q / rs], rc = q % rs;
+    // the weight side holds B13/B2 rows of (adapter, expert), the token side
+    // the bf16 shrink rows of the tokens carrying that adapter and zeros for
+    // every other token, so the same MFMAs add exactly the expand term.
     auto issue = [&](int kt) {
-        const int64_t k0 = (int64_t)kt * kTileBK;
         lds_t *stage = lds_base + (kt % kStages) * STAGE_BYTES;
+        if (kt < nk) {
+            const int64_t k0 = (int64_t)kt * kTileBK;
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) {
+                const bool kin = k0 + chunk_of[j] * 8 < Kd;
+                dma(kin ? (const void *)(src[j] + k0) : (const void *)g_zero_chunk, stage, j);
+            }
+            return;
+        }
+        const int q = kt - nk;
+        const int ai = q / rs;
+        const int kk0 = (q - ai * rs) * kTileBK;
+        const int a = __builtin_amdgcn_readfirstlane(alist[ai]);
+        const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r;
+        const uint16_t *s16 = reinterpret_cast<const uint16_t *>(p.s_part);
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const bool kin = k0 + chunk_of[j] * 8 < Kd;
-            const void *g = kin ? (const void *)(src[j] + k0) : (const void *)g_zero_chunk;
-            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(stage + (w + 4 * j) * 1024),
-                                             16, 0, 0);
+            const int rr = (w + 4 * j) * 16 + (lane >> 2);
+            const int kk = kk0 + chunk_of[j] * 8;
+            const void *g = g_zero_chunk;
+            if (rr < BW) {
+                bool ok;
+                const int grow = tile_weight_row<GU>(rr, i0, N, ok);
+                if (ok && kk < p.r) g = Bae + (int64_t)grow * p.r + kk;
+            } else {
+                const int j_tok = rr - BW;
+                if (j_tok < nrows && kk < p.r && tok_a[j_tok] == a) g = s16 + (int64_t)(row0 + j_tok) * p.r + kk;
+            }
+            dma(g, stage, j);
         }
     };
 
@@ -213,17 +261,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mt]), as_bf16x8(bfr[nt]),
                                                                       acc[mt][nt], 0, 0, 0);
     };
-    const int nk = (int)((Kd + kTileBK - 1) / kTileBK);
-    // The whole K loop, specialised on the live column tiles so it has no
-    // branches.  Two fragment register sets alternate: while the MFMAs of one
-    // k-step run, the reads of the next are in flight.  The barrier that makes
-    // slab kt+1 visible sits between the two k-steps of slab kt, so the first
-    // reads of slab kt+1 overlap the second half of slab kt's MFMAs.  The slab
-    // refilled right after that barrier, (kt + kStages - 1) mod kStages ==
-    // (kt - 1) mod kStages, was last read before the previous barrier, so
-    // every wave is done with it.
     // Wait for this wave's loads of the slab needed next, given `younger`
-    // younger slabs that may stay in flight, then barrier.
+    // younger slabs that may stay in flight, then barrier.  Loads issued before
+    // the slabs (token metadata) are older than all of them, so they only make
+    // a wait longer, never shorter.
     auto wait_slab = [&](int younger) {
         static_assert(kStages <= 6, "extend the wait ladder");
         if (younger >= 4) wait_vm_barrier<4 * LPW>();
@@ -232,20 +273,54 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         else if (younger == 1) wait_vm_barrier<LPW>();
         else wait_vm_barrier<0>();
     };
+
+    // Ring prologue: the K slabs first; the adapter list is built while they
+    // are in flight, then any LoRA slabs the prologue still has to issue.
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nk) issue(s);
+    if (tid < BT) {
+        tok_f[tid] = tid < nrows ? f_row : p.P;
+        tok_a[tid] = (tid < nrows && a_row < p.L) ? a_row : -1;
+    }
+    lds_barrier();
+    {
+        const int a = tid < BT ? tok_a[tid] : -1;
+        const bool start = a >= 0 && (tid == 0 || tok_a[tid - 1] != a);
+        const uint64_t m = __ballot(start);
+        if (lane == 0) wcnt[w] = __popcll(m);
+        lds_barrier();
+        int before = 0;
+        for (int v = 0; v < w; ++v) before += wcnt[v];
+        if (start) alist[before + __popcll(m & lanemask_lt())] = a;
+        if (tid == 0) wcnt[4] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+        lds_barrier();
+    }
+    const int n_adapters = __builtin_amdgcn_readfirstlane(wcnt[4]);
+    const int nk_tot = nk + (p.lora ? n_adapters * rs : 0);
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s >= nk && s < nk_tot) issue(s);
+
+    // The whole K loop, specialised on the live column tiles so it has no
+    // branches.  Two fragment register sets alternate: while the MFMAs of one
+    // k-step run, the reads of the next are in flight.  The barrier that makes
+    // slab kt+1 visible sits between the two k-steps of slab kt, so the first
+    // reads of slab kt+1 overlap the second half of slab kt's MFMAs.  The slab
+    // refilled right after that barrier, (kt + kStages - 1) mod kStages ==
+    // (kt - 1) mod kStages, was last read before the previous barrier, so
+    // every wave is done with it.
     auto mainloop = [&](auto ntl) {
         u32x4 a0[MT], b0[NT], a1[MT], b1[NT];
-#pragma unroll
-        for (int s = 0; s < kStages - 1; ++s)
-            if (s < nk) issue(s);
-        wait_slab(min(kStages - 2, nk - 1));
+        wait_slab(min(kStages - 2, nk_tot - 1));
         rd(ntl, a0, b0, 0, 0);
-        for (int kt = 0; kt < nk; ++kt) {
+        for (int kt = 0; kt < nk_tot; ++kt) {
             rd(ntl, a1, b1, kt % kStages, 1);
             mm(ntl, a0, b0);
-            if (kt + 1 < nk) {
-                // issued so far: slabs 0 .. min(kt + kStages - 2, nk - 1)
-                wait_slab(min(kStages - 3, nk - 2 - kt));
-                if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+            if (kt + 1 < nk_tot) {
+                // issued so far: slabs 0 .. min(kt + kStages - 2, nk_tot - 1)
+                wait_slab(min(kStages - 3, nk_tot - 2 - kt));
+                if (kt + kStages - 1 < nk_tot) issue(kt + kStages - 1);
                 rd(ntl, a0, b0, (kt + 1) % kStages, 0);
             }
             mm(ntl, a1, b1);
@@ -259,72 +334,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         default: mainloop(std::integral_constant<int, NT>{}); break;
     }
 
-    // ---- LoRA expand: extra MFMA k-steps per adapter present --------------
-    int prow_t[NT], f_t[NT], a_t[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int j_tok = wn * (BT / 2) + nt * 32 + l32;
-        prow_t[nt] = row0 + min(j_tok, nrows - 1);
-        const int f = p.sorted_ids[prow_t[nt]];
-        f_t[nt] = (j_tok < nrows) ? f : p.P;
-        int a = -1;
-        if (p.lora && f_t[nt] < p.P) {
-            a = p.adapter_ids[f_t[nt] / p.Kp];
-            if (a >= p.L) a = -1;
-        }
-        a_t[nt] = a;
-    }
-    if (p.lora) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            if (nt >= nt_live) break;
-            uint64_t remaining = __ballot(a_t[nt] >= 0);
-            while (remaining) {
-                const int src_lane = __ffsll((unsigned long long)remaining) - 1;
-                const int a = __shfl(a_t[nt], src_lane, 64);
-                const bool mine = a_t[nt] == a;
-                remaining &= ~__ballot(mine);
-                const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r;
-                for (int k0 = 0; k0 < p.r; k0 += 16) {
-                    const int kk = k0 + lh * 8;
-                    const bool kin = kk < p.r;
-                    float s[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) s[i] = 0.f;
-                    if (mine && kin) {
-                        for (int sp = 0; sp < p.split; ++sp) {
-                            const float4 *sv = reinterpret_cast<const float4 *>(
-                                p.s_part + ((int64_t)sp * p.cap + prow_t[nt]) * p.r + kk);
-                            const float4 lo = sv[0], hi = sv[1];
-                            s[0] += lo.x; s[1] += lo.y; s[2] += lo.z; s[3] += lo.w;
-                            s[4] += hi.x; s[5] += hi.y; s[6] += hi.z; s[7] += hi.w;
-                        }
-                    }
-                    u32x4 sb;
-                    sb[0] = pack_bf16x2(s[0], s[1]);
-                    sb[1] = pack_bf16x2(s[2], s[3]);
-                    sb[2] = pack_bf16x2(s[4], s[5]);
-                    sb[3] = pack_bf16x2(s[6], s[7]);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        bool ok;
-                        const int grow = tile_weight_row<GU>(wm * (BW / 2) + mt * 32 + l32, i0, N, ok);
-                        const u32x4 bw = ld16(Bae + (int64_t)(ok ? grow : 0) * p.r + kk, ok && kin);
-                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bw), as_bf16x8(sb),
-                                                                              acc[mt][nt], 0, 0, 0);
-                    }
-                }
-            }
-        }
-    }
-
     // ---- epilogue --------------------------------------------------------
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         if (nt >= nt_live) break;
         const int j_tok = wn * (BT / 2) + nt * 32 + l32;
         if (j_tok >= nrows) continue;
-        const int prow = prow_t[nt], f = f_t[nt];
+        const int prow = row0 + j_tok, f = tok_f[j_tok];
         const bool valid = f < p.P;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {

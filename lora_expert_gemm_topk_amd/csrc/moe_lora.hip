@@ -51,7 +51,7 @@ struct Plan {
     bool fuse_route = false; // route + align in one launch
     bool lora = false;
     // workspace offsets (bytes)
-    size_t o_ids = 0, o_w = 0, o_sorted = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0, o_tiles = 0;
+    size_t o_ids = 0, o_w = 0, o_sorted = 0, o_sadp = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0, o_tiles = 0;
     size_t o_s13 = 0, o_s2 = 0, o_h = 0, o_y2 = 0, total = 0;
     size_t align_total = 0;  // tmp + nothing else, for moe_lora_align
 };
@@ -116,7 +116,9 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
             p.split = (d->T <= 512) ? (int)std::min<int64_t>(2, std::max<int64_t>(1, ch / 16)) : 1;
         }
     }
-    if (!lora) p.split = 1;
+    // The tiled kernel streams the shrink result through its LDS ring as bf16
+    // rows, so the shrink runs unsplit and rounds its fp32 sums there.
+    if (!lora || p.kind == 2) p.split = 1;
 
     const int64_t nz = std::min(p.Ep, p.P);
     p.max_blocks = (p.P + p.bm - 1) / p.bm + nz;
@@ -164,6 +166,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     p.o_ids = take(sizeof(int32_t) * p.P);
     p.o_w = take(sizeof(float) * p.P);
     p.o_sorted = take(sizeof(int32_t) * p.cap);
+    p.o_sadp = take(p.kind == 2 ? sizeof(int32_t) * p.cap : 0);
     p.o_bexp = take(sizeof(int32_t) * p.max_blocks);
     p.o_cnt = take(sizeof(int32_t) * 16);
     p.o_items = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_items, 1));
@@ -227,8 +230,9 @@ int launch_route(const moe_lora_dims *d, const float *logits, int32_t *ids, floa
 
 // Alignment (and, with `route` non-null, the routing in the same launch).
 int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
-                 int32_t *sorted, int32_t *bexp, int32_t *npp, int32_t *items, int32_t *nitems, int32_t *tmp,
-                 int32_t *tiles, int32_t *ntiles, const RouteParams *route, hipStream_t st) {
+                 int32_t *sorted, int32_t *sorted_adapter, int32_t *bexp, int32_t *npp, int32_t *items,
+                 int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles, const RouteParams *route,
+                 hipStream_t st) {
     std::call_once(g_attr_once, set_kernel_attributes);
     if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
     AlignParams ap;
@@ -237,6 +241,7 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
     ap.topk_ids = ids;
     ap.adapter_ids = adapter_ids;
     ap.sorted_ids = sorted;
+    ap.sorted_adapter = sorted_adapter;
     ap.block_expert = bexp;
     ap.npp_out = npp;
     ap.nitems_out = nitems;
@@ -424,7 +429,7 @@ int moe_lora_align(const moe_lora_dims *d, const int32_t *topk_ids, const int32_
     char *ws = (char *)workspace;
     int32_t *tmp = (int32_t *)ws;
     int32_t *cnt = (int32_t *)(ws + round_up(sizeof(int32_t) * p.P, 256));
-    int r2 = launch_align(p, d, topk_ids, adapter_ids, sorted_ids, block_expert, num_post_pad, lora_items,
+    int r2 = launch_align(p, d, topk_ids, adapter_ids, sorted_ids, nullptr, block_expert, num_post_pad, lora_items,
                           num_items ? num_items : cnt + 1, tmp, nullptr, nullptr, nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;
     const hipError_t e = hipGetLastError();
@@ -442,6 +447,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     int32_t *ids = a->topk_ids_out ? a->topk_ids_out : (int32_t *)(ws + p.o_ids);
     float *wts = a->topk_weights_out ? a->topk_weights_out : (float *)(ws + p.o_w);
     int32_t *sorted = (int32_t *)(ws + p.o_sorted);
+    int32_t *sadp = (int32_t *)(ws + p.o_sadp);
     int32_t *bexp = (int32_t *)(ws + p.o_bexp);
     int32_t *cnt = (int32_t *)(ws + p.o_cnt);
     int32_t *items = (int32_t *)(ws + p.o_items);
@@ -462,7 +468,8 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     if (!p.fuse_route) launch_route(d, a->router_logits, ids, wts, st);
     mark(2 * MOE_LORA_STAGE_ROUTE + 1);
     mark(2 * MOE_LORA_STAGE_ALIGN);
-    int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, bexp, cnt, items, cnt + 1, tmp,
+    int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt, items,
+                          cnt + 1, tmp,
                           p.kind == 2 ? tiles : nullptr, cnt + 2, p.fuse_route ? &rp : nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;
     mark(2 * MOE_LORA_STAGE_ALIGN + 1);
@@ -530,6 +537,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         sp.Kp = (int)p.Kp;
         sp.P = (int)p.P;
         sp.cap = (int)p.cap;
+        sp.out_bf16 = p.kind == 2 ? 1 : 0;
         mark(2 * MOE_LORA_STAGE_SHRINK13);
         if (p.lora) {
             sp.in = (const uint16_t *)a->hidden;
@@ -541,6 +549,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         mark(2 * MOE_LORA_STAGE_SHRINK13 + 1);
         GemmParams gp;
         gp.sorted_ids = sorted;
+        gp.sorted_adapter = sadp;
         gp.block_expert = bexp;
         gp.counters = cnt;
         gp.adapter_ids = a->adapter_ids;

@@ -8,8 +8,10 @@
 // `split` workgroups (grid.y) and, inside a workgroup, across its 4
 // wavefronts.  Partials go to s_part[split][row][r] in fp32 and are summed
 // in fixed order by the consumer (the expand in the next GEMM's epilogue), so
-// the result does not depend on scheduling.  Items past the item count exit
-// at once: a layer call whose tokens carry no adapter does no shrink work.
+// the result does not depend on scheduling.  For the LDS-tiled GEMM the
+// shrink runs unsplit and writes its sums rounded once to bf16, the operand
+// type the tiled kernel streams.  Items past the item count exit at once: a
+// layer call whose tokens carry no adapter does no shrink work.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16): the MFMA M side is the
 // rank index k (A rows), the N side is the item's rows (tokens), K is the
@@ -26,8 +28,9 @@ struct ShrinkParams {
     const uint16_t *A;         // [L, Ep, r, Kdim]
     const int32_t *items;      // [max_items][4]
     const int32_t *counters;   // [1] = item count
-    float *s_part;             // [split][cap][r]
+    float *s_part;             // [split][cap][r] fp32, or [cap][r] bf16 when out_bf16
     int Kdim, r, Ep, Kp, P, cap;
+    int out_bf16;              // 1: split == 1, write the sum rounded once to bf16
     int chunks_per_split;      // in units of 32 along Kdim
 };
 
@@ -112,11 +115,13 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
     __syncthreads();
     const int R4 = (p.r + 3) / 4;
     float *dst = p.s_part + ((int64_t)blockIdx.y * p.cap + p0) * p.r;
+    uint16_t *dst16 = reinterpret_cast<uint16_t *>(p.s_part) + (int64_t)p0 * p.r;
     for (int q = (int)threadIdx.x; q < len * R4; q += 256) {
         const int j = q / R4, k = (q % R4) * 4;
         for (int i = 0; i < 4 && k + i < p.r; ++i) {
             const float v = ((red[0][j][k + i] + red[1][j][k + i]) + red[2][j][k + i]) + red[3][j][k + i];
-            dst[(int64_t)j * p.r + k + i] = v;
+            if (p.out_bf16) dst16[(int64_t)j * p.r + k + i] = f32_to_bf16(v);
+            else dst[(int64_t)j * p.r + k + i] = v;
         }
     }
 }
