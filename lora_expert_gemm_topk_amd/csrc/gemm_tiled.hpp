@@ -62,6 +62,7 @@ constexpr int kTileBK = 32;   // K per LDS stage
 #define MOELORA_TILED_STAGES 4
 #endif
 constexpr int kStages = MOELORA_TILED_STAGES;  // LDS ring depth
+static_assert(kStages >= 3, "the K loop keeps at least two slabs in flight");
 
 // 16 bytes of zeros: the source of every load past the end of K
 __device__ __attribute__((aligned(16))) const uint16_t g_zero_chunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -310,11 +311,33 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // refilled right after that barrier, (kt + kStages - 1) mod kStages ==
     // (kt - 1) mod kStages, was last read before the previous barrier, so
     // every wave is done with it.
+    // A K slab that lies wholly inside K, branch-free: the steady-state loop
+    // below is then a single basic block the compiler can schedule as a whole
+    // (measured ~15% faster than one loop with the slab-kind and end-of-K
+    // branches inside).
+    auto issue_full = [&](int kt) {
+        lds_t *stage = lds_base + (kt % kStages) * STAGE_BYTES;
+        const int64_t k0 = (int64_t)kt * kTileBK;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) dma(src[j] + k0, stage, j);
+    };
+    const int nk_full = (int)(Kd / kTileBK);
     auto mainloop = [&](auto ntl) {
         u32x4 a0[MT], b0[NT], a1[MT], b1[NT];
         wait_slab(min(kStages - 2, nk_tot - 1));
         rd(ntl, a0, b0, 0, 0);
-        for (int kt = 0; kt < nk_tot; ++kt) {
+        int kt = 0;
+        // steady state: each iteration refills the ring with a full K slab
+        for (; kt + kStages - 1 < nk_full; ++kt) {
+            rd(ntl, a1, b1, kt % kStages, 1);
+            mm(ntl, a0, b0);
+            wait_vm_barrier<(kStages - 3) * LPW>();
+            rd(ntl, a0, b0, (kt + 1) % kStages, 0);
+            issue_full(kt + kStages - 1);
+            mm(ntl, a1, b1);
+        }
+        // the rest: LoRA slabs and the drain of the ring
+        for (; kt < nk_tot; ++kt) {
             rd(ntl, a1, b1, kt % kStages, 1);
             mm(ntl, a0, b0);
             if (kt + 1 < nk_tot) {
