@@ -60,4 +60,23 @@ __device__ __forceinline__ u32x4 ld16(const void *p, bool ok) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Packed operand layout ("row groups x K slabs").  Rows are taken in groups of
+// 16 and K in slabs of 32; each (group, slab) pair is one 1 KiB block, blocks
+// group-major (a group's slabs are consecutive).  Inside a block, element
+// (r, k) sits at element index (k/8)*128 + r*8 + k%8: 16-byte chunk
+// (k/8)*16 + r.  That is the per-lane order of a v_mfma_f32_16x16x32_bf16
+// operand fragment (lane = (k/8)*16 + r holds 8 consecutive k of row r), so a
+// wave fetches a whole fragment with one 16-byte load per lane reading 1 KiB
+// contiguously, and an LDS copy of a block serves 32x32x16 fragment reads
+// without bank conflicts (16 consecutive lanes read 256 contiguous bytes).
+// K past the last element of a slab is zero.
+constexpr int kGroupRows = 16;
+constexpr int kSlabK = 32;
+constexpr int kBlockElems = kGroupRows * kSlabK;  // 512 bf16 = 1 KiB
+
+// Element offset of (row, k) in a packed matrix with `nslab` slabs per group.
+__host__ __device__ __forceinline__ int64_t packed_off(int64_t row, int64_t k, int64_t nslab) {
+    return ((row >> 4) * nslab + (k >> 5)) * kBlockElems + ((k >> 3) & 3) * 128 + (row & 15) * 8 + (k & 7);
+}
+
 }  // namespace moelora

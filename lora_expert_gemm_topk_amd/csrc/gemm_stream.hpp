@@ -29,7 +29,7 @@
 namespace moelora {
 
 struct GemmParams {
-    const uint16_t *in;          // gate_up: x [T, Kdim]; down: h [cap, Kdim]
+    const uint16_t *in;          // gate_up: x [T, Kdim]; down: h [cap, Kdim] (LDS-tiled kernel: h packed)
     const int32_t *sorted_ids;   // [cap]
     const int32_t *sorted_adapter; // [cap] adapter per sorted row (LDS-tiled kernel only)
     const int32_t *block_expert; // [max_blocks]
@@ -38,7 +38,7 @@ struct GemmParams {
     const uint16_t *W;           // gate_up: w13 [Ep, 2*Nout, Kdim]; down: w2 [Ep, Nout, Kdim]
     const uint16_t *B;           // gate_up: b13 [L, Ep, 2*Nout, r]; down: b2 [L, Ep, Nout, r]
     const float *s_part;         // [split][cap][r] fp32; LDS-tiled kernel: bf16 [cap][r]
-    void *out;                   // gate_up: h bf16 [cap, Nout]; down: y2 f32 [P, Nout]
+    void *out;                   // gate_up: h bf16 [cap, Nout] (LDS-tiled kernel: packed); down: y2 f32 [P, Nout]
     int Kdim, Nout, Kp, P, cap, Ep, L, r, split, lora;
 };
 

@@ -21,15 +21,15 @@
 // rows x 64 bytes, filled by gfx950's direct global->LDS loads
 // (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16*l), so no
 // registers stage the data and kStages-1 slabs are in flight while the MFMAs
-// work on the oldest one.  Each wave waits only for its own loads of the slab
+// work on the oldest one.  One load instruction fills one 16-row group of a
+// stage: from a packed operand (h for down) it copies one 1 KiB block, from a
+// row-major one lane l fetches chunk l/16 of row l%16.  Each wave waits only for its own loads of the slab
 // it needs next (s_waitcnt vmcnt with the number of younger slabs still
 // allowed in flight) and then meets the others at one barrier per slab; the
 // wait and the barrier are one asm statement with a memory clobber, which
 // keeps the compiler from moving LDS accesses across the barrier without the
-// vmcnt(0) a fenced barrier would force.  The four 16-byte chunks of a row
-// are XOR-swizzled (swz_slot) so that the fragment reads of 8 or 16
-// consecutive lanes (consecutive rows, same chunk) hit distinct 16-byte slots.
-// K beyond the reduction length reads a 16-byte zero chunk.
+// vmcnt(0) a fenced barrier would force.  K beyond the reduction length reads
+// a 16-byte zero chunk (row-major operands) or the zero tail of a packed slab.
 //
 // gate_up row order inside a tile: rows 4a, 4a+1 hold gate features
 // i0+2a, i0+2a+1 and rows 4a+2, 4a+3 the matching up features.  The 32 x 32
@@ -89,16 +89,34 @@ __device__ __forceinline__ int tile_weight_row(int rr, int i0, int N, bool &ok) 
     return feat;
 }
 
-// byte offset of 16-byte chunk `c` (0..3) of LDS row `row` inside a stage.
-// The XOR term makes 8 consecutive rows (same c) fall in 8 different 16-byte
-// slots of a 128-byte window AND 16 consecutive rows in 16 different slots of
-// a 256-byte window, so fragment reads are conflict-free whether the LDS
-// serves 8 or 16 lanes of a 16-byte read per cycle.
+// Byte offset of 16-byte chunk `c` (0..3) of LDS row `row` inside a stage.
+// A 16-row group of a stage is 1 KiB in one of two layouts:
+//  * row-major (rows copied from a row-major operand): 4 consecutive lanes of
+//    a copy fetch one row's 64 contiguous bytes (coalesced), and the chunks
+//    of a row are XOR-swizzled (swz_slot) so that 8 or 16 consecutive rows at
+//    one chunk fall in distinct 16-byte slots;
+//  * packed (a block of a packed operand copied as is): the block order of
+//    common.hpp, where 16 consecutive rows at one chunk are 256 contiguous
+//    bytes.
+// Either way the 32x32x16 fragment reads are free of bank conflicts.
 __device__ __forceinline__ int swz_slot(int row, int c) { return c ^ (((row >> 1) ^ (row >> 3)) & 3); }
-__device__ __forceinline__ int swz(int row, int c) { return row * 64 + (swz_slot(row, c) << 4); }
+template <bool PACKED>
+__device__ __forceinline__ int lds_off(int row, int c) {
+    return PACKED ? (row >> 4) * 1024 + (c * 16 + (row & 15)) * 16 : row * 64 + (swz_slot(row, c) << 4);
+}
 
-// Wait until at most N direct-to-LDS loads of this wave are still in flight,
-// then barrier; the memory clobber pins every LDS access to its side.
+// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// address `dst` + 16*l (dst uniform).  Issued as inline asm so that the
+// compiler does not track it: its own wait insertion would otherwise drain
+// every outstanding slab load before each LDS fragment read it cannot prove
+// disjoint from the slab being filled.  The K loop orders these copies
+// itself (wait_vm_barrier); since loads retire in order for vmcnt, copies the
+// compiler does not know of only make its own vmcnt waits stricter.
+__device__ __forceinline__ void dma16(const void *g, __attribute__((address_space(3))) unsigned char *dst) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g) : "m0");
+}
+
 // Barrier for LDS data only: waits for this wave's LDS accesses, not for its
 // loads in flight.  (__syncthreads also waits for every outstanding global
 // load, and placed before the K loop it leads the compiler to drain all slab
@@ -154,42 +172,49 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     const int a_row = (p.lora && tid < BT) ? p.sorted_adapter[my_row] : -1;
 
     // ---- direct-to-LDS stage loads ----------------------------------------
-    // One wave instruction fills 16 rows x 64 bytes (1 KiB) of a stage; wave w
-    // owns instructions w, w+4, ...  Lane l writes row R0 + l/4, slot l&3,
-    // which holds logical chunk swz_slot(row, l&3).
+    // Wave w owns the stage's 16-row groups w, w+4, ...: instruction j fills
+    // group w + 4j.  Groups below BW/16 hold weight rows, the rest token rows.
+    // Row-major operands: lane l fetches row l/4 of the group at the chunk
+    // its slot l&3 holds (swizzled); packed h (down): lane l fetches bytes
+    // 16l .. 16l+15 of the block.
     constexpr int GROUPS = ROWS / 16;               // 16-row groups per stage
-    static_assert(GROUPS % 4 == 0, "row groups must split evenly over 4 waves");
+    static_assert(GROUPS % 4 == 0 && BW % 64 == 0, "row groups must split evenly over 4 waves");
     constexpr int LPW = GROUPS / 4;                 // load instructions per wave per stage
+    constexpr int LPW_A = BW / 64;                  // of which weight groups
+    constexpr bool B_PACKED = !GU;                  // h arrives packed
+    const int64_t nslab_in = (Kd + kSlabK - 1) / kSlabK;
     const uint16_t *src[LPW];
-    int chunk_of[LPW];
+    int chunk_of[LPW];  // chunk (0..3) this lane moves, row-major groups
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
         const int rr = (w + 4 * j) * 16 + (lane >> 2);
         const int c = swz_slot(rr, lane & 3);  // slot -> chunk (the XOR is its own inverse)
         chunk_of[j] = c;
-        const uint16_t *row;
-        if (rr < BW) {
+        if (j < LPW_A) {
             bool ok;
             const int grow = tile_weight_row<GU>(rr, i0, N, ok);
-            row = p.W + ((int64_t)e * rows_per_expert + (ok ? grow : 0)) * Kd;
-        } else {
+            src[j] = p.W + ((int64_t)e * rows_per_expert + (ok ? grow : 0)) * Kd + c * 8;
+        } else if (!B_PACKED) {
             const int j_tok = rr - BW;
             const int prow = row0 + min(j_tok, nrows - 1);
             const int f = p.sorted_ids[prow];
             int64_t xr = 0;
-            if (j_tok < nrows && f < p.P) xr = GU ? (f / p.Kp) : prow;
-            row = p.in + xr * Kd;
+            if (j_tok < nrows && f < p.P) xr = f / p.Kp;
+            src[j] = p.in + xr * Kd + c * 8;
+        } else {
+            // the tile's rows start on a group boundary and fill whole groups;
+            // groups past them repeat its last one (those columns are discarded)
+            const int grp = row0 / 16 + min((w + 4 * j) - BW / 16, nrows / 16 - 1);
+            src[j] = p.in + (int64_t)grp * nslab_in * kBlockElems + lane * 8;
         }
-        src[j] = row + c * 8;
     }
+    // per-slab advance of a source: 32 elements along a row, or one block
+    auto src_step = [&](int j) -> int64_t { return (j < LPW_A || !B_PACKED) ? (int64_t)kTileBK : (int64_t)kBlockElems; };
     const int nk = (int)((Kd + kTileBK - 1) / kTileBK);
     const int rs = (p.r + kTileBK - 1) / kTileBK;  // LoRA slabs per adapter
     typedef __attribute__((address_space(3))) unsigned char lds_t;
     lds_t *lds_base = (lds_t *)lds;
-    auto dma = [&](const void *g, lds_t *stage, int j) {
-        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(stage + (w + 4 * j) * 1024),
-                                         16, 0, 0);
-    };
+    auto dma = [&](const void *g, lds_t *stage, int j) { dma16(g, stage + (w + 4 * j) * 1024); };
     // Slab kt < nk: K columns [32 kt, 32 kt + 32) of the weights and tokens.
     // Slab nk + q (LoRA expand, aitrends.kr summary of the AWS multi-LoRA MoE
     // post, "section details": the LoRA sum folded into the expand step):
@@ -203,8 +228,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             const int64_t k0 = (int64_t)kt * kTileBK;
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
-                const bool kin = k0 + chunk_of[j] * 8 < Kd;
-                dma(kin ? (const void *)(src[j] + k0) : (const void *)g_zero_chunk, stage, j);
+                const bool kin = (j >= LPW_A && B_PACKED) || k0 + chunk_of[j] * 8 < Kd;
+                dma(kin ? (const void *)(src[j] + kt * src_step(j)) : (const void *)g_zero_chunk, stage, j);
             }
             return;
         }
@@ -216,10 +241,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         const uint16_t *s16 = reinterpret_cast<const uint16_t *>(p.s_part);
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int rr = (w + 4 * j) * 16 + (lane >> 2);
-            const int kk = kk0 + chunk_of[j] * 8;
+            // token groups of a packed-layout stage take lane l as (row l%16,
+            // chunk l/16), the block order the fragment reads expect
+            const bool pk = j >= LPW_A && B_PACKED;
+            const int rr = (w + 4 * j) * 16 + (pk ? (lane & 15) : (lane >> 2));
+            const int kk = kk0 + (pk ? (lane >> 4) : chunk_of[j]) * 8;
             const void *g = g_zero_chunk;
-            if (rr < BW) {
+            if (j < LPW_A) {
                 bool ok;
                 const int grow = tile_weight_row<GU>(rr, i0, N, ok);
                 if (ok && kk < p.r) g = Bae + (int64_t)grow * p.r + kk;
@@ -248,10 +276,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         const int c = ks * 2 + lh;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            af[mt] = *reinterpret_cast<const u32x4 *>(base + swz(a_row0 + mt * 32, c));
+            af[mt] = *reinterpret_cast<const u32x4 *>(base + lds_off<false>(a_row0 + mt * 32, c));
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt)
-            bfr[nt] = *reinterpret_cast<const u32x4 *>(base + swz(b_row0 + nt * 32, c));
+            bfr[nt] = *reinterpret_cast<const u32x4 *>(base + lds_off<B_PACKED>(b_row0 + nt * 32, c));
     };
     auto mm = [&](auto ntl, const u32x4 *af, const u32x4 *bfr) {
         constexpr int NTL = decltype(ntl)::value;
@@ -318,8 +346,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     auto issue_full = [&](int kt) {
         lds_t *stage = lds_base + (kt % kStages) * STAGE_BYTES;
         const int64_t k0 = (int64_t)kt * kTileBK;
+        (void)k0;
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) dma(src[j] + k0, stage, j);
+        for (int j = 0; j < LPW; ++j) dma(src[j] + kt * src_step(j), stage, j);
     };
     const int nk_full = (int)(Kd / kTileBK);
     auto mainloop = [&](auto ntl) {
@@ -331,9 +360,14 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         for (; kt + kStages - 1 < nk_full; ++kt) {
             rd(ntl, a1, b1, kt % kStages, 1);
             mm(ntl, a0, b0);
+            // keep each k-step's MFMAs on its side of the barrier, so the
+            // fragment reads issued after it overlap the second k-step
+            __builtin_amdgcn_sched_barrier(0);
             wait_vm_barrier<(kStages - 3) * LPW>();
-            rd(ntl, a0, b0, (kt + 1) % kStages, 0);
+            // refill first, so the slab loads leave as early as possible
             issue_full(kt + kStages - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            rd(ntl, a0, b0, (kt + 1) % kStages, 0);
             mm(ntl, a1, b1);
         }
         // the rest: LoRA slabs and the drain of the ring
@@ -358,6 +392,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     }
 
     // ---- epilogue --------------------------------------------------------
+    const int64_t nslab_out = (N + kSlabK - 1) / kSlabK;  // h is packed
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         if (nt >= nt_live) break;
@@ -372,14 +407,15 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
                 const int rr = wm * (BW / 2) + mt * 32 + g4 * 8 + lh * 4;  // first of 4 consecutive rows
                 if (GU) {
                     const int feat = i0 + 2 * (rr >> 2);
-                    if (feat >= N) continue;
-                    uint32_t v = 0u;
-                    if (valid) {
+                    if (feat >= nslab_out * kSlabK) continue;
+                    uint32_t v = 0u;  // padding rows and features past N stay zero
+                    if (valid && feat < N) {
                         const float g0 = acc[mt][nt][4 * g4 + 0], g1 = acc[mt][nt][4 * g4 + 1];
                         const float u0 = acc[mt][nt][4 * g4 + 2], u1 = acc[mt][nt][4 * g4 + 3];
                         v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
                     }
-                    *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(p.out) + (int64_t)prow * N + feat) = v;
+                    *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(p.out) +
+                                                  packed_off(prow, feat, nslab_out)) = v;
                 } else {
                     const int feat = i0 + rr;
                     if (feat >= N || !valid) continue;

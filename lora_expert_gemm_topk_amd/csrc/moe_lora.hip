@@ -174,7 +174,8 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     p.o_tiles = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_tiles, 1));
     p.o_s13 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
     p.o_s2 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
-    p.o_h = take(es * p.cap * d->I);
+    // room for h packed (the tiled GEMM's layout): whole 32-wide slabs
+    p.o_h = take(es * p.cap * (d->dtype == MOE_LORA_BF16 ? (d->I + 31) / 32 * 32 : d->I));
     p.o_y2 = take(sizeof(float) * p.P * d->H);
     p.total = o;
     p.align_total = round_up(sizeof(int32_t) * std::max<int64_t>(p.P, 1), A) + round_up(sizeof(int32_t) * 16, A);
@@ -538,6 +539,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         sp.P = (int)p.P;
         sp.cap = (int)p.cap;
         sp.out_bf16 = p.kind == 2 ? 1 : 0;
+        sp.in_packed = p.kind == 2 ? 1 : 0;  // the tiled GEMM keeps h packed
         mark(2 * MOE_LORA_STAGE_SHRINK13);
         if (p.lora) {
             sp.in = (const uint16_t *)a->hidden;

@@ -23,7 +23,7 @@
 namespace moelora {
 
 struct ShrinkParams {
-    const uint16_t *in;        // gate_up: x [T, H]; down: h [cap, I] (row = sorted position)
+    const uint16_t *in;        // gate_up: x [T, H]; down: h (row = sorted position), row-major or packed
     const int32_t *sorted_ids; // gate_up only: pair index per sorted position
     const uint16_t *A;         // [L, Ep, r, Kdim]
     const int32_t *items;      // [max_items][4]
@@ -31,6 +31,7 @@ struct ShrinkParams {
     float *s_part;             // [split][cap][r] fp32, or [cap][r] bf16 when out_bf16
     int Kdim, r, Ep, Kp, P, cap;
     int out_bf16;              // 1: split == 1, write the sum rounded once to bf16
+    int in_packed;             // down only: h in the packed layout of common.hpp
     int chunks_per_split;      // in units of 32 along Kdim
 };
 
@@ -47,20 +48,28 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
     const int g = lane >> 4, l16 = lane & 15;
     const int64_t Kd = p.Kdim;
 
-    // per-lane row pointers for the N side (tokens) and the M side (rank rows)
+    // Per-lane pointers for the N side (tokens) at this lane's k-group of
+    // chunk 0, advanced by xstep per 32-wide chunk: gathered x rows, rows of
+    // h, or rows of the packed h (one 1 KiB block per 16 rows x 32 k).
     const uint16_t *xrow[NT];
     bool xok[NT];
+    const int64_t nslab = (Kd + kSlabK - 1) / kSlabK;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int j = nt * 16 + l16;
         xok[nt] = j < len;
-        int64_t row = 0;
-        if (xok[nt]) {
-            if (GATHER) row = p.sorted_ids[p0 + j] / p.Kp;
-            else row = p0 + j;
+        if (GATHER) {
+            const int64_t row = xok[nt] ? p.sorted_ids[p0 + j] / p.Kp : 0;
+            xrow[nt] = p.in + row * Kd + g * 8;
+        } else if (p.in_packed) {
+            const int64_t row = p0 + (xok[nt] ? j : 0);
+            xrow[nt] = p.in + packed_off(row, (int64_t)g * 8, nslab);
+        } else {
+            const int64_t row = p0 + (xok[nt] ? j : 0);
+            xrow[nt] = p.in + row * Kd + g * 8;
         }
-        xrow[nt] = p.in + row * Kd;
     }
+    const int64_t xstep = (GATHER || !p.in_packed) ? kSlabK : kBlockElems;
     const uint16_t *arow[MT];
     bool aok[MT];
     const uint16_t *Abase = p.A + ((int64_t)a * p.Ep + e) * p.r * Kd;
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16(arow[mt] + k0, aok[mt] && kin);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) xv[u][nt] = ld16(xrow[nt] + k0, xok[nt] && kin);
+            for (int nt = 0; nt < NT; ++nt) xv[u][nt] = ld16(xrow[nt] + (int64_t)cc * xstep, xok[nt] && kin);
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
