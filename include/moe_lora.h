@@ -134,7 +134,9 @@ typedef struct moe_lora_plan {
  *     stage_events[2s] on `stream` right before stage s and
  *     stage_events[2s+1] right after it (both back to back for a stage that
  *     launches nothing), so the caller can time each kernel on the stream it
- *     runs on.  Stages: see MOE_LORA_STAGE_*. */
+ *     runs on.  Stages: see MOE_LORA_STAGE_*.
+ *   weights_packed: 0 = w13 and w2 as above; 1 = w13 and w2 are the packed
+ *     copies written by moe_lora_pack_weights (bf16 only). */
 typedef struct moe_lora_args {
     const void *hidden;
     const float *router_logits;
@@ -151,6 +153,7 @@ typedef struct moe_lora_args {
     int32_t *topk_ids_out;
     float *topk_weights_out;
     void **stage_events;
+    int32_t weights_packed;
 } moe_lora_args;
 
 /* Validate dims and describe the plan.  Pure host code: touches no device
@@ -198,6 +201,40 @@ int moe_lora_align(const moe_lora_dims *dims, const int32_t *topk_ids, const int
 
 /* The whole layer (steps 1-3), enqueued on `stream`. */
 int moe_lora_forward(const moe_lora_dims *dims, const moe_lora_args *args, void *stream);
+
+/* Packed expert weights (bf16 only).  An optional one-time re-layout of w13
+ * and w2 (for example at model load) into the order the GEMM kernels read:
+ * rows in groups of 16 and the reduction dimension in slabs of 32, one
+ * 1 KiB block per (group, slab), so each load instruction of a wavefront
+ * reads 1 KiB contiguously instead of 16 rows x 64 bytes.  The layer's
+ * arithmetic does not change: moe_lora_forward with weights_packed = 1 gives
+ * the same bits as with the row-major weights.
+ *
+ * Layout.  Inside a block, element (r, k), r in [0,16), k in [0,32), is at
+ * element index (k/8)*128 + r*8 + k%8.  Blocks are ordered
+ * [expert][group][slab]; elements past the matrix edge are zero.
+ *   w13 (G = 16*ceil(I/128) groups, ceil(H/32) slabs): row r of group q
+ *     holds feature f = 8q + 2*(r/4) + r%2 of the gate half (r%4 < 2, row f
+ *     of w13[e]) or of the up half (r%4 >= 2, row I+f), so each group
+ *     carries the gate and up rows of 8 features; K = H.
+ *   w2 (G = 16*ceil(H/256) groups, ceil(I/32) slabs): row r of group q is
+ *     row 16q + r of w2[e]; K = I.
+ *   (G rounds the group count up to whole 256-row GEMM tiles; groups past
+ *   the last feature or row are zero.)
+ * The interleave of gate and up rows is a property of the layout only: the
+ * packed w13 is read as w13, with the same meaning.
+ *
+ * moe_lora_packed_weight_bytes: size of the packed w13 (which = 0) or w2
+ * (which = 1); 0 for invalid dims or a dtype other than bf16.  Pure host
+ * code.
+ * moe_lora_pack_weights: writes w13_packed from w13 and w2_packed from w2
+ * (either pair may be NULL to skip it) on `stream`.  Buffers: device
+ * memory, 16-byte aligned, sizes as above; the source and the packed copy
+ * must not overlap.  Returns MOE_LORA_OK, MOE_LORA_EINVAL (bad pointers),
+ * MOE_LORA_EUNSUPPORTED (dims or dtype) or MOE_LORA_EHIP. */
+size_t moe_lora_packed_weight_bytes(const moe_lora_dims *dims, int which);
+int moe_lora_pack_weights(const moe_lora_dims *dims, const void *w13, const void *w2, void *w13_packed,
+                          void *w2_packed, void *stream);
 
 /* Text for a return code.  For MOE_LORA_EHIP it includes the HIP error of
  * the failing call on this thread.  Never NULL. */

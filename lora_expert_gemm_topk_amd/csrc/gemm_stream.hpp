@@ -25,6 +25,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "pack.hpp"
 
 namespace moelora {
 
@@ -74,7 +75,10 @@ __device__ __forceinline__ void lora_expand_add(const GemmParams &p, int e, int 
     }
 }
 
-template <int BW, int BT, bool GU>
+// WP: weights in the packed layout of moe_lora_pack_weights.  A weight
+// fragment is then one 16-row group (for gate_up the gate and up rows of 8
+// features, in quads gate f, gate f+1, up f, up f+1), read 1 KiB-contiguous.
+template <int BW, int BT, bool GU, bool WP>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
     constexpr int MS = BW / 16, NS = BT / 16;
     constexpr int LDW = BW + 4;
@@ -93,6 +97,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
 
     const uint16_t *wrow[MS];
     bool wok[MS];
+    const int64_t nslab_w = (Kd + kSlabK - 1) / kSlabK;
+    if constexpr (WP) {
+        // the packed group count covers every tile of the grid
+        const int64_t G = GU ? packed_w13_groups(N) : packed_w2_groups(N);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+            wok[ms] = true;
+            wrow[ms] = p.W + ((int64_t)e * G + (int64_t)blockIdx.x * MS + ms) * nslab_w * kBlockElems + l16 * 8;
+        }
+    } else {
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
         int col, grow;
@@ -106,6 +120,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
         }
         wok[ms] = col < N;
         wrow[ms] = p.W + ((int64_t)e * rows_per_expert + (wok[ms] ? grow : 0)) * Kd;
+    }
     }
     const uint16_t *xrow[NS];
     bool xok[NS];
@@ -132,8 +147,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
         const bool k_lo = k0 < Kd, k_hi = k0 + 8 < Kd;
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
-            wa[buf_i][ms][0] = ld16(wrow[ms] + k0, wok[ms] && k_lo);
-            wa[buf_i][ms][1] = ld16(wrow[ms] + k0 + 8, wok[ms] && k_hi);
+            if constexpr (WP) {
+                // k0 = 64c + 16g (+8) sits in slab 2c + g/2, chunk 2(g%2) (+1)
+                const int64_t slab = (int64_t)c * 2 + (g >> 1);
+                const uint16_t *blk = wrow[ms] + slab * kBlockElems + (g & 1) * 256;
+                wa[buf_i][ms][0] = ld16(blk, slab < nslab_w);
+                wa[buf_i][ms][1] = ld16(blk + 128, slab < nslab_w);
+            } else {
+                wa[buf_i][ms][0] = ld16(wrow[ms] + k0, wok[ms] && k_lo);
+                wa[buf_i][ms][1] = ld16(wrow[ms] + k0 + 8, wok[ms] && k_hi);
+            }
         }
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
@@ -191,7 +214,48 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
     __syncthreads();
 
     // Epilogue on the finished tile buf[1][token][feature].
-    if (GU) {
+    if (GU && WP) {
+        // tile rows 8qp .. 8qp+7 = gate f, gate f+1, up f, up f+1, gate f+2,
+        // gate f+3, up f+2, up f+3 with f = i0 + 4qp
+        constexpr int QP = BW / 8;
+        uint16_t *hout = reinterpret_cast<uint16_t *>(p.out);
+        for (int q = (int)threadIdx.x; q < BT * QP; q += 256) {
+            const int j = q / QP, qp = q % QP;
+            const int prow = b * BT + j;
+            const int col0 = i0 + 4 * qp;
+            if (col0 >= N) continue;
+            const int f = p.sorted_ids[prow];
+            uint2 packed = make_uint2(0u, 0u);
+            if (f < p.P) {
+                float v[8];  // gate col0..col0+3, up col0..col0+3
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    v[2 * h2 + 0] = buf[1][j][8 * qp + 4 * h2 + 0];
+                    v[2 * h2 + 1] = buf[1][j][8 * qp + 4 * h2 + 1];
+                    v[4 + 2 * h2 + 0] = buf[1][j][8 * qp + 4 * h2 + 2];
+                    v[4 + 2 * h2 + 1] = buf[1][j][8 * qp + 4 * h2 + 3];
+                }
+                if (p.lora) {
+                    const int a = p.adapter_ids[f / p.Kp];
+                    if (a >= 0 && a < p.L) {
+                        int rows[8];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            rows[i] = col0 + i;
+                            rows[4 + i] = N + col0 + i;
+                        }
+                        lora_expand_add<8>(p, e, a, prow, rows, rows_per_expert, v);
+                    }
+                }
+                float hv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hv[i] = silu(v[i]) * v[4 + i];
+                packed.x = pack_bf16x2(hv[0], hv[1]);
+                packed.y = pack_bf16x2(hv[2], hv[3]);
+            }
+            *reinterpret_cast<uint2 *>(hout + (int64_t)prow * N + col0) = packed;
+        }
+    } else if (GU) {
         constexpr int CG = BW / 8;  // 4-column groups in the gate half
         uint16_t *hout = reinterpret_cast<uint16_t *>(p.out);
         for (int q = (int)threadIdx.x; q < BT * CG; q += 256) {

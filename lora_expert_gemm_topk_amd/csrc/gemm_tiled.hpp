@@ -3,7 +3,9 @@
 //
 // Same contract as the streaming kernel (gemm_stream.hpp): weights are the
 // MFMA M side, the expert's tokens the N side, y13 -> SwiGLU -> h (bf16,
-// sorted row) for gate_up and y2 (fp32, pair row) for down.
+// sorted row) for gate_up and y2 (fp32, pair row) for down.  The token side
+// comes in the packed layout of common.hpp: x gathered and packed per sorted
+// row (pack.hpp) for gate_up, h as written by gate_up for down.
 //
 // Work unit: one (weight tile of BW rows, token tile) pair.  Token tiles come
 // from a list built by the alignment: up to BT consecutive sorted rows of ONE
@@ -22,8 +24,8 @@
 // (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16*l), so no
 // registers stage the data and kStages-1 slabs are in flight while the MFMAs
 // work on the oldest one.  One load instruction fills one 16-row group of a
-// stage: from a packed operand (h for down) it copies one 1 KiB block, from a
-// row-major one lane l fetches chunk l/16 of row l%16.  Each wave waits only for its own loads of the slab
+// stage: from a packed operand (the tokens) it copies one 1 KiB block, from a
+// row-major one (the weights) 16 rows x 64 bytes.  Each wave waits only for its own loads of the slab
 // it needs next (s_waitcnt vmcnt with the number of younger slabs still
 // allowed in flight) and then meets the others at one barrier per slab; the
 // wait and the barrier are one asm statement with a memory clobber, which
@@ -54,6 +56,7 @@
 
 #include "common.hpp"
 #include "gemm_stream.hpp"
+#include "pack.hpp"
 
 namespace moelora {
 
@@ -128,7 +131,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int BW, int BT, bool GU>
+// WP: weights in the packed layout of moe_lora_pack_weights (copied block by
+// block like the tokens) instead of row-major.
+template <int BW, int BT, bool GU, bool WP>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int32_t *__restrict__ tiles,
                                                          const int32_t *__restrict__ n_tiles, int n_wtiles) {
     constexpr int MT = BW / 64, NT = BT / 64;          // 32x32 tiles per wave
@@ -174,14 +179,14 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // ---- direct-to-LDS stage loads ----------------------------------------
     // Wave w owns the stage's 16-row groups w, w+4, ...: instruction j fills
     // group w + 4j.  Groups below BW/16 hold weight rows, the rest token rows.
-    // Row-major operands: lane l fetches row l/4 of the group at the chunk
-    // its slot l&3 holds (swizzled); packed h (down): lane l fetches bytes
-    // 16l .. 16l+15 of the block.
+    // Weights (row-major): lane l fetches row l/4 of the group at the chunk
+    // its slot l&3 holds (swizzled).  Tokens (packed x for gate_up, packed h
+    // for down): lane l fetches bytes 16l .. 16l+15 of the block.
     constexpr int GROUPS = ROWS / 16;               // 16-row groups per stage
     static_assert(GROUPS % 4 == 0 && BW % 64 == 0, "row groups must split evenly over 4 waves");
     constexpr int LPW = GROUPS / 4;                 // load instructions per wave per stage
     constexpr int LPW_A = BW / 64;                  // of which weight groups
-    constexpr bool B_PACKED = !GU;                  // h arrives packed
+    constexpr bool B_PACKED = true;                 // tokens arrive packed (x packed per sorted row, h)
     const int64_t nslab_in = (Kd + kSlabK - 1) / kSlabK;
     const uint16_t *src[LPW];
     int chunk_of[LPW];  // chunk (0..3) this lane moves, row-major groups
@@ -190,17 +195,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         const int rr = (w + 4 * j) * 16 + (lane >> 2);
         const int c = swz_slot(rr, lane & 3);  // slot -> chunk (the XOR is its own inverse)
         chunk_of[j] = c;
-        if (j < LPW_A) {
+        if (j < LPW_A && WP) {
+            // packed weights: group (w + 4j) of this tile; a tile spans BW/16
+            // whole groups (the packed group count is padded to full tiles)
+            const int64_t G = GU ? packed_w13_groups(N) : packed_w2_groups(N);
+            const int64_t gq = (int64_t)wt * (BW / 16) + (w + 4 * j);
+            src[j] = p.W + ((int64_t)e * G + gq) * nslab_in * kBlockElems + lane * 8;
+        } else if (j < LPW_A) {
             bool ok;
             const int grow = tile_weight_row<GU>(rr, i0, N, ok);
             src[j] = p.W + ((int64_t)e * rows_per_expert + (ok ? grow : 0)) * Kd + c * 8;
-        } else if (!B_PACKED) {
-            const int j_tok = rr - BW;
-            const int prow = row0 + min(j_tok, nrows - 1);
-            const int f = p.sorted_ids[prow];
-            int64_t xr = 0;
-            if (j_tok < nrows && f < p.P) xr = f / p.Kp;
-            src[j] = p.in + xr * Kd + c * 8;
         } else {
             // the tile's rows start on a group boundary and fill whole groups;
             // groups past them repeat its last one (those columns are discarded)
@@ -209,7 +213,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         }
     }
     // per-slab advance of a source: 32 elements along a row, or one block
-    auto src_step = [&](int j) -> int64_t { return (j < LPW_A || !B_PACKED) ? (int64_t)kTileBK : (int64_t)kBlockElems; };
+    auto src_step = [&](int j) -> int64_t {
+        return (j < LPW_A ? WP : B_PACKED) ? (int64_t)kBlockElems : (int64_t)kTileBK;
+    };
     const int nk = (int)((Kd + kTileBK - 1) / kTileBK);
     const int rs = (p.r + kTileBK - 1) / kTileBK;  // LoRA slabs per adapter
     typedef __attribute__((address_space(3))) unsigned char lds_t;
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             const int64_t k0 = (int64_t)kt * kTileBK;
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
-                const bool kin = (j >= LPW_A && B_PACKED) || k0 + chunk_of[j] * 8 < Kd;
+                const bool kin = (j < LPW_A ? WP : B_PACKED) || k0 + chunk_of[j] * 8 < Kd;
                 dma(kin ? (const void *)(src[j] + kt * src_step(j)) : (const void *)g_zero_chunk, stage, j);
             }
             return;
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         for (int j = 0; j < LPW; ++j) {
             // token groups of a packed-layout stage take lane l as (row l%16,
             // chunk l/16), the block order the fragment reads expect
-            const bool pk = j >= LPW_A && B_PACKED;
+            const bool pk = j < LPW_A ? WP : B_PACKED;
             const int rr = (w + 4 * j) * 16 + (pk ? (lane & 15) : (lane >> 2));
             const int kk = kk0 + (pk ? (lane >> 4) : chunk_of[j]) * 8;
             const void *g = g_zero_chunk;
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         const int c = ks * 2 + lh;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            af[mt] = *reinterpret_cast<const u32x4 *>(base + lds_off<false>(a_row0 + mt * 32, c));
+            af[mt] = *reinterpret_cast<const u32x4 *>(base + lds_off<WP>(a_row0 + mt * 32, c));
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt)
             bfr[nt] = *reinterpret_cast<const u32x4 *>(base + lds_off<B_PACKED>(b_row0 + nt * 32, c));

@@ -26,6 +26,7 @@
 #include "fp32_path.hpp"
 #include "gemm_stream.hpp"
 #include "gemm_tiled.hpp"
+#include "pack.hpp"
 #include "route.hpp"
 #include "shrink.hpp"
 
@@ -52,7 +53,7 @@ struct Plan {
     bool lora = false;
     // workspace offsets (bytes)
     size_t o_ids = 0, o_w = 0, o_sorted = 0, o_sadp = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0, o_tiles = 0;
-    size_t o_s13 = 0, o_s2 = 0, o_h = 0, o_y2 = 0, total = 0;
+    size_t o_s13 = 0, o_s2 = 0, o_h = 0, o_y2 = 0, o_xp = 0, total = 0;
     size_t align_total = 0;  // tmp + nothing else, for moe_lora_align
 };
 
@@ -177,6 +178,8 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     // room for h packed (the tiled GEMM's layout): whole 32-wide slabs
     p.o_h = take(es * p.cap * (d->dtype == MOE_LORA_BF16 ? (d->I + 31) / 32 * 32 : d->I));
     p.o_y2 = take(sizeof(float) * p.P * d->H);
+    // tiled GEMM: x gathered and packed per sorted row
+    p.o_xp = take(p.kind == 2 ? es * p.cap * ((d->H + 31) / 32 * 32) : 0);
     p.total = o;
     p.align_total = round_up(sizeof(int32_t) * std::max<int64_t>(p.P, 1), A) + round_up(sizeof(int32_t) * 16, A);
     *pl = p;
@@ -310,45 +313,46 @@ void launch_shrink(const Plan &pl, ShrinkParams sp, bool gather, int r, hipStrea
 // Weight rows per tile of the LDS-tiled kernel.  256 (16 MFMAs per 8
 // fragment reads per wave) measured fastest for both projections of the
 // GPT-OSS-20B prefill layer even where N is not a multiple of the tile; 128
-// only when N is too small to fill wider tiles.
+// only when N is too small to fill wider tiles.  (Both are whole multiples of
+// the 128-row half tiles the packed weight layout is padded to.)
 int tiled_bw(int N, bool gu) {
-#ifdef MOELORA_TILED_BW
-    (void)N;
-    (void)gu;
-    return MOELORA_TILED_BW;
-#endif
     const int feats = gu ? N * 2 : N;
     return feats <= 128 ? 128 : 256;
 }
 
-template <int BW, int BT, bool GU>
+template <int BW, int BT, bool GU, bool WP>
 void launch_tiled(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
                   hipStream_t st) {
     const int n_wt = (gp.Nout + (GU ? BW / 2 : BW) - 1) / (GU ? BW / 2 : BW);
     const unsigned total = (unsigned)(n_wt * pl.max_tiles);
-    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU>), dim3(total), dim3(256), 0, st, gp, tiles, ntiles, n_wt);
+    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU, WP>), dim3(total), dim3(256), 0, st, gp, tiles, ntiles, n_wt);
 }
 
-template <bool GU>
-void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
-                 hipStream_t st) {
+template <bool GU, bool WP>
+void launch_gemm_wp(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
+                    hipStream_t st) {
     if (pl.kind == 1) {
         const int tile = GU ? kStreamBW / 2 : kStreamBW;
         const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
-        if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU>), grid, block, 0, st, gp);
-        else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU>), grid, block, 0, st, gp);
+        if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, WP>), grid, block, 0, st, gp);
+        else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, WP>), grid, block, 0, st, gp);
         return;
     }
     const int bw = tiled_bw(gp.Nout, GU);
     if (pl.tile == 128) {
-        if (bw == 256) launch_tiled<256, 128, GU>(pl, gp, tiles, ntiles, st);
-        else if (bw == 192) launch_tiled<192, 128, GU>(pl, gp, tiles, ntiles, st);
-        else launch_tiled<128, 128, GU>(pl, gp, tiles, ntiles, st);
+        if (bw == 256) launch_tiled<256, 128, GU, WP>(pl, gp, tiles, ntiles, st);
+        else launch_tiled<128, 128, GU, WP>(pl, gp, tiles, ntiles, st);
     } else {
-        if (bw == 256) launch_tiled<256, 256, GU>(pl, gp, tiles, ntiles, st);
-        else if (bw == 192) launch_tiled<192, 256, GU>(pl, gp, tiles, ntiles, st);
-        else launch_tiled<128, 256, GU>(pl, gp, tiles, ntiles, st);
+        if (bw == 256) launch_tiled<256, 256, GU, WP>(pl, gp, tiles, ntiles, st);
+        else launch_tiled<128, 256, GU, WP>(pl, gp, tiles, ntiles, st);
     }
+}
+
+template <bool GU>
+void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles, bool wp,
+                 hipStream_t st) {
+    if (wp) launch_gemm_wp<GU, true>(pl, gp, tiles, ntiles, st);
+    else launch_gemm_wp<GU, false>(pl, gp, tiles, ntiles, st);
 }
 
 }  // namespace
@@ -396,7 +400,58 @@ int moe_lora_check_args(const moe_lora_dims *d, const moe_lora_args *a) {
     }
     if (!aligned(a->workspace, 256)) return MOE_LORA_EINVAL;
     if (a->workspace_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    if (a->weights_packed != 0 && a->weights_packed != 1) return MOE_LORA_EINVAL;
+    if (a->weights_packed && d->dtype != MOE_LORA_BF16) return MOE_LORA_EUNSUPPORTED;
     return MOE_LORA_OK;
+}
+
+size_t moe_lora_packed_weight_bytes(const moe_lora_dims *d, int which) {
+    Plan p;
+    if (make_plan(d, &p) != MOE_LORA_OK || d->dtype != MOE_LORA_BF16) return 0;
+    if (which == 0) return (size_t)p.Ep * packed_w13_groups(d->I) * ((d->H + 31) / 32) * 1024;
+    if (which == 1) return (size_t)p.Ep * packed_w2_groups(d->H) * ((d->I + 31) / 32) * 1024;
+    return 0;
+}
+
+int moe_lora_pack_weights(const moe_lora_dims *d, const void *w13, const void *w2, void *w13_packed,
+                          void *w2_packed, void *stream) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc != MOE_LORA_OK) return rc;
+    if (d->dtype != MOE_LORA_BF16) return MOE_LORA_EUNSUPPORTED;
+    if ((w13 == nullptr) != (w13_packed == nullptr) || (w2 == nullptr) != (w2_packed == nullptr))
+        return MOE_LORA_EINVAL;
+    const void *ptrs[] = {w13, w2, w13_packed, w2_packed};
+    for (const void *ptr : ptrs)
+        if (ptr && !aligned(ptr, 16)) return MOE_LORA_EINVAL;
+    if (!w13 && !w2) return MOE_LORA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (w13) {
+        PackWParams pw;
+        pw.src = (const uint16_t *)w13;
+        pw.dst = (uint16_t *)w13_packed;
+        pw.rows_src = 2 * d->I;
+        pw.K = (int)d->H;
+        pw.nslab = (int)((d->H + 31) / 32);
+        pw.G = (int)packed_w13_groups(d->I);
+        pw.N = (int)d->I;
+        pw.gate_up = 1;
+        hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)pw.G, (unsigned)p.Ep), dim3(256), 0, st, pw);
+    }
+    if (w2) {
+        PackWParams pw;
+        pw.src = (const uint16_t *)w2;
+        pw.dst = (uint16_t *)w2_packed;
+        pw.rows_src = d->H;
+        pw.K = (int)d->I;
+        pw.nslab = (int)((d->I + 31) / 32);
+        pw.G = (int)packed_w2_groups(d->H);
+        pw.N = (int)d->H;
+        pw.gate_up = 0;
+        hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)pw.G, (unsigned)p.Ep), dim3(256), 0, st, pw);
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "pack launch");
 }
 
 int moe_lora_route(const moe_lora_dims *d, const float *logits, int32_t *topk_ids, float *topk_weights,
@@ -565,13 +620,25 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.lora = p.lora ? 1 : 0;
         gp.in = (const uint16_t *)a->hidden;
         gp.W = (const uint16_t *)a->w13;
+        mark(2 * MOE_LORA_STAGE_GATE_UP);
+        if (p.kind == 2) {
+            PackXParams xp;
+            xp.x = (const uint16_t *)a->hidden;
+            xp.sorted_ids = sorted;
+            xp.counters = cnt;
+            xp.xp = (uint16_t *)(ws + p.o_xp);
+            xp.H = H;
+            xp.P = (int)p.P;
+            xp.Kp = (int)p.Kp;
+            hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)(p.cap / 16)), dim3(256), 0, st, xp);
+            gp.in = xp.xp;
+        }
         gp.B = (const uint16_t *)a->b13;
         gp.s_part = s13;
         gp.out = h;
         gp.Kdim = H;
         gp.Nout = I;
-        mark(2 * MOE_LORA_STAGE_GATE_UP);
-        launch_gemm<true>(p, gp, tiles, cnt + 2, st);
+        launch_gemm<true>(p, gp, tiles, cnt + 2, a->weights_packed != 0, st);
         mark(2 * MOE_LORA_STAGE_GATE_UP + 1);
         mark(2 * MOE_LORA_STAGE_SHRINK2);
         if (p.lora) {
@@ -590,7 +657,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.Kdim = I;
         gp.Nout = H;
         mark(2 * MOE_LORA_STAGE_DOWN);
-        launch_gemm<false>(p, gp, tiles, cnt + 2, st);
+        launch_gemm<false>(p, gp, tiles, cnt + 2, a->weights_packed != 0, st);
         mark(2 * MOE_LORA_STAGE_DOWN + 1);
         mark(2 * MOE_LORA_STAGE_COMBINE);
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)d->T), dim3(256),

@@ -26,7 +26,8 @@ MOE_LORA_BF16 = 1
 STAGES = ("route", "align", "shrink13", "gate_up", "shrink2", "down", "combine")
 
 EXPORTED = ("moe_lora_plan_query", "moe_lora_workspace_bytes", "moe_lora_check_args", "moe_lora_route",
-            "moe_lora_align", "moe_lora_forward", "moe_lora_strerror")
+            "moe_lora_align", "moe_lora_forward", "moe_lora_packed_weight_bytes", "moe_lora_pack_weights",
+            "moe_lora_strerror")
 
 
 class MoeLoraDims(ctypes.Structure):
@@ -50,7 +51,8 @@ class MoeLoraArgs(ctypes.Structure):
                 ("a13", ctypes.c_void_p), ("b13", ctypes.c_void_p), ("a2", ctypes.c_void_p),
                 ("b2", ctypes.c_void_p), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("topk_ids_out", ctypes.c_void_p),
-                ("topk_weights_out", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+                ("topk_weights_out", ctypes.c_void_p), ("stage_events", ctypes.c_void_p),
+                ("weights_packed", ctypes.c_int32)]
 
 
 class MoeLoraError(RuntimeError):
@@ -86,6 +88,10 @@ def lib():
     L.moe_lora_align.restype = ctypes.c_int
     L.moe_lora_forward.argtypes = [P(MoeLoraDims), P(MoeLoraArgs), vp]
     L.moe_lora_forward.restype = ctypes.c_int
+    L.moe_lora_packed_weight_bytes.argtypes = [P(MoeLoraDims), ctypes.c_int]
+    L.moe_lora_packed_weight_bytes.restype = ctypes.c_size_t
+    L.moe_lora_pack_weights.argtypes = [P(MoeLoraDims), vp, vp, vp, vp, vp]
+    L.moe_lora_pack_weights.restype = ctypes.c_int
     L.moe_lora_strerror.argtypes = [ctypes.c_int]
     L.moe_lora_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -177,6 +183,41 @@ def moe_lora_align(topk_ids: torch.Tensor, adapter_ids: Optional[torch.Tensor], 
                 lora_items=items[:plan["max_items"]], num_items=nitems, plan=plan)
 
 
+def moe_lora_packed_weight_bytes(dims: MoeLoraDims, which: int) -> int:
+    """Bytes of the packed w13 (which=0) or w2 (which=1); 0 if unsupported."""
+    return int(lib().moe_lora_packed_weight_bytes(ctypes.byref(dims), int(which)))
+
+
+class PackedWeights:
+    """w13 and w2 re-laid out once by moe_lora_pack_weights (bf16 only).
+
+    Pass an instance as `w13` (with `w2=None`) to moe_lora_forward; the layer
+    then reads the packed copies and gives the same bits as with the
+    row-major weights.  Holds the shapes the layout was made for."""
+
+    def __init__(self, w13: torch.Tensor, w2: torch.Tensor):
+        _dev_tensor(w13, "w13", torch.bfloat16)
+        _dev_tensor(w2, "w2", torch.bfloat16)
+        self.Ep, twoI, self.H = (int(v) for v in w13.shape)
+        self.I = twoI // 2
+        if tuple(w2.shape) != (self.Ep, self.H, self.I):
+            raise ValueError(f"w2 shape {tuple(w2.shape)} does not match w13 {tuple(w13.shape)}")
+        # routing fields do not affect the layout: one routed expert, K = 1
+        self.dims = make_dims(1, self.H, self.I, self.Ep, 1, 0, 0, 0, 1.0, 1, "bf16")
+        n13 = moe_lora_packed_weight_bytes(self.dims, 0)
+        n2 = moe_lora_packed_weight_bytes(self.dims, 1)
+        if n13 == 0 or n2 == 0:
+            raise ValueError("weights cannot be packed for these shapes")
+        self.w13 = torch.empty(n13, dtype=torch.uint8, device=w13.device)
+        self.w2 = torch.empty(n2, dtype=torch.uint8, device=w13.device)
+        self.device = w13.device
+        with torch.cuda.device(w13.device):
+            rc = lib().moe_lora_pack_weights(ctypes.byref(self.dims), w13.data_ptr(), w2.data_ptr(),
+                                             self.w13.data_ptr(), self.w2.data_ptr(), _stream(w13.device))
+        if rc != MOE_LORA_OK:
+            raise MoeLoraError(rc, "moe_lora_pack_weights")
+
+
 class Workspace:
     """A reusable device workspace: grows on demand, never shrinks."""
 
@@ -199,20 +240,32 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     """The fused MoE-LoRA layer on the GPU (enqueued on the current stream).
 
     Shapes: x [T,H], logits [T,E] f32, adapter_ids [T] i32 (-1 = none),
-    w13 [E+S,2I,H], w2 [E+S,H,I], a13 [L,E+S,r,H], b13 [L,E+S,2I,r],
+    w13 [E+S,2I,H], w2 [E+S,H,I] (or w13 = PackedWeights of both, w2 = None),
+    a13 [L,E+S,r,H], b13 [L,E+S,2I,r],
     a2 [L,E+S,r,I], b2 [L,E+S,H,r]; x, weights and out share one dtype
     (bf16 or f32).  routing_out = (ids [T,K+S] i32, weights [T,K+S] f32)
     receives the routing decisions when given.  stage_events: optional
     ctypes array of 2*len(STAGES) hipEvent_t handles recorded around each
     stage on the launch stream."""
     dt = x.dtype
-    for name, t in (("x", x), ("w13", w13), ("w2", w2), ("a13", a13), ("b13", b13), ("a2", a2), ("b2", b2)):
+    packed = isinstance(w13, PackedWeights)
+    if packed:
+        if w2 is not None:
+            raise ValueError("with PackedWeights as w13, pass w2=None")
+        if w13.device != x.device:
+            raise ValueError("packed weights live on another device")
+        Ep, I = w13.Ep, w13.I
+    for name, t in (("x", x), ("a13", a13), ("b13", b13), ("a2", a2), ("b2", b2)) + \
+            (() if packed else (("w13", w13), ("w2", w2))):
         _dev_tensor(t, name, dt)
     _dev_tensor(logits, "logits", torch.float32)
     _dev_tensor(adapter_ids, "adapter_ids", torch.int32)
     T, H = x.shape
-    Ep, twoI, _ = w13.shape
-    I = twoI // 2
+    if packed and w13.H != H:
+        raise ValueError(f"packed weights are for H={w13.H}, x has H={H}")
+    if not packed:
+        Ep, twoI, _ = w13.shape
+        I = twoI // 2
     E = logits.shape[1]
     L, r = (a13.shape[0], a13.shape[2]) if a13 is not None else (0, 0)
     dims = make_dims(T, H, I, E, K, S, L, r, rsf, renormalize, dt, block_m, lora_block_m, split_k)
@@ -222,13 +275,15 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     nbytes = moe_lora_workspace_bytes(dims)
     ws = (workspace or Workspace()).get(nbytes, x.device)
     ids_out, w_out = routing_out if routing_out is not None else (None, None)
+    w13_ptr, w2_ptr = (w13.w13.data_ptr(), w13.w2.data_ptr()) if packed else (w13.data_ptr(), w2.data_ptr())
     args = MoeLoraArgs(x.data_ptr(), logits.data_ptr(), adapter_ids.data_ptr() if adapter_ids is not None else None,
-                       w13.data_ptr(), w2.data_ptr(),
+                       w13_ptr, w2_ptr,
                        *(t.data_ptr() if t is not None else None for t in (a13, b13, a2, b2)),
                        out.data_ptr(), ws.data_ptr(), ws.numel(),
                        ids_out.data_ptr() if ids_out is not None else None,
                        w_out.data_ptr() if w_out is not None else None,
-                       ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None)
+                       ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None,
+                       1 if packed else 0)
     with torch.cuda.device(x.device):
         rc = lib().moe_lora_forward(ctypes.byref(dims), ctypes.byref(args), _stream(x.device))
     if rc != MOE_LORA_OK:
@@ -236,11 +291,13 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     return out
 
 
-def forward_inputs(inp, *, lora: bool = True, **kw) -> torch.Tensor:
-    """moe_lora_forward over a synth.LayerInputs bundle already on the GPU."""
+def forward_inputs(inp, *, lora: bool = True, packed: Optional[PackedWeights] = None, **kw) -> torch.Tensor:
+    """moe_lora_forward over a synth.LayerInputs bundle already on the GPU
+    (with `packed`, the packed copies of its w13 and w2 are read instead)."""
     s = inp.shape
     use = lora and s.lora
-    return moe_lora_forward(inp.x, inp.logits, inp.adapter_ids if use else None, inp.w13, inp.w2,
+    w13, w2 = (packed, None) if packed is not None else (inp.w13, inp.w2)
+    return moe_lora_forward(inp.x, inp.logits, inp.adapter_ids if use else None, w13, w2,
                             inp.a13 if use else None, inp.b13 if use else None,
                             inp.a2 if use else None, inp.b2 if use else None,
                             K=s.K, S=s.S, rsf=s.rsf, renormalize=s.renormalize, **kw)

@@ -104,3 +104,37 @@ def test_check_args_codes_without_device():
     assert ml.moe_lora_check_args(d0, _args(adapter_ids=None, a13=None, b13=None, a2=None, b2=None)) == 0
     # T = 0 is a no-op and needs no buffers
     assert ml.moe_lora_check_args(_dims(T=0), _args(hidden=None, out=None, workspace=None)) == 0
+
+
+def test_check_args_weights_packed_flag():
+    d = _dims()
+    assert ml.moe_lora_check_args(d, _args(weights_packed=1)) == ml.MOE_LORA_OK
+    assert ml.moe_lora_check_args(d, _args(weights_packed=2)) == ml.MOE_LORA_EINVAL
+    assert ml.moe_lora_check_args(_dims(dtype="f32"), _args(weights_packed=1)) == ml.MOE_LORA_EUNSUPPORTED
+
+
+def test_packed_weight_bytes_formula():
+    # w13: E+S experts x 16*ceil(I/128) groups x ceil(H/32) slabs x 1 KiB;
+    # w2: E+S experts x 16*ceil(H/256) groups x ceil(I/32) slabs x 1 KiB
+    for (H, I, E, S) in ((2880, 2880, 32, 0), (136, 200, 5, 1), (64, 8, 4, 0), (4096, 1536, 64, 1)):
+        d = _dims(H=H, I=I, E=E, S=S)
+        Ep = E + S
+        assert mm.moe_lora_packed_weight_bytes(d, 0) == Ep * 16 * -(-I // 128) * -(-H // 32) * 1024
+        assert mm.moe_lora_packed_weight_bytes(d, 1) == Ep * 16 * -(-H // 256) * -(-I // 32) * 1024
+        assert mm.moe_lora_packed_weight_bytes(d, 2) == 0
+    assert mm.moe_lora_packed_weight_bytes(_dims(dtype="f32"), 0) == 0
+    assert mm.moe_lora_packed_weight_bytes(_dims(H=100), 0) == 0   # H not a multiple of 8
+
+
+def test_pack_weights_rejects_without_device():
+    L = mm.lib()
+    d = _dims()
+    vp = ctypes.c_void_p
+    # a source without a destination (or the reverse), misaligned pointers, f32
+    assert L.moe_lora_pack_weights(ctypes.byref(d), vp(0x1000), None, None, None, None) == ml.MOE_LORA_EINVAL
+    assert L.moe_lora_pack_weights(ctypes.byref(d), None, None, None, vp(0x1000), None) == ml.MOE_LORA_EINVAL
+    assert L.moe_lora_pack_weights(ctypes.byref(d), vp(0x1008), None, vp(0x2000), None, None) == ml.MOE_LORA_EINVAL
+    assert L.moe_lora_pack_weights(ctypes.byref(_dims(dtype="f32")), vp(0x1000), None, vp(0x2000), None,
+                                   None) == ml.MOE_LORA_EUNSUPPORTED
+    # nothing to do is fine (no launch)
+    assert L.moe_lora_pack_weights(ctypes.byref(d), None, None, None, None, None) == ml.MOE_LORA_OK
