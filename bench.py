@@ -6,9 +6,11 @@ one batch of seeded synthetic inputs already resident in HBM.  Prints ONE JSON
 line.  The default workload is the GPT-OSS-20B-shaped decode layer
 (T=64, H=I=2880, 32 experts top-4, 8 LoRA adapters of rank 16, 25% tokens
 without LoRA); the prefill layer (T=4096, 32 adapters of rank 32) is measured
-beside it and reported under "prefill".
+beside it and reported under "prefill".  Expert weights are packed once with
+moe_lora_pack_weights before timing (as a model would at load time);
+--row-major times the row-major weights instead.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--row-major]
 """
 from __future__ import annotations
 
@@ -37,7 +39,7 @@ ROOT = Path(__file__).resolve().parent
 CSRC = ROOT / "lora_expert_gemm_topk_amd" / "csrc"
 # the dominant kernels' sources and their launch code: a recorded counter
 # reading stays valid only while these are unchanged
-KERNEL_SOURCES = ("common.hpp", "gemm_stream.hpp", "gemm_tiled.hpp", "moe_lora.hip")
+KERNEL_SOURCES = ("common.hpp", "gemm_stream.hpp", "gemm_tiled.hpp", "pack.hpp", "moe_lora.hip")
 
 
 def kernel_sources_sha256() -> str:
@@ -132,7 +134,10 @@ class StageEvents:
 
 # ------------------------------------------------------------ measurement
 
-def measure(name: str, steps: int, warmup: int, seed: int = 0) -> dict:
+def measure(name: str, steps: int, warmup: int, seed: int = 0, packed: bool = True) -> dict:
+    """Time `steps` layer calls.  With `packed`, w13/w2 are re-laid out once by
+    moe_lora_pack_weights before any timing (a model-load step, like loading
+    the weights themselves) and every call reads the packed copies."""
     shape, recipe = synth.workload(name)
     inp = synth.make_inputs(shape, recipe, seed=seed, device="cuda")
     dev = inp.x.device
@@ -140,9 +145,10 @@ def measure(name: str, steps: int, warmup: int, seed: int = 0) -> dict:
     ws = ml.Workspace()
     ids = torch.empty((shape.T, shape.Kp), dtype=torch.int32, device=dev)
     wts = torch.empty((shape.T, shape.Kp), dtype=torch.float32, device=dev)
+    pw = ml.PackedWeights(inp.w13, inp.w2) if packed and shape.dtype == synth.BF16 else None
 
     def step(ev=None):
-        ml.forward_inputs(inp, out=out, workspace=ws, routing_out=(ids, wts), stage_events=ev)
+        ml.forward_inputs(inp, out=out, workspace=ws, routing_out=(ids, wts), stage_events=ev, packed=pw)
 
     for _ in range(warmup):
         step()
@@ -168,12 +174,12 @@ def measure(name: str, steps: int, warmup: int, seed: int = 0) -> dict:
     wk = work(shape, ids.cpu().numpy(), inp.adapter_ids.cpu().numpy())
     plan = ml.moe_lora_plan_query(ml.make_dims(shape.T, shape.H, shape.I, shape.E, shape.K, shape.S, shape.L,
                                                shape.r, shape.rsf, shape.renormalize, shape.dtype))
-    return dict(name=name, shape=shape, inp=inp, ms=ms, stage=stage, work=wk, plan=plan)
+    return dict(name=name, shape=shape, inp=inp, ms=ms, stage=stage, work=wk, plan=plan, packed=pw is not None)
 
 
 def roofline_obj(m: dict, bound: str) -> dict:
     st = m["stage"]["gate_up"] * 1e-3
-    kern = ("gemm_stream" if m["plan"]["block_m"] <= 32 else "gemm_tiled") + \
+    kern = ("gemm_tiled" if m["plan"]["gemm_kind"] == 2 else "gemm_stream") + \
         " gate_up (+LoRA expand13, SwiGLU)"
     traffic = recorded_traffic(m["name"], "gate_up")
     if bound == "hbm":
@@ -240,6 +246,8 @@ def main() -> int:
     ap.add_argument("--prefill", default="gptoss_prefill_T4096", help="secondary workload ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--row-major", action="store_true",
+                    help="read w13/w2 row-major instead of packing them once before timing")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -256,7 +264,7 @@ def main() -> int:
         copy_calibration(args.copy_calib_mib, args.steps)
         return 0
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
-    m = measure(args.workload, args.steps, args.warmup)
+    m = measure(args.workload, args.steps, args.warmup, packed=not args.row_major)
     s = m["shape"]
     result = {
         "metric": METRIC,
@@ -272,7 +280,8 @@ def main() -> int:
         "dtype": s.dtype,
         "data": "synthetic (seeded)",
         "config": {"workload": args.workload, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "K": s.K, "S": s.S,
-                   "L": s.L, "r": s.r, "block_m": m["plan"]["block_m"], "split_k": m["plan"]["split_k"]},
+                   "L": s.L, "r": s.r, "block_m": m["plan"]["block_m"], "split_k": m["plan"]["split_k"],
+                   "weights": "packed once before timing" if m["packed"] else "row-major"},
         "roofline": roofline_obj(m, "hbm"),
         "layer": layer_roofline(m),
         "stage_us": {k: v * 1e3 for k, v in m["stage"].items()},
@@ -287,7 +296,7 @@ def main() -> int:
     torch.cuda.empty_cache()
     if args.prefill:
         print(f"bench: {args.prefill}", file=sys.stderr, flush=True)
-        p = measure(args.prefill, max(5, args.steps // 5), max(2, args.warmup // 5))
+        p = measure(args.prefill, max(5, args.steps // 5), max(2, args.warmup // 5), packed=not args.row_major)
         ps = p["shape"]
         result["prefill"] = {"workload": args.prefill, "tokens_per_s": ps.T / (p["ms"] * 1e-3),
                              "ms_per_step": p["ms"], "roofline": roofline_obj(p, "mfma"),

@@ -58,7 +58,9 @@ extern "C" {
 #define MOE_LORA_F32 0
 #define MOE_LORA_BF16 1
 
-/* Stages of moe_lora_forward, in launch order (for moe_lora_args.stage_events). */
+/* Stages of moe_lora_forward, in launch order (for moe_lora_args.stage_events).
+ * ALIGN includes, with the LDS-tiled GEMM (gemm_kind 2), the gather-and-pack
+ * of x into sorted-row order; each other stage is one kernel. */
 #define MOE_LORA_STAGE_ROUTE 0
 #define MOE_LORA_STAGE_ALIGN 1
 #define MOE_LORA_STAGE_SHRINK13 2

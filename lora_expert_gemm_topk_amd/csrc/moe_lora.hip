@@ -528,6 +528,18 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
                           cnt + 1, tmp,
                           p.kind == 2 ? tiles : nullptr, cnt + 2, p.fuse_route ? &rp : nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;
+    if (p.kind == 2) {
+        // the tiled GEMM reads x gathered and packed per sorted row
+        PackXParams xp;
+        xp.x = (const uint16_t *)a->hidden;
+        xp.sorted_ids = sorted;
+        xp.counters = cnt;
+        xp.xp = (uint16_t *)(ws + p.o_xp);
+        xp.H = H;
+        xp.P = (int)p.P;
+        xp.Kp = (int)p.Kp;
+        hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)(p.cap / 16)), dim3(256), 0, st, xp);
+    }
     mark(2 * MOE_LORA_STAGE_ALIGN + 1);
 
     if (p.kind == 0) {
@@ -618,21 +630,9 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.L = (int)p.La;
         gp.split = p.split;
         gp.lora = p.lora ? 1 : 0;
-        gp.in = (const uint16_t *)a->hidden;
+        gp.in = (p.kind == 2) ? (const uint16_t *)(ws + p.o_xp) : (const uint16_t *)a->hidden;
         gp.W = (const uint16_t *)a->w13;
         mark(2 * MOE_LORA_STAGE_GATE_UP);
-        if (p.kind == 2) {
-            PackXParams xp;
-            xp.x = (const uint16_t *)a->hidden;
-            xp.sorted_ids = sorted;
-            xp.counters = cnt;
-            xp.xp = (uint16_t *)(ws + p.o_xp);
-            xp.H = H;
-            xp.P = (int)p.P;
-            xp.Kp = (int)p.Kp;
-            hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)(p.cap / 16)), dim3(256), 0, st, xp);
-            gp.in = xp.xp;
-        }
         gp.B = (const uint16_t *)a->b13;
         gp.s_part = s13;
         gp.out = h;
