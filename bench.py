@@ -171,10 +171,97 @@ def measure(name: str, steps: int, warmup: int, seed: int = 0, packed: bool = Tr
     stage = se.stage_ms()
     se.close()
 
+    # third pass: each step between its own events, for median / p10 / p90
+    dist = per_iteration(step, steps, 0)
+
     wk = work(shape, ids.cpu().numpy(), inp.adapter_ids.cpu().numpy())
     plan = ml.moe_lora_plan_query(ml.make_dims(shape.T, shape.H, shape.I, shape.E, shape.K, shape.S, shape.L,
                                                shape.r, shape.rsf, shape.renormalize, shape.dtype))
-    return dict(name=name, shape=shape, inp=inp, ms=ms, stage=stage, work=wk, plan=plan, packed=pw is not None)
+    return dict(name=name, shape=shape, inp=inp, ms=ms, stage=stage, work=wk, plan=plan, packed=pw is not None,
+                dist=dist)
+
+
+MALL_FLUSH_BYTES = 512 << 20   # > 2x the 256 MB MALL
+
+
+def per_iteration(call, steps: int, warmup: int, flush_bytes: int = 0) -> dict:
+    """Time `call` `steps` times, each between its own pair of HIP events on
+    the current stream; with flush_bytes, a scratch buffer of that size is
+    written between iterations (outside the events) so that a small
+    footprint cannot stay resident in the MALL.  Returns mean, median, p10
+    and p90 in ms."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        if scratch is not None:
+            scratch.fill_(1)
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"mean_ms": float(t.mean()), "median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90))}
+
+
+def report_config(name: str, steps: int, warmup: int, packed: bool = True) -> dict:
+    """One of the reported-only configurations: per-iteration median/p10/p90
+    and roofline fractions of the whole layer, the MALL flushed between
+    iterations when the working set is within about 2x of it."""
+    shape, recipe = synth.workload(name)
+    inp = synth.make_inputs(shape, recipe, seed=0, device="cuda")
+    out = torch.empty((shape.T, shape.H), dtype=inp.x.dtype, device="cuda")
+    ws = ml.Workspace()
+    ids = torch.empty((shape.T, shape.Kp), dtype=torch.int32, device="cuda")
+    wts = torch.empty((shape.T, shape.Kp), dtype=torch.float32, device="cuda")
+    pw = ml.PackedWeights(inp.w13, inp.w2) if packed and shape.dtype == synth.BF16 else None
+
+    def call():
+        ml.forward_inputs(inp, out=out, workspace=ws, routing_out=(ids, wts), packed=pw)
+
+    call()
+    torch.cuda.synchronize()
+    wk = work(shape, ids.cpu().numpy(), inp.adapter_ids.cpu().numpy())
+    flush = MALL_FLUSH_BYTES if wk["bytes_layer"] < 2 * (256 << 20) else 0
+    t = per_iteration(call, steps, warmup, flush)
+    sec = t["median_ms"] * 1e-3
+    res = {"tokens_per_s": shape.T / sec, **t, "mall_flushed": bool(flush),
+           "weights": "packed" if pw is not None else "row-major", "dtype": shape.dtype,
+           "hbm_frac": wk["bytes_layer"] / sec / HBM_PEAK, "mfma_frac": wk["flops_layer"] / sec / MFMA_BF16_PEAK,
+           "bytes": wk["bytes_layer"], "flops": wk["flops_layer"], "experts": wk["experts"], "bins": wk["bins"]}
+    if shape.S > 0 and not shape.lora:
+        # the unfused comparator: the routed experts alone (output x rsf) plus
+        # the shared expert as a separate dense MLP through the same kernels
+        # (E = 1, K = 1, weight 1), then the sum
+        E = shape.E
+        w13r, w2r = inp.w13[:E].contiguous(), inp.w2[:E].contiguous()
+        w13s, w2s = inp.w13[E:].contiguous(), inp.w2[E:].contiguous()
+        pr = ml.PackedWeights(w13r, w2r) if pw is not None else None
+        ps = ml.PackedWeights(w13s, w2s) if pw is not None else None
+        ones = torch.zeros((shape.T, 1), dtype=torch.float32, device="cuda")
+        o1 = torch.empty_like(out)
+        o2 = torch.empty_like(out)
+        ws2 = ml.Workspace()
+
+        def unfused():
+            ml.moe_lora_forward(inp.x, inp.logits, None, pr if pr is not None else w13r, None if pr else w2r,
+                                K=shape.K, S=0, rsf=shape.rsf, out=o1, workspace=ws)
+            ml.moe_lora_forward(inp.x, ones, None, ps if ps is not None else w13s, None if ps else w2s,
+                                K=1, S=0, rsf=1.0, out=o2, workspace=ws2)
+            torch.add(o1, o2, out=out)
+
+        tu = per_iteration(unfused, steps, warmup, flush)
+        res["unfused"] = {"tokens_per_s": shape.T / (tu["median_ms"] * 1e-3), **tu,
+                          "speedup_fused": tu["median_ms"] / t["median_ms"]}
+    del inp, pw
+    torch.cuda.empty_cache()
+    return res
+
+
+REPORTED = ("tiny_fp32_T16", "shared_fused_T1", "shared_fused_T32", "shared_fused_T128", "heavy_skewed_T8192")
 
 
 def roofline_obj(m: dict, bound: str) -> dict:
@@ -246,6 +333,8 @@ def main() -> int:
     ap.add_argument("--prefill", default="gptoss_prefill_T4096", help="secondary workload ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--no-reported", action="store_true",
+                    help="skip the reported-only configurations (tiny fp32, shared sweep, heavy)")
     ap.add_argument("--row-major", action="store_true",
                     help="read w13/w2 row-major instead of packing them once before timing")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -274,6 +363,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": m["ms"],
+        "step_ms": {k: m["dist"][k] for k in ("median_ms", "p10_ms", "p90_ms")},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -300,8 +390,15 @@ def main() -> int:
         ps = p["shape"]
         result["prefill"] = {"workload": args.prefill, "tokens_per_s": ps.T / (p["ms"] * 1e-3),
                              "ms_per_step": p["ms"], "roofline": roofline_obj(p, "mfma"),
+                             "step_ms": {k: p["dist"][k] for k in ("median_ms", "p10_ms", "p90_ms")},
                              "layer": layer_roofline(p), "stage_us": {k: v * 1e3 for k, v in p["stage"].items()},
                              "block_m": p["plan"]["block_m"], "work": p["work"]}
+    if not args.no_reported:
+        result["reported"] = {}
+        for name in REPORTED:
+            print(f"bench: reported {name}", file=sys.stderr, flush=True)
+            result["reported"][name] = report_config(name, max(20, args.steps), max(5, args.warmup),
+                                                     packed=not args.row_major)
     print(json.dumps(result), flush=True)
     return 0
 
