@@ -171,14 +171,16 @@ def measure(name: str, steps: int, warmup: int, seed: int = 0, packed: bool = Tr
     stage = se.stage_ms()
     se.close()
 
-    # third pass: each step between its own events, for median / p10 / p90
+    # third pass: each step between its own events, for median / p10 / p90;
+    # then the same step captured once in a HIP graph and replayed
     dist = per_iteration(step, steps, 0)
+    gdist = graph_per_iteration(step, steps, 2)
 
     wk = work(shape, ids.cpu().numpy(), inp.adapter_ids.cpu().numpy())
     plan = ml.moe_lora_plan_query(ml.make_dims(shape.T, shape.H, shape.I, shape.E, shape.K, shape.S, shape.L,
                                                shape.r, shape.rsf, shape.renormalize, shape.dtype))
     return dict(name=name, shape=shape, inp=inp, ms=ms, stage=stage, work=wk, plan=plan, packed=pw is not None,
-                dist=dist)
+                dist=dist, gdist=gdist)
 
 
 MALL_FLUSH_BYTES = 512 << 20   # > 2x the 256 MB MALL
@@ -207,6 +209,22 @@ def per_iteration(call, steps: int, warmup: int, flush_bytes: int = 0) -> dict:
             "p90_ms": float(np.percentile(t, 90))}
 
 
+def graph_per_iteration(call, steps: int, warmup: int, flush_bytes: int = 0) -> dict:
+    """per_iteration over replays of `call` captured once in a HIP graph
+    (torch.cuda.CUDAGraph); `call` must already have run once eagerly so its
+    workspace exists."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    return per_iteration(g.replay, steps, warmup, flush_bytes)
+
+
 def report_config(name: str, steps: int, warmup: int, packed: bool = True) -> dict:
     """One of the reported-only configurations: per-iteration median/p10/p90
     and roofline fractions of the whole layer, the MALL flushed between
@@ -227,11 +245,13 @@ def report_config(name: str, steps: int, warmup: int, packed: bool = True) -> di
     wk = work(shape, ids.cpu().numpy(), inp.adapter_ids.cpu().numpy())
     flush = MALL_FLUSH_BYTES if wk["bytes_layer"] < 2 * (256 << 20) else 0
     t = per_iteration(call, steps, warmup, flush)
+    tg = graph_per_iteration(call, steps, warmup, flush)
     sec = t["median_ms"] * 1e-3
     res = {"tokens_per_s": shape.T / sec, **t, "mall_flushed": bool(flush),
            "weights": "packed" if pw is not None else "row-major", "dtype": shape.dtype,
            "hbm_frac": wk["bytes_layer"] / sec / HBM_PEAK, "mfma_frac": wk["flops_layer"] / sec / MFMA_BF16_PEAK,
-           "bytes": wk["bytes_layer"], "flops": wk["flops_layer"], "experts": wk["experts"], "bins": wk["bins"]}
+           "bytes": wk["bytes_layer"], "flops": wk["flops_layer"], "experts": wk["experts"], "bins": wk["bins"],
+           "graph_replay": {"tokens_per_s": shape.T / (tg["median_ms"] * 1e-3), **tg}}
     if shape.S > 0 and not shape.lora:
         # the unfused comparator: the routed experts alone (output x rsf) plus
         # the shared expert as a separate dense MLP through the same kernels
@@ -364,6 +384,8 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": m["ms"],
         "step_ms": {k: m["dist"][k] for k in ("median_ms", "p10_ms", "p90_ms")},
+        "graph_replay": {"tokens_per_s": s.T / (m["gdist"]["median_ms"] * 1e-3),
+                         **{k: m["gdist"][k] for k in ("median_ms", "p10_ms", "p90_ms")}},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -391,6 +413,8 @@ def main() -> int:
         result["prefill"] = {"workload": args.prefill, "tokens_per_s": ps.T / (p["ms"] * 1e-3),
                              "ms_per_step": p["ms"], "roofline": roofline_obj(p, "mfma"),
                              "step_ms": {k: p["dist"][k] for k in ("median_ms", "p10_ms", "p90_ms")},
+                             "graph_replay": {"tokens_per_s": ps.T / (p["gdist"]["median_ms"] * 1e-3),
+                                              **{k: p["gdist"][k] for k in ("median_ms", "p10_ms", "p90_ms")}},
                              "layer": layer_roofline(p), "stage_us": {k: v * 1e3 for k, v in p["stage"].items()},
                              "block_m": p["plan"]["block_m"], "work": p["work"]}
     if not args.no_reported:

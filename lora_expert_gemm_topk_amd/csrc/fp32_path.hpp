@@ -24,6 +24,21 @@ struct F32Params {
     int Kdim, Nout, Kp, P, cap, Ep, L, r, lora, bt;
 };
 
+// sum_c x[c] * w[c] over K (a multiple of 8): 16-byte loads, four fp32
+// accumulators (lanes of the float4) combined in a fixed order.
+__device__ __forceinline__ float dot_f32(const float *x, const float *w, int K) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < K; c += 4) {
+        const float4 xv = *reinterpret_cast<const float4 *>(x + c);
+        const float4 wv = *reinterpret_cast<const float4 *>(w + c);
+        a.x = fmaf(xv.x, wv.x, a.x);
+        a.y = fmaf(xv.y, wv.y, a.y);
+        a.z = fmaf(xv.z, wv.z, a.z);
+        a.w = fmaf(xv.w, wv.w, a.w);
+    }
+    return (a.x + a.y) + (a.z + a.w);
+}
+
 __global__ __launch_bounds__(256) void shrink_f32_kernel(const float *__restrict__ in, const int32_t *sorted_ids,
                                                          const float *__restrict__ A, const int32_t *items,
                                                          const int32_t *counters, float *s, int Kdim, int r,
@@ -37,9 +52,7 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(const float *__restrict
         const int64_t row = gather ? (int64_t)(sorted_ids[prow] / Kp) : (int64_t)prow;
         const float *x = in + row * Kdim;
         const float *a = A + (((int64_t)it.z * Ep + it.w) * r + k) * Kdim;
-        float acc = 0.f;
-        for (int c = 0; c < Kdim; ++c) acc = fmaf(x[c], a[c], acc);
-        s[(int64_t)prow * r + k] = acc;
+        s[(int64_t)prow * r + k] = dot_f32(x, a, Kdim);
     }
 }
 
@@ -61,12 +74,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
         }
         const float *x = p.in + (GU ? (int64_t)(f / p.Kp) : (int64_t)prow) * p.Kdim;
         const float *w0 = p.W + ((int64_t)e * rows_per_expert + n) * p.Kdim;
-        float v0 = 0.f, v1 = 0.f;
-        for (int c = 0; c < p.Kdim; ++c) v0 = fmaf(x[c], w0[c], v0);
-        if (GU) {
-            const float *w1 = p.W + ((int64_t)e * rows_per_expert + N + n) * p.Kdim;
-            for (int c = 0; c < p.Kdim; ++c) v1 = fmaf(x[c], w1[c], v1);
-        }
+        const float *w1 = p.W + ((int64_t)e * rows_per_expert + N + n) * p.Kdim;
+        float v0 = dot_f32(x, w0, p.Kdim), v1 = 0.f;
+        if (GU) v1 = dot_f32(x, w1, p.Kdim);
         if (p.lora) {
             const int a = p.adapter_ids[f / p.Kp];
             if (a >= 0 && a < p.L) {
