@@ -57,6 +57,11 @@ struct AlignParams {
     int tile_rows;
     int nbits_a, nbits_e;
     int lds_keys;         // 1: stage keys and the intermediate order in LDS
+    // multi-workgroup alignment (align_hist / align_scan / align_scatter)
+    int32_t *hist;        // [nb][NK] per-(block, key) counts, then prefixes
+    int32_t *ktot;        // [NK] pairs per key, then the key's first position
+    int nb, chunk;        // blocks and pairs per block
+    int nbits_k;          // bits of a composite key
 };
 
 // Ids outside their documented ranges (a precondition) are clamped so that
@@ -125,6 +130,111 @@ __device__ inline int block_excl_scan(int *arr, int n, int *scr) {
 // Where the staged 16-bit keys start inside the alignment's LDS.
 __device__ __forceinline__ uint16_t *align_keys(int *lds, int NW, int Ep, int La) {
     return reinterpret_cast<uint16_t *>(lds + align_lds_fixed_ints(NW, Ep, La));
+}
+
+// Everything after the scatter: padding rows, the tail, the block -> expert
+// map, the GEMM token tiles, the LoRA items and the counts.  Needs offE[Ep+1]
+// and totE[Ep] (expert offsets and pair counts) and, with LoRA, cnt2[NK]
+// (pairs per (expert, adapter+1) key) in LDS; tk, scr and itemOff are LDS
+// scratch.  Run by one whole workgroup.
+__device__ void align_finish(const AlignParams &p, const int *offE, const int *totE, int *tk, int *scr,
+                             const int *cnt2, int *itemOff, int npp) {
+    const int NW = (int)(blockDim.x >> 6);
+    const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int La = p.La, Ep = p.Ep, A1 = La + 1;
+    const int NK = Ep * A1;
+    const int P = p.P;
+    // ---- padding, tail and block -> expert map ---------------------------
+    for (int e = w; e < Ep; e += NW) {
+        const int b = offE[e] + totE[e], end = offE[e + 1];
+        for (int q = b + lane; q < end; q += 64) {
+            p.sorted_ids[q] = P;
+            if (p.sorted_adapter) p.sorted_adapter[q] = -1;
+        }
+    }
+    for (int q = npp + tid; q < p.cap; q += nt) {
+        p.sorted_ids[q] = P;
+        if (p.sorted_adapter) p.sorted_adapter[q] = -1;
+    }
+    for (int b = tid; b < p.max_blocks; b += nt) {
+        const int pos = b * p.bm;
+        int ex = -1;
+        if (pos < npp) {
+            int lo = 0, hi = Ep - 1;  // last e with offE[e] <= pos
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (offE[mid] <= pos) lo = mid;
+                else hi = mid - 1;
+            }
+            ex = lo;
+        }
+        p.block_expert[b] = ex;
+    }
+
+    // ---- token tiles of the LDS-tiled GEMM ---------------------------------
+    if (p.tiles != nullptr) {
+        __syncthreads();
+        for (int e = tid; e < Ep; e += nt) tk[e] = (offE[e + 1] - offE[e] + p.tile_rows - 1) / p.tile_rows;
+        __syncthreads();
+        const int ntiles = block_excl_scan(tk, Ep, scr);
+        for (int e = tid; e < Ep; e += nt) {
+            const int pad = offE[e + 1] - offE[e];
+            int it = tk[e];
+            const int t0 = it, nt_e = (pad + p.tile_rows - 1) / p.tile_rows;
+            for (int q = 0; q < pad; q += p.tile_rows) {
+                int4 v;
+                v.x = offE[e] + q;
+                v.y = min(p.tile_rows, pad - q) | (nt_e << 16);
+                v.z = e;
+                v.w = t0;
+                reinterpret_cast<int4 *>(p.tiles)[it++] = v;
+            }
+        }
+        if (tid == 0) *p.ntiles_out = ntiles;
+    }
+
+    // ---- LoRA work items: (adapter >= 0, expert) runs cut to lbm rows ------
+    int nitems = 0;
+    if (La > 0 && p.items != nullptr) {
+        for (int k = tid; k < NK; k += nt) {
+            const int a1 = k % A1;
+            itemOff[k] = (a1 == 0) ? 0 : (cnt2[k] + p.lbm - 1) / p.lbm;
+        }
+        __syncthreads();
+        nitems = block_excl_scan(itemOff, NK, scr);
+        for (int e = tid; e < Ep; e += nt) {
+            int run = offE[e];
+            for (int a1 = 0; a1 < A1; ++a1) {
+                const int k = e * A1 + a1;
+                const int c = cnt2[k];
+                if (a1 > 0) {
+                    int it = itemOff[k];
+                    for (int q = 0; q < c; q += p.lbm) {
+                        int4 v;
+                        v.x = run + q;
+                        v.y = min(p.lbm, c - q);
+                        v.z = a1 - 1;
+                        v.w = e;
+                        reinterpret_cast<int4 *>(p.items)[it++] = v;
+                    }
+                }
+                run += c;
+            }
+        }
+        for (int q = nitems + tid; q < p.max_items; q += nt) {
+            int4 v;
+            v.x = 0;
+            v.y = 0;
+            v.z = -1;
+            v.w = -1;
+            reinterpret_cast<int4 *>(p.items)[q] = v;
+        }
+    }
+    if (tid == 0) {
+        *p.npp_out = npp;
+        *p.nitems_out = nitems;
+    }
 }
 
 // The alignment proper, run by one whole workgroup.  With p.lds_keys the
@@ -255,95 +365,161 @@ __device__ void align_body(const AlignParams &p, int *lds, bool keys_ready) {
         }
     }
 
-    // ---- padding, tail and block -> expert map ---------------------------
-    for (int e = w; e < Ep; e += NW) {
-        const int b = offE[e] + totE[e], end = offE[e + 1];
-        for (int q = b + lane; q < end; q += 64) {
-            p.sorted_ids[q] = P;
-            if (p.sorted_adapter) p.sorted_adapter[q] = -1;
-        }
-    }
-    for (int q = npp + tid; q < p.cap; q += nt) {
-        p.sorted_ids[q] = P;
-        if (p.sorted_adapter) p.sorted_adapter[q] = -1;
-    }
-    for (int b = tid; b < p.max_blocks; b += nt) {
-        const int pos = b * p.bm;
-        int ex = -1;
-        if (pos < npp) {
-            int lo = 0, hi = Ep - 1;  // last e with offE[e] <= pos
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (offE[mid] <= pos) lo = mid;
-                else hi = mid - 1;
-            }
-            ex = lo;
-        }
-        p.block_expert[b] = ex;
-    }
+    align_finish(p, offE, totE, tk, scr, cnt2, itemOff, npp);
+}
 
-    // ---- token tiles of the LDS-tiled GEMM ---------------------------------
-    if (p.tiles != nullptr) {
-        __syncthreads();
-        for (int e = tid; e < Ep; e += nt) tk[e] = (offE[e + 1] - offE[e] + p.tile_rows - 1) / p.tile_rows;
-        __syncthreads();
-        const int ntiles = block_excl_scan(tk, Ep, scr);
-        for (int e = tid; e < Ep; e += nt) {
-            const int pad = offE[e + 1] - offE[e];
-            int it = tk[e];
-            const int t0 = it, nt_e = (pad + p.tile_rows - 1) / p.tile_rows;
-            for (int q = 0; q < pad; q += p.tile_rows) {
-                int4 v;
-                v.x = offE[e] + q;
-                v.y = min(p.tile_rows, pad - q) | (nt_e << 16);
-                v.z = e;
-                v.w = t0;
-                reinterpret_cast<int4 *>(p.tiles)[it++] = v;
-            }
-        }
-        if (tid == 0) *p.ntiles_out = ntiles;
-    }
+// ---- multi-workgroup alignment -------------------------------------------
+// For many pairs one workgroup is latency bound, so the same stable sort by
+// the composite key (expert, adapter+1) runs in four launches:
+//   hist     nb blocks count the keys of their contiguous slices of pairs
+//            (slice b = pairs [b*chunk, (b+1)*chunk)) into hist[b][key];
+//   colscan  per key, an exclusive prefix over the blocks (in place) and the
+//            key's total into ktot[key];
+//   scan     one workgroup turns the totals into expert offsets, writes the
+//            first position of each key back into ktot and builds the
+//            padding, block map, tiles and items as the one-workgroup path;
+//   scatter  nb blocks place their slices in pair order, one wave each.
+// Every position depends only on the input, and the output is bitwise that
+// of the one-workgroup path.
+__device__ __forceinline__ int align_key_of(const AlignParams &p, int f) {
+    const int e = clamp_expert(p.topk_ids[f], p.Ep);
+    const int a1 = p.La > 0 ? adapter_key_of(p.adapter_ids[f / p.Kp], p.La) : 0;
+    return e * (p.La + 1) + a1;
+}
 
-    // ---- LoRA work items: (adapter >= 0, expert) runs cut to lbm rows ------
-    int nitems = 0;
-    if (La > 0 && p.items != nullptr) {
-        for (int k = tid; k < NK; k += nt) {
-            const int a1 = k % A1;
-            itemOff[k] = (a1 == 0) ? 0 : (cnt2[k] + p.lbm - 1) / p.lbm;
-        }
-        __syncthreads();
-        nitems = block_excl_scan(itemOff, NK, scr);
-        for (int e = tid; e < Ep; e += nt) {
-            int run = offE[e];
-            for (int a1 = 0; a1 < A1; ++a1) {
-                const int k = e * A1 + a1;
-                const int c = cnt2[k];
-                if (a1 > 0) {
-                    int it = itemOff[k];
-                    for (int q = 0; q < c; q += p.lbm) {
-                        int4 v;
-                        v.x = run + q;
-                        v.y = min(p.lbm, c - q);
-                        v.z = a1 - 1;
-                        v.w = e;
-                        reinterpret_cast<int4 *>(p.items)[it++] = v;
-                    }
-                }
-                run += c;
-            }
-        }
-        for (int q = nitems + tid; q < p.max_items; q += nt) {
-            int4 v;
-            v.x = 0;
-            v.y = 0;
-            v.z = -1;
-            v.w = -1;
-            reinterpret_cast<int4 *>(p.items)[q] = v;
+// grid nb, block 256, LDS NK ints
+__global__ __launch_bounds__(256) void align_hist_kernel(AlignParams p) {
+    extern __shared__ int cnt[];
+    const int NK = p.Ep * (p.La + 1);
+    const int tid = (int)threadIdx.x;
+    for (int k = tid; k < NK; k += 256) cnt[k] = 0;
+    __syncthreads();
+    const int f0 = blockIdx.x * p.chunk, f1 = min(p.P, f0 + p.chunk);
+    for (int f = f0 + tid; f < f1; f += 256) atomicAdd(&cnt[align_key_of(p, f)], 1);
+    __syncthreads();
+    int32_t *row = p.hist + (int64_t)blockIdx.x * NK;
+    for (int k = tid; k < NK; k += 256) row[k] = cnt[k];
+}
+
+// grid ceil(NK/256), block 256: thread k scans column k of hist
+__global__ __launch_bounds__(256) void align_colscan_kernel(AlignParams p) {
+    const int NK = p.Ep * (p.La + 1);
+    const int k = blockIdx.x * 256 + (int)threadIdx.x;
+    if (k >= NK) return;
+    int run = 0;
+    int b = 0;
+    for (; b + 8 <= p.nb; b += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = p.hist[(int64_t)(b + u) * NK + k];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            p.hist[(int64_t)(b + u) * NK + k] = run;
+            run += c[u];
         }
     }
-    if (tid == 0) {
-        *p.npp_out = npp;
-        *p.nitems_out = nitems;
+    for (; b < p.nb; ++b) {
+        const int c = p.hist[(int64_t)b * NK + k];
+        p.hist[(int64_t)b * NK + k] = run;
+        run += c;
+    }
+    p.ktot[k] = run;
+}
+
+// ints of LDS the scan workgroup needs
+__host__ __device__ inline int64_t align_scan_lds_ints(int Ep, int La) {
+    const int64_t nk = (int64_t)Ep * (La + 1);
+    const int64_t tk = (Ep > La + 1 ? Ep : La + 1) + 1;
+    return 2 * nk + 1 + 2 * (int64_t)Ep + 1 + tk + 80;
+}
+
+// one workgroup
+__global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
+    extern __shared__ int lds[];
+    const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
+    const int La = p.La, Ep = p.Ep, A1 = La + 1;
+    const int NK = Ep * A1;
+    const int TK = (Ep > A1 ? Ep : A1) + 1;
+    int *cnt2 = lds;                 // [NK] pairs per key
+    int *itemOff = cnt2 + NK;        // [NK+1] scratch of align_finish
+    int *offE = itemOff + NK + 1;    // [Ep+1]
+    int *totE = offE + Ep + 1;       // [Ep]
+    int *tk = totE + Ep;             // [TK]
+    int *scr = tk + TK;              // [80]
+    for (int k = tid; k < NK; k += nt) cnt2[k] = p.ktot[k];
+    __syncthreads();
+    for (int e = tid; e < Ep; e += nt) {
+        int run = 0;
+        for (int a1 = 0; a1 < A1; ++a1) run += cnt2[e * A1 + a1];
+        totE[e] = run;
+        tk[e] = (run + p.bm - 1) / p.bm * p.bm;
+    }
+    __syncthreads();
+    const int npp = block_excl_scan(tk, Ep, scr);
+    for (int e = tid; e < Ep; e += nt) offE[e] = tk[e];
+    if (tid == 0) offE[Ep] = npp;
+    __syncthreads();
+    // first position of each key: its expert's offset plus the keys before it
+    for (int e = tid; e < Ep; e += nt) {
+        int run = offE[e];
+        for (int a1 = 0; a1 < A1; ++a1) {
+            p.ktot[e * A1 + a1] = run;
+            run += cnt2[e * A1 + a1];
+        }
+    }
+    align_finish(p, offE, totE, tk, scr, cnt2, itemOff, npp);
+}
+
+// grid nb, block 256, LDS NK ints: the next position of each key.  All four
+// waves load the cursors; wave 0 alone then walks the slice in pair order,
+// in windows of kScatterWin pairs per lane whose keys are loaded up front so
+// their loads overlap.  Past the one workgroup barrier only wave 0 runs, and
+// its LDS accesses execute in program order, so no further barrier is needed.
+constexpr int kScatterWin = 16;
+__global__ __launch_bounds__(256) void align_scatter_kernel(AlignParams p) {
+    extern __shared__ int cur[];
+    const int NK = p.Ep * (p.La + 1);
+    const int tid = (int)threadIdx.x, lane = lane_id();
+    const int32_t *row = p.hist + (int64_t)blockIdx.x * NK;
+    for (int k0 = 0; k0 < NK; k0 += 4 * 256) {
+        int v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k = k0 + u * 256 + tid;
+            v[u] = k < NK ? p.ktot[k] + row[k] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k = k0 + u * 256 + tid;
+            if (k < NK) cur[k] = v[u];
+        }
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    const int f0 = blockIdx.x * p.chunk, f1 = min(p.P, f0 + p.chunk);
+    for (int w0 = f0; w0 < f1; w0 += 64 * kScatterWin) {
+        int key[kScatterWin];
+#pragma unroll
+        for (int u = 0; u < kScatterWin; ++u) {
+            const int f = w0 + 64 * u + lane;
+            key[u] = f < f1 ? align_key_of(p, f) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kScatterWin; ++u) {
+            const int f = w0 + 64 * u + lane;
+            if (w0 + 64 * u >= f1) break;  // uniform
+            const bool valid = key[u] >= 0;
+            const uint64_t m = match_key((uint32_t)(valid ? key[u] : 0), valid, p.nbits_k);
+            const uint64_t lt = m & lanemask_lt();
+            if (valid) {
+                const int pos = cur[key[u]] + __popcll(lt);
+                p.sorted_ids[pos] = f;
+                if (p.sorted_adapter) p.sorted_adapter[pos] = key[u] % (p.La + 1) - 1;
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (valid && lt == 0) cur[key[u]] += __popcll(m);
+            __builtin_amdgcn_wave_barrier();
+        }
     }
 }
 

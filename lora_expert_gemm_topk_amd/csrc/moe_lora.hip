@@ -50,6 +50,9 @@ struct Plan {
     size_t align_lds = 0;
     bool lds_keys = false;   // alignment keys staged in LDS
     bool fuse_route = false; // route + align in one launch
+    bool multi = false;      // multi-workgroup alignment
+    int anb = 0, achunk = 0; // its blocks and pairs per block
+    int64_t tmp_ints = 0;    // ints of alignment scratch
     bool lora = false;
     // workspace offsets (bytes)
     size_t o_ids = 0, o_w = 0, o_sorted = 0, o_sadp = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0, o_tiles = 0;
@@ -154,6 +157,20 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
         }
     }
     if (p.align_nw == 0) return MOE_LORA_EUNSUPPORTED;
+    // many pairs: the multi-workgroup alignment (slices of 256..1024+ pairs,
+    // at most 64 slices so the per-key column scans stay short)
+#ifndef MOELORA_ALIGN_MULTI_MIN
+#define MOELORA_ALIGN_MULTI_MIN 8192
+#endif
+    const int64_t NK = p.Ep * (p.La + 1);
+    p.multi = p.P >= MOELORA_ALIGN_MULTI_MIN && NK * 4 <= kLdsBytes &&
+              align_scan_lds_ints((int)p.Ep, (int)p.La) * 4 <= kLdsBytes;
+    p.tmp_ints = p.P;
+    if (p.multi) {
+        p.achunk = (int)std::max<int64_t>(256, ((p.P + 63) / 64 + 63) / 64 * 64);
+        p.anb = (int)((p.P + p.achunk - 1) / p.achunk);
+        p.tmp_ints = std::max<int64_t>(p.P, (int64_t)p.anb * NK + NK);
+    }
     p.fuse_route = false;  // measured slower than two launches: one workgroup routes tokens serially
 
     const size_t A = 256;
@@ -171,7 +188,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     p.o_bexp = take(sizeof(int32_t) * p.max_blocks);
     p.o_cnt = take(sizeof(int32_t) * 16);
     p.o_items = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_items, 1));
-    p.o_tmp = take(sizeof(int32_t) * p.P);
+    p.o_tmp = take(sizeof(int32_t) * p.tmp_ints);
     p.o_tiles = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_tiles, 1));
     p.o_s13 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
     p.o_s2 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
@@ -181,7 +198,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     // tiled GEMM: x gathered and packed per sorted row
     p.o_xp = take(p.kind == 2 ? es * p.cap * ((d->H + 31) / 32 * 32) : 0);
     p.total = o;
-    p.align_total = round_up(sizeof(int32_t) * std::max<int64_t>(p.P, 1), A) + round_up(sizeof(int32_t) * 16, A);
+    p.align_total = round_up(sizeof(int32_t) * std::max<int64_t>(p.tmp_ints, 1), A) + round_up(sizeof(int32_t) * 16, A);
     *pl = p;
     return MOE_LORA_OK;
 }
@@ -199,7 +216,9 @@ hipError_t g_attr_err = hipSuccess;
 void set_kernel_attributes() {
     const void *fns[] = {(const void *)align_kernel, (const void *)route_align_kernel<1>,
                          (const void *)route_align_kernel<2>, (const void *)route_align_kernel<4>,
-                         (const void *)route_align_kernel<8>, (const void *)route_align_kernel<16>};
+                         (const void *)route_align_kernel<8>, (const void *)route_align_kernel<16>,
+                         (const void *)align_hist_kernel,     (const void *)align_scan_kernel,
+                         (const void *)align_scatter_kernel};
     for (const void *fn : fns) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         if (e != hipSuccess) g_attr_err = e;
@@ -265,6 +284,21 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
     ap.max_items = (int)pl.max_items;
     ap.nbits_a = bits_for(pl.La + 1);
     ap.nbits_e = bits_for(pl.Ep);
+    const int NK = (int)(pl.Ep * (pl.La + 1));
+    ap.nbits_k = bits_for(NK);
+    ap.nb = pl.anb;
+    ap.chunk = pl.achunk;
+    ap.hist = tmp;
+    ap.ktot = tmp + (int64_t)pl.anb * NK;
+    if (pl.multi && route == nullptr) {
+        const size_t klds = sizeof(int) * (size_t)NK;
+        hipLaunchKernelGGL(align_hist_kernel, dim3((unsigned)pl.anb), dim3(256), klds, st, ap);
+        hipLaunchKernelGGL(align_colscan_kernel, dim3((unsigned)((NK + 255) / 256)), dim3(256), 0, st, ap);
+        hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024),
+                           sizeof(int) * (size_t)align_scan_lds_ints((int)pl.Ep, (int)pl.La), st, ap);
+        hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)pl.anb), dim3(256), klds, st, ap);
+        return MOE_LORA_OK;
+    }
     const dim3 grid(1), block((unsigned)(pl.align_nw * 64));
     if (route != nullptr) {
         const int E = route->E;
@@ -484,7 +518,7 @@ int moe_lora_align(const moe_lora_dims *d, const int32_t *topk_ids, const int32_
     hipStream_t st = (hipStream_t)stream;
     char *ws = (char *)workspace;
     int32_t *tmp = (int32_t *)ws;
-    int32_t *cnt = (int32_t *)(ws + round_up(sizeof(int32_t) * p.P, 256));
+    int32_t *cnt = (int32_t *)(ws + round_up(sizeof(int32_t) * p.tmp_ints, 256));
     int r2 = launch_align(p, d, topk_ids, adapter_ids, sorted_ids, nullptr, block_expert, num_post_pad, lora_items,
                           num_items ? num_items : cnt + 1, tmp, nullptr, nullptr, nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;

@@ -80,6 +80,9 @@ ALIGN_CASES = [
     dict(T=300, E=8, K=3, S=0, L=5, r=8, one_expert=True), dict(T=77, E=5, K=5, S=2, L=1, r=8, bm=16),
     dict(T=8192, E=128, K=8, S=0, L=64, r=64, adapters="zipf", logits="zipf_bias"),
     dict(T=200, E=16, K=2, S=0, L=4, r=16, adapters="none"),
+    # pair counts at and just past the switch to the multi-workgroup alignment
+    # (8192 pairs; the second leaves a last slice of 4 pairs)
+    dict(T=2048, E=33, K=3, S=1, L=0, r=0), dict(T=2049, E=7, K=4, S=0, L=2, r=8),
 ]
 
 
