@@ -39,7 +39,7 @@ struct GemmParams {
     const uint16_t *W;           // gate_up: w13 [Ep, 2*Nout, Kdim]; down: w2 [Ep, Nout, Kdim]
     const uint16_t *B;           // gate_up: b13 [L, Ep, 2*Nout, r]; down: b2 [L, Ep, Nout, r]
     const float *s_part;         // [split][cap][r] fp32; LDS-tiled kernel: bf16 [cap][r]
-    void *out;                   // gate_up: h bf16 [cap, Nout] (LDS-tiled kernel: packed); down: y2 f32 [P, Nout]
+    void *out;                   // gate_up: h bf16 [cap, Nout] (LDS-tiled kernel: packed); down: y2 bf16 [P, Nout]
     int Kdim, Nout, Kp, P, cap, Ep, L, r, split, lora;
 };
 
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
         }
     } else {
         constexpr int CG = BW / 4;
-        float *yout = reinterpret_cast<float *>(p.out);
+        uint16_t *yout = reinterpret_cast<uint16_t *>(p.out);
         for (int q = (int)threadIdx.x; q < BT * CG; q += 256) {
             const int j = q / CG, cg = q % CG;
             const int prow = b * BT + j;
@@ -314,7 +314,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
                     lora_expand_add<4>(p, e, a, prow, rows, rows_per_expert, v);
                 }
             }
-            *reinterpret_cast<float4 *>(yout + (int64_t)f * N + col0) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<uint2 *>(yout + (int64_t)f * N + col0) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
     }
 }

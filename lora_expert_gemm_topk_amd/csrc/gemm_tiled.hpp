@@ -3,7 +3,7 @@
 //
 // Same contract as the streaming kernel (gemm_stream.hpp): weights are the
 // MFMA M side, the expert's tokens the N side, y13 -> SwiGLU -> h (bf16,
-// sorted row) for gate_up and y2 (fp32, pair row) for down.  The token side
+// sorted row) for gate_up and y2 (bf16, pair row) for down.  The token side
 // comes in the packed layout of common.hpp: x gathered and packed per sorted
 // row (pack.hpp) for gate_up, h as written by gate_up for down.
 //
@@ -474,17 +474,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             }
         }
     } else {
-        // y2 rows in fp32, staged through LDS so that every store writes whole
-        // 512-byte row segments.  The ring is free once every wave is past its
-        // last fragment read (no slab copy is in flight by then).  Wave w
-        // stages one 32-token column tile at a time, 32 rows x (BW/2) floats
-        // with rows padded by 16 bytes against bank conflicts.
+        // y2 rows in bf16, staged through LDS so that every store writes
+        // whole 256-byte row segments.  The ring is free once every wave is
+        // past its last fragment read (no slab copy is in flight by then).
+        // Wave w stages one 32-token column tile at a time, 32 rows x (BW/2)
+        // values with rows padded by 16 bytes against bank conflicts.
         __syncthreads();
-        constexpr int ROWF = BW / 2;                  // floats of a staged row
-        constexpr int RSTR = ROWF * 4 + 16;           // bytes between staged rows
+        constexpr int ROWF = BW / 2;                  // values of a staged row
+        constexpr int RSTR = ROWF * 2 + 16;           // bytes between staged rows
         static_assert(4 * 32 * RSTR <= kStages * STAGE_BYTES, "epilogue staging must fit the ring");
         unsigned char *stg = lds + w * 32 * RSTR;
         const int fw = i0 + wm * ROWF;                // first feature of this wave
+        uint16_t *y2 = reinterpret_cast<uint16_t *>(p.out);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (nt >= nt_live) break;
@@ -492,25 +493,24 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const float4 v = make_float4(acc[mt][nt][4 * g4 + 0], acc[mt][nt][4 * g4 + 1],
-                                                 acc[mt][nt][4 * g4 + 2], acc[mt][nt][4 * g4 + 3]);
-                    *reinterpret_cast<float4 *>(stg + l32 * RSTR + (mt * 32 + g4 * 8 + lh * 4) * 4) = v;
+                    const uint2 v = make_uint2(pack_bf16x2(acc[mt][nt][4 * g4 + 0], acc[mt][nt][4 * g4 + 1]),
+                                               pack_bf16x2(acc[mt][nt][4 * g4 + 2], acc[mt][nt][4 * g4 + 3]));
+                    *reinterpret_cast<uint2 *>(stg + l32 * RSTR + (mt * 32 + g4 * 8 + lh * 4) * 2) = v;
                 }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // lane (h, c): token 2*it + h of the column tile, floats 4c .. 4c+3
-            const int c = lane & 31, h = lane >> 5;
-            const int feat = fw + c * 4;
+            // lane (h, c): token 4*it + h of the column tile, values 8c .. 8c+7
+            const int c = lane & 15, h = lane >> 4;
+            const int feat = fw + c * 8;
 #pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const int t = 2 * it + h;
+            for (int it = 0; it < 8; ++it) {
+                const int t = 4 * it + h;
                 const int j_tok = wn * (BT / 2) + nt * 32 + t;
-                if (c * 4 < ROWF) {
-                    const float4 v = *reinterpret_cast<const float4 *>(stg + t * RSTR + c * 16);
+                if (c * 8 < ROWF) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + t * RSTR + c * 16);
                     const int f = j_tok < nrows ? tok_f[j_tok] : p.P;
-                    if (f < p.P && feat < N)
-                        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.out) + (int64_t)f * N + feat) = v;
+                    if (f < p.P && feat < N) *reinterpret_cast<u32x4 *>(y2 + (int64_t)f * N + feat) = v;
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -194,7 +194,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     p.o_s2 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
     // room for h packed (the tiled GEMM's layout): whole 32-wide slabs
     p.o_h = take(es * p.cap * (d->dtype == MOE_LORA_BF16 ? (d->I + 31) / 32 * 32 : d->I));
-    p.o_y2 = take(sizeof(float) * p.P * d->H);
+    p.o_y2 = take(es * p.P * d->H);  // y2 in the layer's dtype
     // tiled GEMM: x gathered and packed per sorted row
     p.o_xp = take(p.kind == 2 ? es * p.cap * ((d->H + 31) / 32 * 32) : 0);
     p.total = o;
@@ -545,7 +545,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     float *s13 = (float *)(ws + p.o_s13);
     float *s2 = (float *)(ws + p.o_s2);
     void *h = (void *)(ws + p.o_h);
-    float *y2 = (float *)(ws + p.o_y2);
+    void *y2 = (void *)(ws + p.o_y2);
     const int H = (int)d->H, I = (int)d->I, r = (int)d->r;
 
     void **ev = a->stage_events;
@@ -618,7 +618,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         fp.W = (const float *)a->w2;
         fp.B = (const float *)a->b2;
         fp.s = s2;
-        fp.out = y2;
+        fp.out = (float *)y2;
         fp.Kdim = I;
         fp.Nout = H;
         mark(2 * MOE_LORA_STAGE_DOWN);
