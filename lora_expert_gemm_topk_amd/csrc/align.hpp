@@ -20,7 +20,9 @@
 //   tiles[][4]              optional token tiles for the LDS-tiled GEMM: each
 //                           expert's padded rows cut into runs of at most
 //                           tile_rows rows: (start row, rows | tiles of the
-//                           expert << 16, expert, first tile of the expert)
+//                           expert << 16, expert, first tile of the expert),
+//                           with the tile count, the most tiles of one expert
+//                           and the number of experts with tiles
 //
 // Implementation: one workgroup of NW wavefronts, no host synchronisation
 // and no atomics on anything but LDS integer counters.  A stable sort by a
@@ -51,7 +53,7 @@ struct AlignParams {
     int32_t *items;
     int32_t *tmp;         // [P] global scratch (used when the keys do not fit in LDS)
     int32_t *tiles;       // optional GEMM token tiles [max_tiles][4]
-    int32_t *ntiles_out;  // tile count (when tiles != nullptr)
+    int32_t *ntiles_out;  // [3]: tile count, most tiles of one expert, experts with tiles
     int T, P, Kp, Ep, La, bm, lbm;
     int cap, max_blocks, max_items;
     int tile_rows;
@@ -173,10 +175,20 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
     }
 
     // ---- token tiles of the LDS-tiled GEMM ---------------------------------
+    // Besides the tiles: the largest tile count of one expert and the number
+    // of experts with tiles, from which the GEMM judges how skewed the load is.
     if (p.tiles != nullptr) {
         __syncthreads();
+        if (tid == 0) {
+            scr[20] = 0;
+            scr[21] = 0;
+        }
         for (int e = tid; e < Ep; e += nt) tk[e] = (offE[e + 1] - offE[e] + p.tile_rows - 1) / p.tile_rows;
         __syncthreads();
+        for (int e = tid; e < Ep; e += nt) {
+            atomicMax(&scr[20], tk[e]);
+            if (tk[e] > 0) atomicAdd(&scr[21], 1);
+        }
         const int ntiles = block_excl_scan(tk, Ep, scr);
         for (int e = tid; e < Ep; e += nt) {
             const int pad = offE[e + 1] - offE[e];
@@ -191,7 +203,12 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
                 reinterpret_cast<int4 *>(p.tiles)[it++] = v;
             }
         }
-        if (tid == 0) *p.ntiles_out = ntiles;
+        __syncthreads();
+        if (tid == 0) {
+            p.ntiles_out[0] = ntiles;
+            p.ntiles_out[1] = scr[20];
+            p.ntiles_out[2] = scr[21];
+        }
     }
 
     // ---- LoRA work items: (adapter >= 0, expert) runs cut to lbm rows ------

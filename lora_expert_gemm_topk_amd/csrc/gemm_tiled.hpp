@@ -157,14 +157,29 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // its first token tile and nt its tile count (both stored in every tile).
     // Only the first n_wtiles * n_tiles workgroups have work; the XCD remap
     // runs over exactly that many so every XCD gets an equal share.
+    //
+    // When the load is skewed (one expert holds more than twice the mean tile
+    // count of the experts with tiles) the per-XCD ranges would carry very
+    // different amounts of work; the work is then enumerated token-tile-major
+    // in dispatch order (token tile, then weight tile) and balances across the
+    // whole chip instead (measured on a Zipf-skewed 128-expert prefill: 11-13%
+    // faster; on uniform routing the XCD ranges are faster by ~12% on down).
     const int live = n_wtiles * n_tiles[0];
     if ((int)blockIdx.x >= live) return;
-    const int logical = xcd_logical((int)blockIdx.x, live);
-    const int tq = logical / n_wtiles;
-    const int4 tq_tile = reinterpret_cast<const int4 *>(tiles)[tq];
-    const int t0 = tq_tile.w, ntl = tq_tile.y >> 16;
-    const int rel = logical - n_wtiles * t0;
-    const int wt = rel / ntl, ti = t0 + rel % ntl;
+    const bool skewed = 2 * n_tiles[0] < n_tiles[1] * n_tiles[2];
+    int wt, ti;
+    if (skewed) {
+        wt = (int)blockIdx.x % n_wtiles;
+        ti = (int)blockIdx.x / n_wtiles;
+    } else {
+        const int logical = xcd_logical((int)blockIdx.x, live);
+        const int tq = logical / n_wtiles;
+        const int4 tq_tile = reinterpret_cast<const int4 *>(tiles)[tq];
+        const int t0 = tq_tile.w, ntl = tq_tile.y >> 16;
+        const int rel = logical - n_wtiles * t0;
+        wt = rel / ntl;
+        ti = t0 + rel % ntl;
+    }
     const int4 tile = reinterpret_cast<const int4 *>(tiles)[ti];
     const int row0 = tile.x, nrows = tile.y & 0xffff, e = tile.z;
     const int tid = (int)threadIdx.x, lane = lane_id();

@@ -157,6 +157,25 @@ def test_forward_small_parity(c):
         assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"
 
 
+@pytest.mark.parametrize("logits,want_skewed", [("zipf_bias", True), ("normal", False)])
+def test_tiled_work_orders(logits, want_skewed):
+    """The LDS-tiled GEMMs enumerate their work in one of two orders, chosen
+    on the device from the tile counts per expert (skewed: most tiles of one
+    expert > 2x the mean over experts with tiles).  Both orders against the
+    oracle; the routing here is checked to select the intended order."""
+    c = dict(T=1200, H=128, I=128, E=16, K=2, S=0, L=3, r=16, dtype="bf16", block_m=128)
+    shape = _shape(c)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all", logits=logits), seed=5)
+    say("work order", logits)
+    oids, _ = oracle.route(inp.logits.cpu().numpy(), shape.K, shape.S, shape.rsf)
+    cnt = np.bincount(oids.reshape(-1), minlength=shape.Ep)
+    nt = -(-(-(-cnt // 32) * 32) // 128)
+    assert (2 * nt.sum() < nt.max() * (nt > 0).sum()) == want_skewed
+    out = ml.forward_inputs(inp, **_kw(c))
+    torch.cuda.synchronize()
+    assert_close(out, oracle.forward_inputs(inp), shape.dtype, f"work order {logits}")
+
+
 @pytest.mark.parametrize("bm", [0, 128])
 def test_lora_off_is_bitwise_base(bm):
     """Zero B or every adapter -1 gives exactly the base layer (compared with ==)."""
