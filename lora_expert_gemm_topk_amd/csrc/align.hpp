@@ -18,8 +18,8 @@
 //   *nitems_out             LoRA work item count
 //   items[max_items][4]     (start row, rows <= lbm, adapter, expert)
 //   tiles[][4]              optional token tiles for the LDS-tiled GEMM: each
-//                           expert's padded rows cut into runs of at most
-//                           tile_rows rows: (start row, rows | tiles of the
+//                           expert's padded rows cut into ceil(rows/tile_rows)
+//                           runs of equal length (to 32 rows): (start row, rows | tiles of the
 //                           expert << 16, expert, first tile of the expert),
 //                           with the tile count, the most tiles of one expert
 //                           and the number of experts with tiles
@@ -183,7 +183,16 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
             scr[20] = 0;
             scr[21] = 0;
         }
-        for (int e = tid; e < Ep; e += nt) tk[e] = (offE[e + 1] - offE[e] + p.tile_rows - 1) / p.tile_rows;
+        // an expert's padded rows in ceil(rows / tile_rows) tiles of equal size
+        // (rounded up to 32 rows; the last one takes what is left)
+        auto tile_len = [&](int pad) {
+            const int n = (pad + p.tile_rows - 1) / p.tile_rows;
+            return n == 0 ? 0 : ((pad + n - 1) / n + 31) / 32 * 32;
+        };
+        for (int e = tid; e < Ep; e += nt) {
+            const int pad = offE[e + 1] - offE[e], len = tile_len(pad);
+            tk[e] = len == 0 ? 0 : (pad + len - 1) / len;
+        }
         __syncthreads();
         for (int e = tid; e < Ep; e += nt) {
             atomicMax(&scr[20], tk[e]);
@@ -191,13 +200,13 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
         }
         const int ntiles = block_excl_scan(tk, Ep, scr);
         for (int e = tid; e < Ep; e += nt) {
-            const int pad = offE[e + 1] - offE[e];
+            const int pad = offE[e + 1] - offE[e], len = tile_len(pad);
             int it = tk[e];
-            const int t0 = it, nt_e = (pad + p.tile_rows - 1) / p.tile_rows;
-            for (int q = 0; q < pad; q += p.tile_rows) {
+            const int t0 = it, nt_e = len == 0 ? 0 : (pad + len - 1) / len;
+            for (int q = 0; q < pad; q += len) {
                 int4 v;
                 v.x = offE[e] + q;
-                v.y = min(p.tile_rows, pad - q) | (nt_e << 16);
+                v.y = min(len, pad - q) | (nt_e << 16);
                 v.z = e;
                 v.w = t0;
                 reinterpret_cast<int4 *>(p.tiles)[it++] = v;

@@ -9,12 +9,14 @@
 //
 // Work unit: one (weight tile of BW rows, token tile) pair.  Token tiles come
 // from a list built by the alignment: up to BT consecutive sorted rows of ONE
-// expert, a multiple of 32 rows (experts are padded to 32 only), so a large
-// expert is cut into full BT-row tiles plus one shorter tail tile.  MFMA
+// expert, a multiple of 32 rows (experts are padded to 32 only); an expert's
+// rows are cut into tiles of equal size (to 32 rows), so the token tiles that
+// share a weight tile run at the same pace and meet its slabs in L2.  MFMA
 // column tiles (32 tokens) past the tile's rows are skipped outright, which
 // keeps the padding cost at 32-row granularity while the tile stays large.
 //
-// Workgroup: 4 wavefronts in a 2 x 2 grid, each owning (BW/2) x (BT/2) as
+// Workgroup: 4 wavefronts in a 2 x 2 grid, each owning BW/2 weight rows and
+// every other 32-token column tile (so a short tile splits evenly), as
 // (BW/64) x (BT/64) MFMA tiles of 32 x 32; with BW = BT = 256 every wave does
 // 16 MFMAs per 16-wide k-step on 8 fragment reads, which keeps LDS traffic
 // (reads + stage fills) under the ~128 B/clk/CU that gfx950 sustains.
@@ -191,7 +193,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     const int i0 = wt * (GU ? BW / 2 : BW);
     const int rows_per_expert = GU ? 2 * N : N;
     // MFMA column tiles of this wave that hold at least one sorted row
-    const int nt_live = max(0, min(NT, (nrows - wn * (BT / 2) + 31) / 32));
+    // 32-row column tiles alternate between the two wave columns (tile c to
+    // wn = c % 2), so a short tile splits its rows evenly between them
+    const int nt_live = max(0, min(NT, (nrows / 32 - wn + 1) / 2));
 
     // ---- token metadata and the tile's adapter list ----------------------
     // tok_f / tok_a: pair index and adapter of each tile row (P / -1 past the
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             for (int q = 0; q < 16; ++q) acc[mt][nt][q] = 0.f;
 
     const int a_row0 = wm * (BW / 2) + l32;        // + mt*32
-    const int b_row0 = BW + wn * (BT / 2) + l32;   // + nt*32
+    const int b_row0 = BW + wn * 32 + l32;         // + nt*64
     // Fragment reads of one 16-wide k-step (NTL live column tiles) and its MFMAs.
     auto rd = [&](auto ntl, u32x4 *af, u32x4 *bfr, int stage, int ks) {
         constexpr int NTL = decltype(ntl)::value;
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             af[mt] = *reinterpret_cast<const u32x4 *>(base + lds_off<WP>(a_row0 + mt * 32, c));
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt)
-            bfr[nt] = *reinterpret_cast<const u32x4 *>(base + lds_off<B_PACKED>(b_row0 + nt * 32, c));
+            bfr[nt] = *reinterpret_cast<const u32x4 *>(base + lds_off<B_PACKED>(b_row0 + nt * 64, c));
     };
     auto mm = [&](auto ntl, const u32x4 *af, const u32x4 *bfr) {
         constexpr int NTL = decltype(ntl)::value;
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         constexpr int I = decltype(i)::value;
         const int c = ks * 2 + lh;
         if constexpr (I < MT) af[I] = *reinterpret_cast<const u32x4 *>(base + lds_off<WP>(a_row0 + I * 32, c));
-        else bfr[I - MT] = *reinterpret_cast<const u32x4 *>(base + lds_off<B_PACKED>(b_row0 + (I - MT) * 32, c));
+        else bfr[I - MT] = *reinterpret_cast<const u32x4 *>(base + lds_off<B_PACKED>(b_row0 + (I - MT) * 64, c));
     };
     auto mm_one = [&](auto i, const u32x4 *af, const u32x4 *bfr) {
         constexpr int I = decltype(i)::value;
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (nt >= nt_live) break;
-            const int j_tok = wn * (BT / 2) + nt * 32 + l32;
+            const int j_tok = (2 * nt + wn) * 32 + l32;
             if (j_tok >= nrows) continue;
             const int prow = row0 + j_tok;
             const bool valid = tok_f[j_tok] < p.P;
@@ -521,7 +525,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
                 const int t = 4 * it + h;
-                const int j_tok = wn * (BT / 2) + nt * 32 + t;
+                const int j_tok = (2 * nt + wn) * 32 + t;
                 if (c * 8 < ROWF) {
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + t * RSTR + c * 16);
                     const int f = j_tok < nrows ? tok_f[j_tok] : p.P;
