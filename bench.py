@@ -39,7 +39,7 @@ ROOT = Path(__file__).resolve().parent
 CSRC = ROOT / "lora_expert_gemm_topk_amd" / "csrc"
 # the dominant kernels' sources and their launch code: a recorded counter
 # reading stays valid only while these are unchanged
-KERNEL_SOURCES = ("common.hpp", "gemm_stream.hpp", "gemm_tiled.hpp", "pack.hpp", "moe_lora.hip")
+KERNEL_SOURCES = ("common.hpp", "align.hpp", "gemm_stream.hpp", "gemm_tiled.hpp", "pack.hpp", "moe_lora.hip")
 
 
 def kernel_sources_sha256() -> str:

@@ -626,7 +626,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
                            dim3(256), 0, st, fp);
         mark(2 * MOE_LORA_STAGE_DOWN + 1);
         mark(2 * MOE_LORA_STAGE_COMBINE);
-        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)d->T), dim3(256),
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((H / kCombineVec<false> + 255) / 256), (unsigned)d->T), dim3(256),
                            0, st, y2, wts, a->out, (int)d->T, H, (int)p.Kp, d->routed_scaling_factor);
         mark(2 * MOE_LORA_STAGE_COMBINE + 1);
     } else {
@@ -694,7 +694,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         launch_gemm<false>(p, gp, tiles, cnt + 2, a->weights_packed != 0, st);
         mark(2 * MOE_LORA_STAGE_DOWN + 1);
         mark(2 * MOE_LORA_STAGE_COMBINE);
-        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)d->T), dim3(256),
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((H / kCombineVec<true> + 255) / 256), (unsigned)d->T), dim3(256),
                            0, st, y2, wts, a->out, (int)d->T, H, (int)p.Kp, d->routed_scaling_factor);
         mark(2 * MOE_LORA_STAGE_COMBINE + 1);
     }
