@@ -24,8 +24,10 @@
 //                           with the tile count, the most tiles of one expert
 //                           and the number of experts with tiles
 //
-// Implementation: one workgroup of NW wavefronts, no host synchronisation
-// and no atomics on anything but LDS integer counters.  A stable sort by a
+// Implementation (below 8192 pairs; the multi-workgroup form for more pairs
+// is described further down): one workgroup of NW wavefronts, no host
+// synchronisation and no atomics on anything but LDS integer counters.  A
+// stable sort by a
 // composite key is done as two stable counting passes (least significant
 // key first): by adapter+1, then by expert.  Each pass gives every wave a
 // contiguous segment of the input; a wave walks its segment 64 pairs at a

@@ -6,7 +6,7 @@
 //             I + [i0, i0+BW/2); epilogue: + LoRA expand (s13 . B13[a,e]),
 //             h = silu(gate) * up, stored bf16 at the sorted row p.
 //   down:     y2[f, n]  = sum_i h[p, i] * W2[e, n, i]; epilogue: + LoRA
-//             expand (s2 . B2[a,e]), stored fp32 at the pair row f.
+//             expand (s2 . B2[a,e]), stored bf16 at the pair row f.
 // (aitrends.kr summary of the AWS multi-LoRA MoE post: LoRA shrink/expand
 // fused into each expert projection, "section details"; an adapter path on
 // gate_up and on down, "image analysis" diagram; the LoRA sum folded into
