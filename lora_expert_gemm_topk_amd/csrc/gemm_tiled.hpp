@@ -463,35 +463,41 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         // features fb + mt*16 + g4*4 + {0, 1} with fb = i0 + wm*64 + lh*2, so
         // packed_off splits into a per-token part and a constant per (mt, g4).
         const int64_t nslab_out = (N + kSlabK - 1) / kSlabK;
+        const int flim = (int)(nslab_out * kSlabK);  // features the packed h holds
         const int fb = i0 + wm * (BW / 4) + lh * 2;
         uint16_t *hbase = reinterpret_cast<uint16_t *>(p.out) + packed_off(0, fb, nslab_out);
+        // Tiles wholly inside N (all but the last weight tile) store without
+        // feature checks; the check is a template flag so that neither form
+        // branches per element.
+        auto emit = [&](auto checked) {
+            constexpr bool CHK = decltype(checked)::value;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            if (nt >= nt_live) break;
-            const int j_tok = (2 * nt + wn) * 32 + l32;
-            if (j_tok >= nrows) continue;
-            const int prow = row0 + j_tok;
-            const bool valid = tok_f[j_tok] < p.P;
-            uint16_t *hrow = hbase + (int64_t)(prow >> 4) * nslab_out * kBlockElems + (prow & 15) * 8;
+            for (int nt = 0; nt < NT; ++nt) {
+                if (nt >= nt_live) break;
+                const int j_tok = (2 * nt + wn) * 32 + l32;  // < nrows: nrows is a multiple of 32
+                const int prow = row0 + j_tok;
+                const bool valid = tok_f[j_tok] < p.P;
+                uint16_t *hrow = hbase + (int64_t)(prow >> 4) * nslab_out * kBlockElems + (prow & 15) * 8;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+                for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int feat = fb + mt * 16 + g4 * 4;
-                    if (feat >= nslab_out * kSlabK) continue;
-                    uint32_t v = 0u;  // padding rows and features past N stay zero
-                    if (valid && feat < N) {
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int feat = fb + mt * 16 + g4 * 4;
                         const float g0 = acc[mt][nt][4 * g4 + 0], g1 = acc[mt][nt][4 * g4 + 1];
                         const float u0 = acc[mt][nt][4 * g4 + 2], u1 = acc[mt][nt][4 * g4 + 3];
-                        v = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
+                        const uint32_t hv = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
+                        // padding rows and features past N stay zero
+                        const uint32_t v = (valid && (!CHK || feat < N)) ? hv : 0u;
+                        // feature offset fb + mt*16 + g4*4 relative to fb: slab mt/2,
+                        // 8-column chunk 2*(mt%2) + g4/2, column 4*(g4%2)
+                        const int koff = (mt >> 1) * kBlockElems + (2 * (mt & 1) + (g4 >> 1)) * 128 + (g4 & 1) * 4;
+                        if (!CHK || feat < flim) *reinterpret_cast<uint32_t *>(hrow + koff) = v;
                     }
-                    // feature offset fb + mt*16 + g4*4 relative to fb: slab mt/2,
-                    // 8-column chunk 2*(mt%2) + g4/2, column 4*(g4%2)
-                    const int koff = (mt >> 1) * kBlockElems + (2 * (mt & 1) + (g4 >> 1)) * 128 + (g4 & 1) * 4;
-                    *reinterpret_cast<uint32_t *>(hrow + koff) = v;
                 }
             }
-        }
+        };
+        if (i0 + BW / 2 <= N) emit(std::false_type{});
+        else emit(std::true_type{});
     } else {
         // y2 rows in bf16, staged through LDS so that every store writes
         // whole 256-byte row segments.  The ring is free once every wave is
