@@ -83,6 +83,9 @@ ALIGN_CASES = [
     # pair counts at and just past the switch to the multi-workgroup alignment
     # (8192 pairs; the second leaves a last slice of 4 pairs)
     dict(T=2048, E=33, K=3, S=1, L=0, r=0), dict(T=2049, E=7, K=4, S=0, L=2, r=8),
+    # 80000 pairs: slices of 1280 pairs, so each scatter wave walks two windows
+    dict(T=10000, E=64, K=8, S=0, L=16, r=16, adapters="zipf", logits="zipf_bias"),
+    dict(T=3000, E=128, K=8, S=1, L=0, r=0),
 ]
 
 
