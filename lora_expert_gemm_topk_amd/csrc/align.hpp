@@ -178,7 +178,7 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
 
     // ---- token tiles of the LDS-tiled GEMM ---------------------------------
     // Besides the tiles: the largest tile count of one expert and the number
-    // of experts with tiles, from which the GEMM judges how skewed the load is.
+    // of experts with tiles, from which the GEMM decides whether the load is skewed.
     if (p.tiles != nullptr) {
         __syncthreads();
         if (tid == 0) {

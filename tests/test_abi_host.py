@@ -79,6 +79,25 @@ def test_plan_sizes_follow_the_bounds():
         assert p["workspace_bytes"] == ml.moe_lora_workspace_bytes(d) > 0
 
 
+def test_align_workspace_covers_both_alignment_forms():
+    """moe_lora_align's workspace holds the P-int scratch of the one-workgroup
+    alignment and, from 8192 pairs on, the [slices][keys] + [keys] ints of the
+    multi-workgroup form (slices of max(256, ceil(P/64) rounded up to 64)
+    pairs)."""
+    for T, E, K, S, L, r in [(64, 32, 4, 0, 8, 16), (2047, 7, 4, 0, 2, 8), (2048, 7, 4, 0, 2, 8),
+                             (4096, 32, 4, 0, 32, 32), (8192, 128, 8, 0, 64, 64), (10000, 64, 8, 0, 16, 16)]:
+        p = ml.moe_lora_plan_query(_dims(T=T, E=E, K=K, S=S, L=L, r=r))
+        P, Ep = T * (K + S), E + S
+        La = L if (L and r) else 0
+        need = 4 * P
+        if P >= 8192:
+            chunk = max(256, -(-(-(-P // 64)) // 64) * 64)
+            nb = -(-P // chunk)
+            nk = Ep * (La + 1)
+            need = max(need, 4 * (nb * nk + nk))
+        assert p["align_workspace_bytes"] >= need + 64
+
+
 def _args(**kw):
     a = ml.MoeLoraArgs()
     fields = dict(hidden=0x1000, router_logits=0x2000, adapter_ids=0x3000, w13=0x4000, w2=0x5000,
