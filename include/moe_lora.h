@@ -59,8 +59,11 @@ extern "C" {
 #define MOE_LORA_BF16 1
 
 /* Stages of moe_lora_forward, in launch order (for moe_lora_args.stage_events).
- * ALIGN includes, with the LDS-tiled GEMM (gemm_kind 2), the gather-and-pack
- * of x into sorted-row order; each other stage is one kernel. */
+ * With the LDS-tiled GEMM (gemm_kind 2) x is gathered and packed into
+ * sorted-row order: in the same launch as the gate_up shrink (stage SHRINK13)
+ * when LoRA is active, else as a second launch of stage ALIGN.  ALIGN is one
+ * launch below 8192 (token, slot) pairs and four from there on; each other
+ * stage is one kernel. */
 #define MOE_LORA_STAGE_ROUTE 0
 #define MOE_LORA_STAGE_ALIGN 1
 #define MOE_LORA_STAGE_SHRINK13 2

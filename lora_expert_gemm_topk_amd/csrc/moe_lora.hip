@@ -331,6 +331,25 @@ void launch_shrink_rows_nt(const ShrinkParams &sp, int r, int split, int max_ite
     else hipLaunchKernelGGL((shrink_kernel<NT, 8, false>), grid, block, 0, st, sp);
 }
 
+template <int NT>
+void launch_pack_shrink_nt(const PackXParams &xp, const ShrinkParams &sp, int r, int mi, unsigned groups,
+                           hipStream_t st) {
+    const dim3 grid((unsigned)mi + groups), block(256);
+    if (r <= 16) hipLaunchKernelGGL((pack_x_shrink_kernel<NT, 1>), grid, block, 0, st, xp, sp, mi);
+    else if (r <= 32) hipLaunchKernelGGL((pack_x_shrink_kernel<NT, 2>), grid, block, 0, st, xp, sp, mi);
+    else if (r <= 64) hipLaunchKernelGGL((pack_x_shrink_kernel<NT, 4>), grid, block, 0, st, xp, sp, mi);
+    else hipLaunchKernelGGL((pack_x_shrink_kernel<NT, 8>), grid, block, 0, st, xp, sp, mi);
+}
+
+// gate_up shrink and x pack in one launch (tiled path; the shrink is unsplit there)
+void launch_pack_shrink(const Plan &pl, const PackXParams &xp, ShrinkParams sp, int r, hipStream_t st) {
+    sp.chunks_per_split = (sp.Kdim + 31) / 32;
+    const int mi = (int)pl.max_items;
+    const unsigned groups = (unsigned)(pl.cap / 16);
+    if (pl.lbm == 16) launch_pack_shrink_nt<1>(xp, sp, r, mi, groups, st);
+    else launch_pack_shrink_nt<2>(xp, sp, r, mi, groups, st);
+}
+
 void launch_shrink(const Plan &pl, ShrinkParams sp, bool gather, int r, hipStream_t st) {
     const int nch = (sp.Kdim + 31) / 32;
     sp.chunks_per_split = (nch + pl.split - 1) / pl.split;
@@ -562,18 +581,18 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
                           cnt + 1, tmp,
                           p.kind == 2 ? tiles : nullptr, cnt + 2, p.fuse_route ? &rp : nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;
-    if (p.kind == 2) {
-        // the tiled GEMM reads x gathered and packed per sorted row
-        PackXParams xp;
-        xp.x = (const uint16_t *)a->hidden;
-        xp.sorted_ids = sorted;
-        xp.counters = cnt;
-        xp.xp = (uint16_t *)(ws + p.o_xp);
-        xp.H = H;
-        xp.P = (int)p.P;
-        xp.Kp = (int)p.Kp;
+    // the tiled GEMM reads x gathered and packed per sorted row; with LoRA
+    // the pack shares one launch with the gate_up shrink (stage SHRINK13)
+    PackXParams xp;
+    xp.x = (const uint16_t *)a->hidden;
+    xp.sorted_ids = sorted;
+    xp.counters = cnt;
+    xp.xp = (uint16_t *)(ws + p.o_xp);
+    xp.H = H;
+    xp.P = (int)p.P;
+    xp.Kp = (int)p.Kp;
+    if (p.kind == 2 && !p.lora)
         hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)(p.cap / 16)), dim3(256), 0, st, xp);
-    }
     mark(2 * MOE_LORA_STAGE_ALIGN + 1);
 
     if (p.kind == 0) {
@@ -647,7 +666,8 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
             sp.A = (const uint16_t *)a->a13;
             sp.s_part = s13;
             sp.Kdim = H;
-            launch_shrink(p, sp, true, r, st);
+            if (p.kind == 2) launch_pack_shrink(p, xp, sp, r, st);
+            else launch_shrink(p, sp, true, r, st);
         }
         mark(2 * MOE_LORA_STAGE_SHRINK13 + 1);
         GemmParams gp;

@@ -21,11 +21,10 @@ struct PackXParams {
     int H, P, Kp;
 };
 
-// One workgroup per 16-row group; wave w packs slabs w, w+4, ...  Lane l
+// One workgroup per 16-row group g; wave w packs slabs w, w+4, ...  Lane l
 // reads row l/4, chunk l%4 of the slab (4 lanes cover one row's 64 contiguous
 // bytes) and writes it to its place in the block.
-__global__ __launch_bounds__(256) void pack_x_kernel(PackXParams p) {
-    const int g = blockIdx.x;
+__device__ __forceinline__ void pack_x_group(const PackXParams &p, int g) {
     if (g * 16 >= p.counters[0]) return;
     const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
     const int r = lane >> 2, c = lane & 3;
@@ -40,6 +39,8 @@ __global__ __launch_bounds__(256) void pack_x_kernel(PackXParams p) {
         *reinterpret_cast<u32x4 *>(dst + (int64_t)s * kBlockElems) = v;
     }
 }
+
+__global__ __launch_bounds__(256) void pack_x_kernel(PackXParams p) { pack_x_group(p, (int)blockIdx.x); }
 
 // Packed expert weights (see moe_lora_pack_weights): w13 with the gate and up
 // rows of 8 features per 16-row group, w2 with 16 consecutive rows per

@@ -19,6 +19,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "pack.hpp"
 
 namespace moelora {
 
@@ -37,10 +38,10 @@ struct ShrinkParams {
 
 // NT: 16-row token subtiles per item (lora_block_m = 16*NT); MT: 16-row
 // rank subtiles (r <= 16*MT); GATHER: rows come from x through sorted_ids.
+// One workgroup's work: item `item`, K split `ks`.
 template <int NT, int MT, bool GATHER>
-__global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
+__device__ __forceinline__ void shrink_item(const ShrinkParams &p, int item, int ks) {
     __shared__ float red[4][16 * NT][16 * MT + 4];
-    const int item = blockIdx.x;
     if (item >= p.counters[1]) return;
     const int4 it = reinterpret_cast<const int4 *>(p.items)[item];
     const int p0 = it.x, len = it.y, a = it.z, e = it.w;
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nch = (int)((Kd + 31) / 32);
-    const int c_beg = blockIdx.y * p.chunks_per_split;
+    const int c_beg = ks * p.chunks_per_split;
     const int c_end = min(nch, c_beg + p.chunks_per_split);
     // Chunks c_beg + w, +4, +8, ... go to wave w; a wave issues the loads of
     // kBatch chunks before their MFMAs so its memory requests overlap (chunks
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
             for (int i = 0; i < 4; ++i) red[w][nt * 16 + l16][mt * 16 + g * 4 + i] = acc[mt][nt][i];
     __syncthreads();
     const int R4 = (p.r + 3) / 4;
-    float *dst = p.s_part + ((int64_t)blockIdx.y * p.cap + p0) * p.r;
+    float *dst = p.s_part + ((int64_t)ks * p.cap + p0) * p.r;
     uint16_t *dst16 = reinterpret_cast<uint16_t *>(p.s_part) + (int64_t)p0 * p.r;
     for (int q = (int)threadIdx.x; q < len * R4; q += 256) {
         const int j = q / R4, k = (q % R4) * 4;
@@ -133,6 +134,23 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
             else dst[(int64_t)j * p.r + k + i] = v;
         }
     }
+}
+
+template <int NT, int MT, bool GATHER>
+__global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
+    shrink_item<NT, MT, GATHER>(p, (int)blockIdx.x, (int)blockIdx.y);
+}
+
+// The gate_up shrink (unsplit, x gathered) and the gather-and-pack of x for
+// the LDS-tiled GEMM in one launch: both need only the alignment, one mostly
+// reads and the other mostly writes, so their memory traffic overlaps and
+// one kernel boundary goes.  Workgroups [0, n_items) take shrink items (they
+// are dispatched first), the rest one 16-row pack group each.
+template <int NT, int MT>
+__global__ __launch_bounds__(256) void pack_x_shrink_kernel(PackXParams xp, ShrinkParams sp, int n_items) {
+    const int b = (int)blockIdx.x;
+    if (b < n_items) shrink_item<NT, MT, true>(sp, b, 0);
+    else pack_x_group(xp, b - n_items);
 }
 
 }  // namespace moelora
