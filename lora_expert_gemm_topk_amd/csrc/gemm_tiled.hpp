@@ -200,8 +200,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // ---- token metadata and the tile's adapter list ----------------------
     // tok_f / tok_a: pair index and adapter of each tile row (P / -1 past the
     // tile's rows); alist: the adapters present, ascending (the alignment
-    // sorts an expert's rows by adapter, so each is one run of rows).
-    __shared__ int tok_f[BT], tok_a[BT], alist[BT], wcnt[5];
+    // sorts an expert's rows by adapter, so each is one run of rows); arun:
+    // the first and one-past-last row of each adapter's run.
+    __shared__ int tok_f[BT], tok_a[BT], alist[BT], arun[2 * BT], wcnt[5];
     const int my_row = row0 + min(tid, nrows - 1);
     const int f_row = (tid < BT) ? p.sorted_ids[my_row] : p.P;
     const int a_row = (p.lora && tid < BT) ? p.sorted_adapter[my_row] : -1;
@@ -326,6 +327,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mt]), as_bf16x8(bfr[nt]),
                                                                       acc[mt][nt], 0, 0, 0);
     };
+    // mm restricted to the column tiles set in `live` (wave-uniform)
+    auto mm_live = [&](auto ntl, const u32x4 *af, const u32x4 *bfr, int live) {
+        constexpr int NTL = decltype(ntl)::value;
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) {
+            if (!((live >> nt) & 1)) continue;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mt]), as_bf16x8(bfr[nt]),
+                                                                      acc[mt][nt], 0, 0, 0);
+        }
+    };
     // Single steps of the above: fragment read i (A fragments first, then B)
     // and MFMA i (column tile i / MT, row tile i % MT).
     auto rd_one = [&](auto i, u32x4 *af, u32x4 *bfr, const unsigned char *base, int ks) {
@@ -365,12 +378,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     {
         const int a = tid < BT ? tok_a[tid] : -1;
         const bool start = a >= 0 && (tid == 0 || tok_a[tid - 1] != a);
+        const bool end = a >= 0 && (tid == BT - 1 || tok_a[tid + 1] != a);
         const uint64_t m = __ballot(start);
         if (lane == 0) wcnt[w] = __popcll(m);
         lds_barrier();
         int before = 0;
         for (int v = 0; v < w; ++v) before += wcnt[v];
-        if (start) alist[before + __popcll(m & lanemask_lt())] = a;
+        const int run = before + __popcll(m & lanemask_lt());  // runs starting before this row
+        if (start) {
+            alist[run] = a;
+            arun[2 * run] = tid;
+        }
+        if (end) arun[2 * (run + (start ? 1 : 0)) - 1] = tid + 1;  // this row's run
         if (tid == 0) wcnt[4] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
         lds_barrier();
     }
@@ -435,17 +454,32 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
                 });
             }
         }
-        // the rest: LoRA slabs and the drain of the ring
+        // The rest: the drain of the ring and the LoRA slabs.  A LoRA slab
+        // adds nonzero products only on its adapter's run of rows, so the
+        // MFMAs of column tiles outside that run (which would add exact zeros)
+        // are skipped.
         for (; kt < nk_tot; ++kt) {
+            int live = (1 << NTL) - 1;
+            if (kt >= nk) {
+                const int ai = (kt - nk) / rs;
+                const int lo = __builtin_amdgcn_readfirstlane(arun[2 * ai]);
+                const int hi = __builtin_amdgcn_readfirstlane(arun[2 * ai + 1]);
+                live = 0;
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    const int c0 = (2 * nt + wn) * 32;
+                    if (c0 < hi && c0 + 32 > lo) live |= 1 << nt;
+                }
+            }
             rd(ntl, a1, b1, kt % kStages, 1);
-            mm(ntl, a0, b0);
+            mm_live(ntl, a0, b0, live);
             if (kt + 1 < nk_tot) {
                 // issued so far: slabs 0 .. min(kt + kStages - 2, nk_tot - 1)
                 wait_slab(min(kStages - 3, nk_tot - 2 - kt));
                 if (kt + kStages - 1 < nk_tot) issue(kt + kStages - 1);
                 rd(ntl, a0, b0, (kt + 1) % kStages, 0);
             }
-            mm(ntl, a1, b1);
+            mm_live(ntl, a1, b1, live);
         }
     };
     switch (nt_live) {
