@@ -40,7 +40,6 @@
 #pragma once
 
 #include "common.hpp"
-#include "route.hpp"
 
 namespace moelora {
 
@@ -266,9 +265,8 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
 }
 
 // The alignment proper, run by one whole workgroup.  With p.lds_keys the
-// keys are bulk-loaded into LDS first unless `keys_ready` says the caller
-// already put them there.
-__device__ void align_body(const AlignParams &p, int *lds, bool keys_ready) {
+// keys are bulk-loaded into LDS first.
+__device__ void align_body(const AlignParams &p, int *lds) {
     const int NW = (int)(blockDim.x >> 6);
     const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -290,7 +288,7 @@ __device__ void align_body(const AlignParams &p, int *lds, bool keys_ready) {
     uint16_t *oL = eL + P;                       // [P] order after the adapter pass
     uint16_t *aL = oL + P;                       // [T] adapter+1 of token t
 
-    if (lk && !keys_ready) {
+    if (lk) {
         for (int f = tid; f < P; f += nt) eL[f] = (uint16_t)clamp_expert(p.topk_ids[f], Ep);
         for (int t = tid; t < p.T; t += nt) aL[t] = (uint16_t)(La > 0 ? adapter_key_of(p.adapter_ids[t], La) : 0);
     }
@@ -553,29 +551,7 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(AlignParams p) {
 
 __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
     extern __shared__ int lds[];
-    align_body(p, lds, false);
-}
-
-// Routing and alignment in one workgroup, for calls small enough that one
-// launch is cheaper than two: every wave routes tokens w, w+NW, ... (the
-// routing rule of route.hpp), writes ids and weights to global memory and
-// the per-pair expert keys straight into LDS, then the workgroup aligns.
-// Needs p.lds_keys.
-template <int VPL>
-__global__ __launch_bounds__(1024) void route_align_kernel(RouteParams rp, AlignParams p) {
-    extern __shared__ int lds[];
-    const int NW = (int)(blockDim.x >> 6);
-    const int w = (int)(threadIdx.x >> 6), lane = lane_id();
-    uint16_t *eL = align_keys(lds, NW, p.Ep, p.La);
-    uint16_t *aL = eL + 2 * p.P;
-    for (int t = w; t < rp.T; t += NW) {
-        const int id = route_one_token<VPL>(rp, t);
-        if (lane < p.Kp) eL[t * p.Kp + lane] = (uint16_t)clamp_expert(id, p.Ep);
-    }
-    for (int t = (int)threadIdx.x; t < p.T; t += (int)blockDim.x)
-        aL[t] = (uint16_t)(p.La > 0 ? adapter_key_of(p.adapter_ids[t], p.La) : 0);
-    __syncthreads();
-    align_body(p, lds, true);
+    align_body(p, lds);
 }
 
 }  // namespace moelora

@@ -49,7 +49,6 @@ struct Plan {
     int align_nw = 16;
     size_t align_lds = 0;
     bool lds_keys = false;   // alignment keys staged in LDS
-    bool fuse_route = false; // route + align in one launch
     bool multi = false;      // multi-workgroup alignment
     int anb = 0, achunk = 0; // its blocks and pairs per block
     int64_t tmp_ints = 0;    // ints of alignment scratch
@@ -171,7 +170,6 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
         p.anb = (int)((p.P + p.achunk - 1) / p.achunk);
         p.tmp_ints = std::max<int64_t>(p.P, (int64_t)p.anb * NK + NK);
     }
-    p.fuse_route = false;  // measured slower than two launches: one workgroup routes tokens serially
 
     const size_t A = 256;
     const size_t es = d->dtype == MOE_LORA_BF16 ? 2 : 4;
@@ -214,9 +212,7 @@ std::once_flag g_attr_once;
 hipError_t g_attr_err = hipSuccess;
 
 void set_kernel_attributes() {
-    const void *fns[] = {(const void *)align_kernel, (const void *)route_align_kernel<1>,
-                         (const void *)route_align_kernel<2>, (const void *)route_align_kernel<4>,
-                         (const void *)route_align_kernel<8>, (const void *)route_align_kernel<16>,
+    const void *fns[] = {(const void *)align_kernel,
                          (const void *)align_hist_kernel,     (const void *)align_scan_kernel,
                          (const void *)align_scatter_kernel};
     for (const void *fn : fns) {
@@ -251,10 +247,10 @@ int launch_route(const moe_lora_dims *d, const float *logits, int32_t *ids, floa
     return MOE_LORA_OK;
 }
 
-// Alignment (and, with `route` non-null, the routing in the same launch).
+// Alignment: one workgroup below the multi-workgroup threshold, else four launches.
 int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
                  int32_t *sorted, int32_t *sorted_adapter, int32_t *bexp, int32_t *npp, int32_t *items,
-                 int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles, const RouteParams *route,
+                 int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles,
                  hipStream_t st) {
     std::call_once(g_attr_once, set_kernel_attributes);
     if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
@@ -290,7 +286,7 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
     ap.chunk = pl.achunk;
     ap.hist = tmp;
     ap.ktot = tmp + (int64_t)pl.anb * NK;
-    if (pl.multi && route == nullptr) {
+    if (pl.multi) {
         const size_t klds = sizeof(int) * (size_t)NK;
         hipLaunchKernelGGL(align_hist_kernel, dim3((unsigned)pl.anb), dim3(256), klds, st, ap);
         hipLaunchKernelGGL(align_colscan_kernel, dim3((unsigned)((NK + 255) / 256)), dim3(256), 0, st, ap);
@@ -300,16 +296,7 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
         return MOE_LORA_OK;
     }
     const dim3 grid(1), block((unsigned)(pl.align_nw * 64));
-    if (route != nullptr) {
-        const int E = route->E;
-        if (E <= 64) hipLaunchKernelGGL(route_align_kernel<1>, grid, block, pl.align_lds, st, *route, ap);
-        else if (E <= 128) hipLaunchKernelGGL(route_align_kernel<2>, grid, block, pl.align_lds, st, *route, ap);
-        else if (E <= 256) hipLaunchKernelGGL(route_align_kernel<4>, grid, block, pl.align_lds, st, *route, ap);
-        else if (E <= 512) hipLaunchKernelGGL(route_align_kernel<8>, grid, block, pl.align_lds, st, *route, ap);
-        else hipLaunchKernelGGL(route_align_kernel<16>, grid, block, pl.align_lds, st, *route, ap);
-    } else {
-        hipLaunchKernelGGL(align_kernel, grid, block, pl.align_lds, st, ap);
-    }
+    hipLaunchKernelGGL(align_kernel, grid, block, pl.align_lds, st, ap);
     return MOE_LORA_OK;
 }
 
@@ -539,7 +526,7 @@ int moe_lora_align(const moe_lora_dims *d, const int32_t *topk_ids, const int32_
     int32_t *tmp = (int32_t *)ws;
     int32_t *cnt = (int32_t *)(ws + round_up(sizeof(int32_t) * p.tmp_ints, 256));
     int r2 = launch_align(p, d, topk_ids, adapter_ids, sorted_ids, nullptr, block_expert, num_post_pad, lora_items,
-                          num_items ? num_items : cnt + 1, tmp, nullptr, nullptr, nullptr, st);
+                          num_items ? num_items : cnt + 1, tmp, nullptr, nullptr, st);
     if (r2 != MOE_LORA_OK) return r2;
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "align launch");
@@ -572,14 +559,13 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         if (ev) (void)hipEventRecord((hipEvent_t)ev[slot], st);
     };
     int32_t *tiles = (int32_t *)(ws + p.o_tiles);
-    const RouteParams rp = route_params(d, a->router_logits, ids, wts);
     mark(2 * MOE_LORA_STAGE_ROUTE);
-    if (!p.fuse_route) launch_route(d, a->router_logits, ids, wts, st);
+    launch_route(d, a->router_logits, ids, wts, st);
     mark(2 * MOE_LORA_STAGE_ROUTE + 1);
     mark(2 * MOE_LORA_STAGE_ALIGN);
     int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt, items,
                           cnt + 1, tmp,
-                          p.kind == 2 ? tiles : nullptr, cnt + 2, p.fuse_route ? &rp : nullptr, st);
+                          p.kind == 2 ? tiles : nullptr, cnt + 2, st);
     if (r2 != MOE_LORA_OK) return r2;
     // the tiled GEMM reads x gathered and packed per sorted row; with LoRA
     // the pack shares one launch with the gate_up shrink (stage SHRINK13)

@@ -160,6 +160,22 @@ def test_forward_small_parity(c):
         assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"
 
 
+def test_forward_multi_workgroup_alignment_all_tokens():
+    """8400 (token, slot) pairs: the multi-workgroup alignment, the x pack in
+    one launch with the gate_up shrink, equal-size token tiles and the LoRA
+    slab skipping of the tiled GEMMs, checked against the oracle on every
+    token (small H and I keep the oracle fast)."""
+    c = dict(T=2100, H=128, I=96, E=16, K=4, S=0, L=6, r=16, dtype="bf16", block_m=128)
+    shape = _shape(c)
+    inp = inputs(shape, synth.Recipe(adapters="zipf", none_frac=0.1), seed=21)
+    say("forward multi-wg align", c)
+    out = ml.forward_inputs(inp, **_kw(c))
+    torch.cuda.synchronize()
+    assert ml.moe_lora_plan_query(ml.make_dims(shape.T, shape.H, shape.I, shape.E, shape.K, shape.S, shape.L,
+                                               shape.r, block_m=128))["gemm_kind"] == 2
+    assert_close(out, oracle.forward_inputs(inp), shape.dtype, "multi-wg align forward")
+
+
 @pytest.mark.parametrize("logits,want_skewed", [("zipf_bias", True), ("normal", False)])
 def test_tiled_work_orders(logits, want_skewed):
     """The LDS-tiled GEMMs enumerate their work in one of two orders, chosen
