@@ -86,6 +86,8 @@ ALIGN_CASES = [
     # 80000 pairs: slices of 1280 pairs, so each scatter wave walks two windows
     dict(T=10000, E=64, K=8, S=0, L=16, r=16, adapters="zipf", logits="zipf_bias"),
     dict(T=3000, E=128, K=8, S=1, L=0, r=0),
+    # the largest router (1025 alignment experts x 9 adapter keys) in both forms
+    dict(T=40, E=1024, K=64, S=1, L=8, r=8), dict(T=200, E=1024, K=64, S=1, L=8, r=8),
 ]
 
 
@@ -237,6 +239,24 @@ def test_empty_and_single_token():
     out = ml.forward_inputs(inp)
     torch.cuda.synchronize()
     assert_close(out, oracle.forward_inputs(inp), synth.BF16, "T=1")
+
+
+@pytest.mark.parametrize("bm", [0, 128])
+def test_largest_router_sizes(bm):
+    """The plan's largest router: 1024 experts, top-64 plus a shared slot (65
+    slots per token), with LoRA (9225 alignment keys); routing bit for bit and
+    the layer against the oracle on every token."""
+    shape = synth.LayerShape(T=40, H=64, I=64, E=1024, K=64, S=1, L=8, r=8, rsf=2.5)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=3)
+    say("largest router", bm)
+    ids = torch.empty((shape.T, shape.Kp), dtype=torch.int32, device=DEV)
+    w = torch.empty((shape.T, shape.Kp), dtype=torch.float32, device=DEV)
+    out = ml.forward_inputs(inp, routing_out=(ids, w), block_m=bm)
+    torch.cuda.synchronize()
+    oids, ow = oracle.route(inp.logits.cpu().numpy(), shape.K, shape.S, shape.rsf)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.array_equal(_bits(w), ow.view(np.int32))
+    assert_close(out, oracle.forward_inputs(inp), synth.BF16, f"largest router bm={bm}")
 
 
 def test_all_tokens_one_expert():
