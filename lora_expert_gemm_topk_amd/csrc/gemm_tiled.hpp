@@ -26,10 +26,11 @@
 // (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16*l), so no
 // registers stage the data and kStages-1 slabs are in flight while the MFMAs
 // work on the oldest one.  One load instruction fills one 16-row group of a
-// stage: from a packed operand (the tokens) it copies one 1 KiB block, from a
-// row-major one (the weights) 16 rows x 64 bytes.  Each wave waits only for its own loads of the slab
-// it needs next (s_waitcnt vmcnt with the number of younger slabs still
-// allowed in flight) and then meets the others at one barrier per slab; the
+// stage: from a packed operand (the tokens, and the weights when packed) it
+// copies one 1 KiB block, from a row-major one 16 rows x 64 bytes.  Each wave
+// waits only for its own loads of the slab it needs next (s_waitcnt vmcnt
+// with the number of younger slabs still allowed in flight) and then meets
+// the others at one barrier per slab; the
 // wait and the barrier are one asm statement with a memory clobber, which
 // keeps the compiler from moving LDS accesses across the barrier without the
 // vmcnt(0) a fenced barrier would force.  K beyond the reduction length reads
@@ -42,16 +43,18 @@
 //
 // LoRA expand runs as extra K slabs of the same ring and MFMAs, one per
 // adapter present in the token tile and 32 rank columns (see `issue`), so it
-// costs a few slabs of the main loop's kind and no separate epilogue pass.
-// This needs, per sorted row, the adapter (written by the alignment) and the
-// shrink result in bf16 (written by an unsplit shrink).
+// costs a few slabs of the main loop's kind and no separate epilogue pass;
+// a wave runs a LoRA slab's MFMAs only on its column tiles that hold the
+// adapter's rows.  This needs, per sorted row, the adapter (written by the
+// alignment) and the shrink result in bf16 (written by an unsplit shrink).
 //
 // Workgroups are numbered so that each XCD (8 per MI355X, dispatched round
 // robin) receives one contiguous range of work in expert-major order (expert,
 // then weight tile, then the expert's token tiles): an XCD works through whole
 // experts, so an expert's gathered token rows stay in that XCD's L2 while all
 // of its weight tiles stream past, and the token tiles sharing a weight tile
-// run side by side.
+// run side by side.  When the load is skewed the work goes token-tile-major
+// in plain dispatch order instead (see the kernel).
 #pragma once
 
 #include <type_traits>

@@ -6,6 +6,10 @@
 // no allocation, grids sized for the worst case so nothing is read back):
 //   route -> align -> [shrink13] -> gate_up GEMM (+expand13, SwiGLU)
 //         -> [shrink2] -> down GEMM (+expand2) -> combine
+// The alignment is one launch below MOELORA_ALIGN_MULTI_MIN pairs and four
+// from there on.  With the LDS-tiled GEMMs (many rows per expert) x is also
+// gathered and packed per sorted row: in the shrink13 launch when the layer
+// has LoRA, else right after the alignment.
 // The LoRA shrink launches are skipped on the host when the layer has no
 // LoRA (L = 0 or r = 0), and on the device every shrink workgroup exits at
 // once when no token of the call carries an adapter (aitrends.kr summary of
