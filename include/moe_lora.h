@@ -94,7 +94,9 @@ extern "C" {
  *      16 or 32 (32 needs r <= 64)
  *   split_k  K-splits of the LoRA shrink; 0 = library choice, else 1..16.
  *      Applies to the streaming GEMM only: with the LDS-tiled GEMM the
- *      shrink runs unsplit (the plan reports 1)
+ *      shrink runs unsplit (the plan reports 1).  With 0 on the streaming
+ *      GEMM (and K+S <= 64, r <= 64) the gate_up shrink runs per pair inside
+ *      the router's launch and only the down shrink uses the split
  * Limits: (E+S) * (La+1) <= 16384 where La = L if LoRA is active else 0;
  *   L <= 1024; T*(K+S) < 2^31 - 1. */
 typedef struct moe_lora_dims {

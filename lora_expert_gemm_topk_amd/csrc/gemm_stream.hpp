@@ -41,11 +41,13 @@ struct GemmParams {
     const float *s_part;         // [split][cap][r] fp32; LDS-tiled kernel: bf16 [cap][r]
     void *out;                   // gate_up: h bf16 [cap, Nout] (LDS-tiled kernel: packed); down: y2 bf16 [P, Nout]
     int Kdim, Nout, Kp, P, cap, Ep, L, r, split, lora;
+    int s_by_pair = 0;           // streaming kernel: s_part is [P][r] by pair index (split 1)
 };
 
 // Add the LoRA expand term sum_k s[p,k] * B[a,e,row,k] to `v` for NC output
 // rows starting at `rows[c]` (rows[c] < 0: skipped).  s is the fixed-order sum
-// of the split-K partials.  r is a multiple of 8.
+// of the split-K partials; `prow` is the row of s (the sorted row, or the
+// pair index when s is kept by pair).  r is a multiple of 8.
 template <int NC>
 __device__ __forceinline__ void lora_expand_add(const GemmParams &p, int e, int a, int prow, const int *rows,
                                                 int rows_per_expert, float *v) {
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
                             rows[i] = col0 + i;
                             rows[4 + i] = N + col0 + i;
                         }
-                        lora_expand_add<8>(p, e, a, prow, rows, rows_per_expert, v);
+                        lora_expand_add<8>(p, e, a, p.s_by_pair ? f : prow, rows, rows_per_expert, v);
                     }
                 }
                 float hv[4];
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
                             rows[i] = col0 + i;
                             rows[4 + i] = N + col0 + i;
                         }
-                        lora_expand_add<8>(p, e, a, prow, rows, rows_per_expert, v);
+                        lora_expand_add<8>(p, e, a, p.s_by_pair ? f : prow, rows, rows_per_expert, v);
                     }
                 }
                 float hv[4];
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
                     int rows[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) rows[i] = col0 + i;
-                    lora_expand_add<4>(p, e, a, prow, rows, rows_per_expert, v);
+                    lora_expand_add<4>(p, e, a, p.s_by_pair ? f : prow, rows, rows_per_expert, v);
                 }
             }
             *reinterpret_cast<uint2 *>(yout + (int64_t)f * N + col0) =

@@ -48,6 +48,7 @@ thread_local char g_errbuf[320];
 
 struct Plan {
     int bm = 0, lbm = 0, split = 1, kind = 0, tile = 0;
+    bool row_shrink = false;  // streaming path: gate_up shrink per pair in the router launch
     int64_t P = 0, Ep = 0, Kp = 0, La = 0;
     int64_t max_blocks = 0, cap = 0, max_items = 0, max_tiles = 0;
     int align_nw = 16;
@@ -126,6 +127,10 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     // The tiled kernel streams the shrink result through its LDS ring as bf16
     // rows, so the shrink runs unsplit and rounds its fp32 sums there.
     if (!lora || p.kind == 2) p.split = 1;
+    // Unless a split is asked for, the streaming path runs the gate_up shrink
+    // per pair inside the router launch (it needs only the routing and the
+    // adapter ids; K+S <= 64).  The down shrink keeps the split-K items.
+    p.row_shrink = lora && p.kind == 1 && d->split_k == 0 && p.Kp <= 64 && d->r <= 64;
 
     const int64_t nz = std::min(p.Ep, p.P);
     p.max_blocks = (p.P + p.bm - 1) / p.bm + nz;
@@ -237,6 +242,37 @@ RouteParams route_params(const moe_lora_dims *d, const float *logits, int32_t *i
     rp.ids = ids;
     rp.wts = w;
     return rp;
+}
+
+template <int VPL>
+void launch_route_shrink_vpl(const RouteParams &rp, const RowShrinkParams &sp, hipStream_t st) {
+    const dim3 grid((unsigned)rp.T, (unsigned)(rp.K + rp.S)), block(256);
+    if (sp.r <= 16) hipLaunchKernelGGL((route_shrink_kernel<VPL, 16>), grid, block, 0, st, rp, sp);
+    else if (sp.r <= 32) hipLaunchKernelGGL((route_shrink_kernel<VPL, 32>), grid, block, 0, st, rp, sp);
+    else hipLaunchKernelGGL((route_shrink_kernel<VPL, 64>), grid, block, 0, st, rp, sp);
+}
+
+// Router and gate_up shrink in one launch (plan.row_shrink): s13 by pair.
+void launch_route_shrink(const Plan &pl, const moe_lora_dims *d, const moe_lora_args *a, int32_t *ids, float *w,
+                         float *s13, hipStream_t st) {
+    const RouteParams rp = route_params(d, a->router_logits, ids, w);
+    RowShrinkParams sp{};
+    sp.in = (const uint16_t *)a->hidden;
+    sp.A = (const uint16_t *)a->a13;
+    sp.adapter_ids = a->adapter_ids;
+    sp.s = s13;
+    sp.Kdim = (int)d->H;
+    sp.r = (int)d->r;
+    sp.Ep = (int)pl.Ep;
+    sp.Kp = (int)pl.Kp;
+    sp.P = (int)pl.P;
+    sp.L = (int)pl.La;
+    const int E = rp.E;
+    if (E <= 64) launch_route_shrink_vpl<1>(rp, sp, st);
+    else if (E <= 128) launch_route_shrink_vpl<2>(rp, sp, st);
+    else if (E <= 256) launch_route_shrink_vpl<4>(rp, sp, st);
+    else if (E <= 512) launch_route_shrink_vpl<8>(rp, sp, st);
+    else launch_route_shrink_vpl<16>(rp, sp, st);
 }
 
 int launch_route(const moe_lora_dims *d, const float *logits, int32_t *ids, float *w, hipStream_t st) {
@@ -564,7 +600,8 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     };
     int32_t *tiles = (int32_t *)(ws + p.o_tiles);
     mark(2 * MOE_LORA_STAGE_ROUTE);
-    launch_route(d, a->router_logits, ids, wts, st);
+    if (p.row_shrink) launch_route_shrink(p, d, a, ids, wts, s13, st);
+    else launch_route(d, a->router_logits, ids, wts, st);
     mark(2 * MOE_LORA_STAGE_ROUTE + 1);
     mark(2 * MOE_LORA_STAGE_ALIGN);
     int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt, items,
@@ -651,7 +688,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         sp.out_bf16 = p.kind == 2 ? 1 : 0;
         sp.in_packed = p.kind == 2 ? 1 : 0;  // the tiled GEMM keeps h packed
         mark(2 * MOE_LORA_STAGE_SHRINK13);
-        if (p.lora) {
+        if (p.lora && !p.row_shrink) {  // row_shrink: done in the router launch
             sp.in = (const uint16_t *)a->hidden;
             sp.A = (const uint16_t *)a->a13;
             sp.s_part = s13;
@@ -672,13 +709,14 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.Ep = (int)p.Ep;
         gp.r = r;
         gp.L = (int)p.La;
-        gp.split = p.split;
+        gp.split = p.row_shrink ? 1 : p.split;  // s13 by pair is unsplit
         gp.lora = p.lora ? 1 : 0;
         gp.in = (p.kind == 2) ? (const uint16_t *)(ws + p.o_xp) : (const uint16_t *)a->hidden;
         gp.W = (const uint16_t *)a->w13;
         mark(2 * MOE_LORA_STAGE_GATE_UP);
         gp.B = (const uint16_t *)a->b13;
         gp.s_part = s13;
+        gp.s_by_pair = p.row_shrink ? 1 : 0;
         gp.out = h;
         gp.Kdim = H;
         gp.Nout = I;
@@ -697,6 +735,8 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.W = (const uint16_t *)a->w2;
         gp.B = (const uint16_t *)a->b2;
         gp.s_part = s2;
+        gp.s_by_pair = 0;
+        gp.split = p.split;
         gp.out = y2;
         gp.Kdim = I;
         gp.Nout = H;

@@ -35,10 +35,10 @@ __device__ __forceinline__ bool better(const Cand &a, const Cand &b) {
 }
 
 // Route token t with the whole wavefront; writes ids and weights of its K+S
-// slots and returns to lane j the expert id of slot j (-1 for j >= K+S; slots
-// beyond lane 63 are written but not returned).
+// slots (unless `write` is false) and returns to lane j the expert id of
+// slot j (-1 for j >= K+S; slots beyond lane 63 are written but not returned).
 template <int VPL>
-__device__ int route_one_token(const RouteParams &rp, int t) {
+__device__ int route_one_token(const RouteParams &rp, int t, bool write = true) {
     const int lane = lane_id();
     const int E = rp.E, K = rp.K, S = rp.S;
     const float *l = rp.logits + (int64_t)t * E;
@@ -84,11 +84,11 @@ __device__ int route_one_token(const RouteParams &rp, int t) {
         for (int e = 0; e < E; ++e) sum += exp((double)l[e] - m);
     }
     const int Kp = K + S;
-    if (lane < K) {
+    if (write && lane < K) {
         rp.ids[(int64_t)t * Kp + lane] = myi;
         rp.wts[(int64_t)t * Kp + lane] = (float)(ex / sum);
     }
-    if (lane < S) {
+    if (write && lane < S) {
         rp.ids[(int64_t)t * Kp + K + lane] = E + lane;
         rp.wts[(int64_t)t * Kp + K + lane] = rp.shared_w;
     }

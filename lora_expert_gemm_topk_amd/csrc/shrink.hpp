@@ -20,6 +20,7 @@
 
 #include "common.hpp"
 #include "pack.hpp"
+#include "route.hpp"
 
 namespace moelora {
 
@@ -151,6 +152,108 @@ __global__ __launch_bounds__(256) void pack_x_shrink_kernel(PackXParams xp, Shri
     const int b = (int)blockIdx.x;
     if (b < n_items) shrink_item<NT, MT, true>(sp, b, 0);
     else pack_x_group(xp, b - n_items);
+}
+
+// ---------------------------------------------------------------------------
+// Per-row gate_up shrink for the streaming GEMM (few rows per expert, decode).
+//
+// With a handful of rows per (adapter, expert) bin the item shrink above is
+// latency bound, and it has to wait for the alignment.  The gate_up shrink
+// needs only the routing (the expert of each pair) and the token's adapter,
+// so it runs in the router's launch: workgroup (t, j) routes token t again
+// in its first wavefront (workgroup j = 0 writes the routing) and then
+// computes pair f = t*(K+S) + j's r sums, s13[f][k] = x[t] . A13[a,e][k],
+// stored by pair index.  The loads for the whole reduction are issued at
+// once: thread i takes the 16-byte chunks i and i + 256 (then i + 512, ...)
+// of every A row, so each load instruction of a wavefront reads 1 KiB
+// contiguously.  Each thread sums its chunks in order, each wavefront folds
+// its 64 lanes with a fixed butterfly and the 4 wavefront sums are added in
+// wave order: the result depends on nothing but the inputs.  A bin's slice
+// of A is read once per pair (the pairs of a bin share it in L2).
+struct RowShrinkParams {
+    const uint16_t *in;           // x [T, Kdim]
+    const uint16_t *A;            // A13 [L, Ep, r, Kdim]
+    const int32_t *adapter_ids;   // [T]
+    float *s;                     // s13 [P][r] fp32 by pair
+    int Kdim, r, Ep, Kp, P, L;
+};
+
+// s_out[k] = sum_c in[c] * A[k][c] for k < r (r <= RMAX), by the whole
+// workgroup of 256 threads; Kdim is a multiple of 8.
+template <int RMAX>
+__device__ __forceinline__ void shrink_row_wg(const uint16_t *__restrict__ in, const uint16_t *__restrict__ A,
+                                              int Kdim, int r, float *__restrict__ s_out) {
+    __shared__ float red[4][RMAX];
+    const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nch = Kdim >> 3;
+    float acc[RMAX];
+#pragma unroll
+    for (int k = 0; k < RMAX; ++k) acc[k] = 0.f;
+    // rows k >= r repeat row r-1 (their sums are never stored), so every
+    // load is in bounds and none is predicated
+    for (int c0 = tid; c0 < nch; c0 += 512) {
+        const int c1 = c0 + 256;
+        const bool has1 = c1 < nch;
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(in + (int64_t)c0 * 8);
+        const u32x4 x1 = ld16(in + (int64_t)c1 * 8, has1);
+#pragma unroll
+        for (int kb = 0; kb < RMAX; kb += 16) {
+            u32x4 a0[16], a1[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int64_t row = (int64_t)min(kb + q, r - 1) * Kdim;
+                a0[q] = *reinterpret_cast<const u32x4 *>(A + row + (int64_t)c0 * 8);
+                a1[q] = ld16(A + row + (int64_t)c1 * 8, has1);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                float v = acc[kb + q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v = fmaf(bf16_to_f32((uint16_t)(a0[q][i] & 0xffffu)), bf16_to_f32((uint16_t)(x0[i] & 0xffffu)), v);
+                    v = fmaf(bf16_to_f32((uint16_t)(a0[q][i] >> 16)), bf16_to_f32((uint16_t)(x0[i] >> 16)), v);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v = fmaf(bf16_to_f32((uint16_t)(a1[q][i] & 0xffffu)), bf16_to_f32((uint16_t)(x1[i] & 0xffffu)), v);
+                    v = fmaf(bf16_to_f32((uint16_t)(a1[q][i] >> 16)), bf16_to_f32((uint16_t)(x1[i] >> 16)), v);
+                }
+                acc[kb + q] = v;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < RMAX; ++k) {
+        float v = acc[k];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        acc[k] = v;
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < RMAX; ++k) red[w][k] = acc[k];
+    }
+    __syncthreads();
+    if (tid < r) s_out[tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+// Router + gate_up shrink: grid (T, K+S), K+S <= 64.
+template <int VPL, int RMAX>
+__global__ __launch_bounds__(256) void route_shrink_kernel(RouteParams rp, RowShrinkParams sp) {
+    const int t = (int)blockIdx.x, j = (int)blockIdx.y;
+    __shared__ int e_slot;
+    if (threadIdx.x < 64) {
+        const int myi = route_one_token<VPL>(rp, t, j == 0);
+        const int e = __shfl(myi, j, 64);
+        if (threadIdx.x == 0) e_slot = e;
+    }
+    const int a = sp.adapter_ids[t];
+    if (!(a >= 0 && a < sp.L)) return;  // the same for the whole workgroup; no barrier passed yet
+    __syncthreads();
+    const int e = e_slot;
+    const int64_t Kd = sp.Kdim;
+    shrink_row_wg<RMAX>(sp.in + (int64_t)t * Kd, sp.A + ((int64_t)a * sp.Ep + e) * sp.r * Kd, sp.Kdim, sp.r,
+                        sp.s + ((int64_t)t * sp.Kp + j) * sp.r);
 }
 
 }  // namespace moelora
