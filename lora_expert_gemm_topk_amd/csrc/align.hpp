@@ -554,4 +554,138 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
     align_body(p, lds);
 }
 
+// ---- small calls: one pass over the composite key ------------------------
+// For at most 1024 pairs and no GEMM token tiles (the streaming GEMM's
+// decode-sized calls) one workgroup with one thread per pair sorts by the
+// composite key (expert, adapter+1) in a single stable counting pass: the
+// pairs of wave w are f = 64w .. 64w+63, equal keys inside a wave are found
+// with bit-sliced ballots, and per-(wave, key) counts give each pair its
+// place.  Key offsets come from two block scans (over the keys, unpadded,
+// and over the experts, padded) instead of the two sorting passes and the
+// per-expert loops of the general form, and the padding, block map and LoRA
+// items are written by independent threads.  The layout is the same as the
+// general form's, bit for bit.
+__host__ __device__ inline int64_t align_small_lds_ints(int NW, int Ep, int La) {
+    const int64_t NK = (int64_t)Ep * (La + 1);
+    return (int64_t)NW * NK + 3 * (NK + 1) + 2 * (int64_t)Ep + 1 + 80;
+}
+
+__global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p) {
+    extern __shared__ int lds[];
+    const int nt = (int)blockDim.x, NW = nt >> 6;
+    const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int La = p.La, Ep = p.Ep, A1 = La + 1, NK = Ep * A1, P = p.P;
+    int *histW = lds;                 // [NW][NK] pairs of wave v with key k, then their prefix over waves
+    int *keyX = histW + NW * NK;      // [NK+1] pairs with a smaller key (exclusive scan of keyN)
+    int *keyN = keyX + NK + 1;        // [NK+1] pairs per key
+    int *itemOff = keyN + NK + 1;     // [NK+1] first LoRA item of each key
+    int *offE = itemOff + NK + 1;     // [Ep+1] padded start of each expert
+    int *totE = offE + Ep + 1;        // [Ep] pairs per expert
+    int *scr = totE + Ep;             // [80] scan scratch
+
+    for (int i = tid; i < NW * NK; i += nt) histW[i] = 0;
+    const int f = tid;
+    const bool valid = f < P;
+    int e = 0, a1 = 0;
+    if (valid) {
+        e = clamp_expert(p.topk_ids[f], Ep);
+        if (La > 0) a1 = adapter_key_of(p.adapter_ids[f / p.Kp], La);
+    }
+    const int key = e * A1 + a1;
+    __syncthreads();
+    const uint64_t m = match_key((uint32_t)key, valid, p.nbits_k);
+    const int rank = __popcll(m & lanemask_lt());
+    if (valid && rank == 0) histW[w * NK + key] = __popcll(m);
+    __syncthreads();
+    for (int k = tid; k < NK; k += nt) {
+        int run = 0;
+        for (int v = 0; v < NW; ++v) {
+            const int c = histW[v * NK + k];
+            histW[v * NK + k] = run;
+            run += c;
+        }
+        keyN[k] = run;
+        keyX[k] = run;
+    }
+    __syncthreads();
+    const int total = block_excl_scan(keyX, NK, scr);
+    if (tid == 0) keyX[NK] = total;
+    __syncthreads();
+    for (int x = tid; x < Ep; x += nt) {
+        const int c = keyX[(x + 1) * A1] - keyX[x * A1];
+        totE[x] = c;
+        offE[x] = (c + p.bm - 1) / p.bm * p.bm;
+    }
+    __syncthreads();
+    const int npp = block_excl_scan(offE, Ep, scr);
+    if (tid == 0) offE[Ep] = npp;
+    __syncthreads();
+
+    // scatter: expert start + keys of the expert before this one + earlier
+    // waves + earlier lanes
+    if (valid) {
+        const int pos = offE[e] + (keyX[key] - keyX[e * A1]) + histW[w * NK + key] + rank;
+        p.sorted_ids[pos] = f;
+        if (p.sorted_adapter) p.sorted_adapter[pos] = a1 - 1;
+    }
+    // the last expert e' with offE[e'] <= pos (empty experts share offsets)
+    auto expert_at = [&](int pos) {
+        int lo = 0, hi = Ep - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (offE[mid] <= pos) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
+    for (int q = tid; q < p.cap; q += nt) {
+        bool pad = q >= npp;
+        if (!pad) {
+            const int x = expert_at(q);
+            pad = q >= offE[x] + totE[x];
+        }
+        if (pad) {
+            p.sorted_ids[q] = P;
+            if (p.sorted_adapter) p.sorted_adapter[q] = -1;
+        }
+    }
+    for (int b = tid; b < p.max_blocks; b += nt) {
+        const int pos = b * p.bm;
+        p.block_expert[b] = pos < npp ? expert_at(pos) : -1;
+    }
+    int nitems = 0;
+    if (La > 0 && p.items != nullptr) {
+        for (int k = tid; k < NK; k += nt) itemOff[k] = (k % A1 == 0) ? 0 : (keyN[k] + p.lbm - 1) / p.lbm;
+        __syncthreads();
+        nitems = block_excl_scan(itemOff, NK, scr);
+        for (int k = tid; k < NK; k += nt) {
+            const int ka = k % A1, c = keyN[k];
+            if (ka == 0 || c == 0) continue;
+            const int x = k / A1;
+            const int start = offE[x] + (keyX[k] - keyX[x * A1]);
+            int it = itemOff[k];
+            for (int q = 0; q < c; q += p.lbm) {
+                int4 v;
+                v.x = start + q;
+                v.y = min(p.lbm, c - q);
+                v.z = ka - 1;
+                v.w = x;
+                reinterpret_cast<int4 *>(p.items)[it++] = v;
+            }
+        }
+        for (int q = nitems + tid; q < p.max_items; q += nt) {
+            int4 v;
+            v.x = 0;
+            v.y = 0;
+            v.z = -1;
+            v.w = -1;
+            reinterpret_cast<int4 *>(p.items)[q] = v;
+        }
+    }
+    if (tid == 0) {
+        *p.npp_out = npp;
+        *p.nitems_out = nitems;
+    }
+}
+
 }  // namespace moelora

@@ -55,6 +55,9 @@ struct Plan {
     size_t align_lds = 0;
     bool lds_keys = false;   // alignment keys staged in LDS
     bool multi = false;      // multi-workgroup alignment
+    bool small_align = false;  // one-pass alignment for small calls without GEMM token tiles
+    int align_small_nw = 4;
+    size_t align_small_lds = 0;
     int anb = 0, achunk = 0; // its blocks and pairs per block
     int64_t tmp_ints = 0;    // ints of alignment scratch
     bool lora = false;
@@ -173,6 +176,14 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     const int64_t NK = p.Ep * (p.La + 1);
     p.multi = p.P >= MOELORA_ALIGN_MULTI_MIN && NK * 4 <= kLdsBytes &&
               align_scan_lds_ints((int)p.Ep, (int)p.La) * 4 <= kLdsBytes;
+    // small calls without GEMM token tiles: one thread per pair, one pass
+    p.small_align = !p.multi && p.kind != 2 && p.P <= 1024;
+    if (p.small_align) {
+        p.align_small_nw = (int)std::max<int64_t>(4, (p.P + 63) / 64);
+        const int64_t ints = align_small_lds_ints(p.align_small_nw, (int)p.Ep, (int)p.La);
+        if (ints * 4 > 65536) p.small_align = false;
+        else p.align_small_lds = (size_t)ints * 4;
+    }
     p.tmp_ints = p.P;
     if (p.multi) {
         p.achunk = (int)std::max<int64_t>(256, ((p.P + 63) / 64 + 63) / 64 * 64);
@@ -333,6 +344,11 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
         hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024),
                            sizeof(int) * (size_t)align_scan_lds_ints((int)pl.Ep, (int)pl.La), st, ap);
         hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)pl.anb), dim3(256), klds, st, ap);
+        return MOE_LORA_OK;
+    }
+    if (pl.small_align && tiles == nullptr) {
+        hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3((unsigned)(pl.align_small_nw * 64)), pl.align_small_lds,
+                           st, ap);
         return MOE_LORA_OK;
     }
     const dim3 grid(1), block((unsigned)(pl.align_nw * 64));
