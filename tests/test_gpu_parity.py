@@ -88,6 +88,10 @@ ALIGN_CASES = [
     dict(T=3000, E=128, K=8, S=1, L=0, r=0),
     # the largest router (1025 alignment experts x 9 adapter keys) in both forms
     dict(T=40, E=1024, K=64, S=1, L=8, r=8), dict(T=200, E=1024, K=64, S=1, L=8, r=8),
+    # the one-pass form for small calls: at its limit (1024 pairs, 16 waves),
+    # one pair past it, and with 1024 composite keys
+    dict(T=128, E=40, K=8, S=0, L=6, r=8), dict(T=205, E=40, K=5, S=0, L=6, r=8),
+    dict(T=64, E=64, K=8, S=0, L=15, r=8),
 ]
 
 
@@ -127,6 +131,8 @@ SMALL = [
     dict(T=500, H=256, I=384, E=6, K=2, S=1, L=4, r=32, rsf=2.5, dtype="bf16", block_m=128),
     dict(T=260, H=192, I=96, E=3, K=2, S=0, L=2, r=16, dtype="bf16", block_m=256, split=2),
     dict(T=200, H=128, I=128, E=5, K=3, S=0, L=0, r=0, dtype="bf16", block_m=128),
+    # 64 slots per token: the most the router launch takes the gate_up shrink for
+    dict(T=8, H=64, I=64, E=100, K=63, S=1, L=3, r=8, rsf=2.0, dtype="bf16"),
 ]
 
 
