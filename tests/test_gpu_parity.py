@@ -349,3 +349,32 @@ def test_shared_fused_equals_unfused_on_gpu():
     unfused = routed.double() + shared.double()
     maxabs, rel = errs(unfused, ref)
     assert maxabs <= 2 * 2e-2 and rel <= 1e-2, (maxabs, rel)
+
+
+@pytest.mark.parametrize("block_m", [32, 128])
+def test_separate_gate_up_slices_as_rank_2r(block_m):
+    """A LoRA given as separate gate and up slices runs as the single-adapter
+    form of rank 2r: A13 = [A_g; A_u] and a block-diagonal B13 (the oracle
+    pins this equivalence on the CPU).  Both GEMM kinds against the oracle,
+    and the LoRA delta on its own."""
+    from dataclasses import replace
+    shape = synth.LayerShape(T=160, H=192, I=128, E=6, K=2, L=3, r=16)   # rank 2r = 16
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=11)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    L, Ep, r, H, I = shape.L, shape.Ep, shape.r // 2, shape.H, shape.I
+    nrm = lambda *s, std: (torch.randn(s, generator=g, device=DEV) * std).to(torch.bfloat16)
+    Ag, Au = nrm(L, Ep, r, H, std=H ** -0.5), nrm(L, Ep, r, H, std=H ** -0.5)
+    Bg, Bu = nrm(L, Ep, I, r, std=0.02), nrm(L, Ep, I, r, std=0.02)
+    a13 = torch.cat([Ag, Au], dim=2).contiguous()
+    b13 = torch.zeros((L, Ep, 2 * I, 2 * r), dtype=torch.bfloat16, device=DEV)
+    b13[:, :, :I, :r] = Bg
+    b13[:, :, I:, r:] = Bu
+    inp = replace(inp, a13=a13, b13=b13.contiguous())
+    say("separate gate/up slices", block_m)
+    out = ml.forward_inputs(inp, block_m=block_m)
+    base = ml.forward_inputs(inp, lora=False, block_m=block_m)
+    torch.cuda.synchronize()
+    ref = oracle.forward_inputs(inp)
+    assert_close(out, ref, synth.BF16, "separate gate/up slices")
+    _, rel = errs(out.double() - base.double(), ref - oracle.forward_inputs(inp, lora=False))
+    assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"

@@ -156,3 +156,37 @@ def test_oracle_rejects_bad_adapter():
     inp.adapter_ids[1] = 7
     with pytest.raises(ValueError):
         oracle.forward_inputs(inp)
+
+
+def test_separate_gate_up_lora_as_rank_2r():
+    """A LoRA with separate gate and up slices (A_g, B_g on rows [0, I), A_u,
+    B_u on rows [I, 2I)) is the single-adapter form of rank 2r with
+    A13 = [A_g; A_u] and the block-diagonal B13 = [[B_g, 0], [0, B_u]]: every
+    token on one adapter, the oracle with those stacks equals the base MoE
+    with the gate and up weights merged slice by slice."""
+    rng = np.random.default_rng(7)
+    inp = _small(T=8, H=20, I=16, E=4, K=2, L=2, r=3)
+    s = inp.shape
+    L, Ep, r, H, I = s.L, s.Ep, s.r, s.H, s.I
+    Ag, Au = rng.normal(0, 0.3, (L, Ep, r, H)), rng.normal(0, 0.3, (L, Ep, r, H))
+    Bg, Bu = rng.normal(0, 0.1, (L, Ep, I, r)), rng.normal(0, 0.1, (L, Ep, I, r))
+    a13 = np.concatenate([Ag, Au], axis=2)
+    b13 = np.zeros((L, Ep, 2 * I, 2 * r))
+    b13[:, :, :I, :r] = Bg
+    b13[:, :, I:, r:] = Bu
+    # A2/B2 of rank 2r as well (one rank for both projections)
+    a2 = rng.normal(0, 0.3, (L, Ep, 2 * r, I))
+    b2 = rng.normal(0, 0.1, (L, Ep, H, 2 * r))
+    t32 = lambda a: torch.from_numpy(a.astype(np.float32))
+    a13, b13, a2, b2 = t32(a13), t32(b13), t32(a2), t32(b2)
+    ad = 1
+    inp.adapter_ids[:] = ad
+    out = oracle.forward(inp.x, inp.logits, inp.adapter_ids, inp.w13, inp.w2, a13, b13, a2, b2, K=s.K)
+    f = bf.to_f64
+    W13m = f(inp.w13).copy()
+    W13m[:, :I] += np.einsum("eik,ekh->eih", f(t32(Bg.astype(np.float32)))[ad], f(t32(Ag.astype(np.float32)))[ad])
+    W13m[:, I:] += np.einsum("eik,ekh->eih", f(t32(Bu.astype(np.float32)))[ad], f(t32(Au.astype(np.float32)))[ad])
+    W2m = f(inp.w2) + np.einsum("enk,eki->eni", f(b2[ad]), f(a2[ad]))
+    ids, w = bf.route(inp.logits.numpy(), s.K)
+    ref = bf.layer_dense(inp.x, W13m, W2m, bf.gate_matrix(ids, w, s.Ep), rsf=s.rsf)
+    assert _rel(out, ref) < 1e-12
