@@ -79,4 +79,12 @@ __host__ __device__ __forceinline__ int64_t packed_off(int64_t row, int64_t k, i
     return ((row >> 4) * nslab + (k >> 5)) * kBlockElems + ((k >> 3) & 3) * 128 + (row & 15) * 8 + (k & 7);
 }
 
+// Map workgroup i (dispatched to XCD i % 8) to a logical index such that each
+// XCD owns one contiguous range of logical indices.  Bijective on [0, total).
+__device__ __forceinline__ int xcd_logical(int i, int total) {
+    const int q = total / 8, rem = total % 8;
+    const int x = i % 8, k = i / 8;
+    return (x < rem) ? x * (q + 1) + k : rem * (q + 1) + (x - rem) * q + k;
+}
+
 }  // namespace moelora

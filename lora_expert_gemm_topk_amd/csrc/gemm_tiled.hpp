@@ -86,14 +86,6 @@ __device__ __forceinline__ void static_for(F &&f) {
 // 16 bytes of zeros: the source of every load past the end of K
 __device__ __attribute__((aligned(16))) const uint16_t g_zero_chunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
-// Map workgroup i (dispatched to XCD i % 8) to a logical index such that each
-// XCD owns one contiguous range of logical indices.  Bijective on [0, total).
-__device__ __forceinline__ int xcd_logical(int i, int total) {
-    const int q = total / 8, rem = total % 8;
-    const int x = i % 8, k = i / 8;
-    return (x < rem) ? x * (q + 1) + k : rem * (q + 1) + (x - rem) * q + k;
-}
-
 // global row of tile row rr for gate_up (interleaved gate/up pairs) or down
 template <bool GU>
 __device__ __forceinline__ int tile_weight_row(int rr, int i0, int N, bool &ok) {

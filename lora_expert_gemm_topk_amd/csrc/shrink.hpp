@@ -137,9 +137,20 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams &p, int item, int
     }
 }
 
+// The items of one (adapter, expert) bin are consecutive in the item list;
+// with an unsplit shrink each XCD takes one contiguous range of items, so a
+// bin's A slice is fetched into one XCD's L2 and its other items hit there.
+__device__ __forceinline__ int shrink_item_of(int b, int n_items) { return xcd_logical(b, n_items); }
+
 template <int NT, int MT, bool GATHER>
 __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
-    shrink_item<NT, MT, GATHER>(p, (int)blockIdx.x, (int)blockIdx.y);
+    int item = (int)blockIdx.x;
+    if (gridDim.y == 1) {
+        const int n = p.counters[1];
+        if (item >= n) return;
+        item = shrink_item_of(item, n);
+    }
+    shrink_item<NT, MT, GATHER>(p, item, (int)blockIdx.y);
 }
 
 // The gate_up shrink (unsplit, x gathered) and the gather-and-pack of x for
@@ -150,8 +161,12 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkParams p) {
 template <int NT, int MT>
 __global__ __launch_bounds__(256) void pack_x_shrink_kernel(PackXParams xp, ShrinkParams sp, int n_items) {
     const int b = (int)blockIdx.x;
-    if (b < n_items) shrink_item<NT, MT, true>(sp, b, 0);
-    else pack_x_group(xp, b - n_items);
+    if (b < n_items) {
+        const int n = sp.counters[1];
+        if (b < n) shrink_item<NT, MT, true>(sp, shrink_item_of(b, n), 0);
+    } else {
+        pack_x_group(xp, b - n_items);
+    }
 }
 
 // ---------------------------------------------------------------------------
