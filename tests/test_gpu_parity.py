@@ -92,6 +92,9 @@ ALIGN_CASES = [
     # one pair past it, and with 1024 composite keys
     dict(T=128, E=40, K=8, S=0, L=6, r=8), dict(T=205, E=40, K=5, S=0, L=6, r=8),
     dict(T=64, E=64, K=8, S=0, L=15, r=8),
+    # a few pairs over many mostly empty experts, and a key count whose LDS
+    # need just exceeds what the one-pass form takes
+    dict(T=16, E=1024, K=4, S=0, L=0, r=0), dict(T=12, E=700, K=3, S=1, L=2, r=8),
 ]
 
 
