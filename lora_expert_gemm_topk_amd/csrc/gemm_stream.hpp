@@ -42,6 +42,7 @@ struct GemmParams {
     void *out;                   // gate_up: h bf16 [cap, Nout] (LDS-tiled kernel: packed); down: y2 bf16 [P, Nout]
     int Kdim, Nout, Kp, P, cap, Ep, L, r, split, lora;
     int s_by_pair = 0;           // streaming kernel: s_part is [P][r] by pair index (split 1)
+    const uint8_t *Wscale = nullptr;  // MXFP8 weights: E8M0 scale of each 32-element block, [rows][Kdim/32]
 };
 
 // Add the LoRA expand term sum_k s[p,k] * B[a,e,row,k] to `v` for NC output
@@ -80,8 +81,18 @@ __device__ __forceinline__ void lora_expand_add(const GemmParams &p, int e, int 
 // WP: weights in the packed layout of moe_lora_pack_weights.  A weight
 // fragment is then one 16-row group (for gate_up the gate and up rows of 8
 // features, in quads gate f, gate f+1, up f, up f+1), read 1 KiB-contiguous.
-template <int BW, int BT, bool GU, bool WP>
+//
+// MX: MXFP8 weights (row-major like the bf16 ones): one byte per element, an
+// FP8 E4M3 code, and one E8M0 scale byte per 32-element block along K; the
+// element is code * 2^(scale - 127).  The reduction then runs in 128-wide
+// chunks: lane (row, g) loads the 32 codes of block 4c + g (whole 128-byte
+// row segments per 4 lanes) and its scale, converts them with the hardware's
+// scaled FP8 -> bf16 conversion (exact: E4M3 has 3 mantissa bits) and feeds
+// the same bf16 MFMAs; the matching 32 activations are that lane's 64 bytes
+// of x.  Weight bytes per layer call halve.
+template <int BW, int BT, bool GU, bool WP, bool MX = false>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
+    static_assert(!(MX && WP), "MXFP8 weights are read row-major");
     constexpr int MS = BW / 16, NS = BT / 16;
     constexpr int LDW = BW + 4;
     __shared__ float buf[2][BT][LDW];
@@ -124,6 +135,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
         wrow[ms] = p.W + ((int64_t)e * rows_per_expert + (wok[ms] ? grow : 0)) * Kd;
     }
     }
+    // MXFP8: the same rows as byte rows, and their scale rows
+    const uint8_t *wrow8[MS], *srow[MS];
+    if constexpr (MX) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+            const int64_t row = (wrow[ms] - p.W) / Kd;  // e * rows_per_expert + row within the expert
+            wrow8[ms] = reinterpret_cast<const uint8_t *>(p.W) + row * Kd;
+            srow[ms] = p.Wscale + row * (Kd / 32);
+        }
+    }
     const uint16_t *xrow[NS];
     bool xok[NS];
 #pragma unroll
@@ -142,9 +163,51 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nch = (int)((Kd + 63) / 64);
-    u32x4 wa[2][MS][2], xa[2][NS][2];
+    constexpr int XQ = MX ? 4 : 2;        // 16-byte x loads per lane and chunk
+    constexpr int KC = MX ? 128 : 64;     // reduction per chunk
+    const int nch = (int)((Kd + KC - 1) / KC);
+    u32x4 wa[2][MS][2], xa[2][NS][XQ];
+    uint32_t sa[2][MS];
+    auto load_mx = [&](int buf_i, int c) {
+        const int64_t k0 = (int64_t)c * 128 + g * 32;  // block 4c + g (K is a multiple of 32)
+        const bool kin = k0 < Kd;
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+            const bool ok = wok[ms] && kin;
+            wa[buf_i][ms][0] = ld16(wrow8[ms] + k0, ok);
+            wa[buf_i][ms][1] = ld16(wrow8[ms] + k0 + 16, ok);
+            sa[buf_i][ms] = ok ? (uint32_t)srow[ms][k0 >> 5] : 127u;
+        }
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+            for (int q = 0; q < XQ; ++q) xa[buf_i][ns][q] = ld16(xrow[ns] + k0 + 8 * q, xok[ns] && kin);
+    };
+    auto compute_mx = [&](int buf_i) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+            const float sc = __uint_as_float(sa[buf_i][ms] << 23);  // 2^(scale - 127)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                // codes 8s .. 8s+7 of the lane's 32: dwords 2s and 2s+1
+                const uint32_t d0 = wa[buf_i][ms][s >> 1][2 * (s & 1)], d1 = wa[buf_i][ms][s >> 1][2 * (s & 1) + 1];
+                u32x4 wb;
+                wb[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, false));
+                wb[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, true));
+                wb[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, false));
+                wb[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, true));
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wb), as_bf16x8(xa[buf_i][ns][s]),
+                                                                          acc[ms][ns], 0, 0, 0);
+            }
+        }
+    };
     auto load = [&](int buf_i, int c) {
+        if constexpr (MX) {
+            load_mx(buf_i, c);
+            return;
+        }
         const int64_t k0 = (int64_t)c * 64 + g * 16;
         const bool k_lo = k0 < Kd, k_hi = k0 + 8 < Kd;
 #pragma unroll
@@ -167,6 +230,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
         }
     };
     auto compute = [&](int buf_i) {
+        if constexpr (MX) {
+            compute_mx(buf_i);
+            return;
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll

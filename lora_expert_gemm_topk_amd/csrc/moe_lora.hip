@@ -447,6 +447,14 @@ void launch_gemm_wp(const Plan &pl, const GemmParams &gp, const int32_t *tiles, 
 template <bool GU>
 void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles, bool wp,
                  hipStream_t st) {
+    if (gp.Wscale != nullptr) {
+        // MXFP8 weights: the streaming kernel only (checked by moe_lora_check_args)
+        const int tile = GU ? kStreamBW / 2 : kStreamBW;
+        const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
+        if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, false, true>), grid, block, 0, st, gp);
+        else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, false, true>), grid, block, 0, st, gp);
+        return;
+    }
     if (wp) launch_gemm_wp<GU, true>(pl, gp, tiles, ntiles, st);
     else launch_gemm_wp<GU, false>(pl, gp, tiles, ntiles, st);
 }
@@ -498,6 +506,12 @@ int moe_lora_check_args(const moe_lora_dims *d, const moe_lora_args *a) {
     if (a->workspace_bytes < p.total) return MOE_LORA_EWORKSPACE;
     if (a->weights_packed != 0 && a->weights_packed != 1) return MOE_LORA_EINVAL;
     if (a->weights_packed && d->dtype != MOE_LORA_BF16) return MOE_LORA_EUNSUPPORTED;
+    if (a->weights_mxfp8 != 0 && a->weights_mxfp8 != 1) return MOE_LORA_EINVAL;
+    if (a->weights_mxfp8) {
+        if (!a->w13_scale || !a->w2_scale) return MOE_LORA_EINVAL;
+        if (d->dtype != MOE_LORA_BF16 || a->weights_packed || d->H % 32 != 0 || d->I % 32 != 0 || p.kind != 1)
+            return MOE_LORA_EUNSUPPORTED;
+    }
     return MOE_LORA_OK;
 }
 
@@ -729,6 +743,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.lora = p.lora ? 1 : 0;
         gp.in = (p.kind == 2) ? (const uint16_t *)(ws + p.o_xp) : (const uint16_t *)a->hidden;
         gp.W = (const uint16_t *)a->w13;
+        gp.Wscale = a->weights_mxfp8 ? (const uint8_t *)a->w13_scale : nullptr;
         mark(2 * MOE_LORA_STAGE_GATE_UP);
         gp.B = (const uint16_t *)a->b13;
         gp.s_part = s13;
@@ -749,6 +764,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         mark(2 * MOE_LORA_STAGE_SHRINK2 + 1);
         gp.in = (const uint16_t *)h;
         gp.W = (const uint16_t *)a->w2;
+        gp.Wscale = a->weights_mxfp8 ? (const uint8_t *)a->w2_scale : nullptr;
         gp.B = (const uint16_t *)a->b2;
         gp.s_part = s2;
         gp.s_by_pair = 0;

@@ -52,7 +52,8 @@ class MoeLoraArgs(ctypes.Structure):
                 ("b2", ctypes.c_void_p), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("topk_ids_out", ctypes.c_void_p),
                 ("topk_weights_out", ctypes.c_void_p), ("stage_events", ctypes.c_void_p),
-                ("weights_packed", ctypes.c_int32)]
+                ("weights_packed", ctypes.c_int32), ("weights_mxfp8", ctypes.c_int32),
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
 
 
 class MoeLoraError(RuntimeError):
@@ -231,6 +232,26 @@ class Workspace:
         return self.buf
 
 
+class Mxfp8Weights:
+    """MXFP8 expert weights for moe_lora_forward (moe_lora_args.weights_mxfp8):
+    FP8 E4M3 codes w13 [E+S,2I,H] and w2 [E+S,H,I] (uint8) with one E8M0
+    scale byte per 32 elements along the reduction, w13_scale [E+S,2I,H/32]
+    and w2_scale [E+S,H,I/32] (uint8).  Pass it as w13 with w2=None."""
+
+    def __init__(self, w13: torch.Tensor, w13_scale: torch.Tensor, w2: torch.Tensor, w2_scale: torch.Tensor):
+        for name, t in (("w13", w13), ("w13_scale", w13_scale), ("w2", w2), ("w2_scale", w2_scale)):
+            _dev_tensor(t, name, torch.uint8)
+        Ep, twoI, H = w13.shape
+        I = twoI // 2
+        if tuple(w2.shape) != (Ep, H, I) or tuple(w13_scale.shape) != (Ep, twoI, H // 32) or \
+                tuple(w2_scale.shape) != (Ep, H, I // 32) or H % 32 or I % 32:
+            raise ValueError("MXFP8 weights: w13 [E',2I,H], w13_scale [E',2I,H/32], w2 [E',H,I], "
+                             "w2_scale [E',H,I/32] with H and I multiples of 32")
+        self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
+        self.Ep, self.I, self.H = Ep, I, H
+        self.device = w13.device
+
+
 def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optional[torch.Tensor],
                      w13: torch.Tensor, w2: torch.Tensor, a13=None, b13=None, a2=None, b2=None, *,
                      K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1,
@@ -249,21 +270,22 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     stage on the launch stream."""
     dt = x.dtype
     packed = isinstance(w13, PackedWeights)
-    if packed:
+    mx = isinstance(w13, Mxfp8Weights)
+    if packed or mx:
         if w2 is not None:
-            raise ValueError("with PackedWeights as w13, pass w2=None")
+            raise ValueError("with PackedWeights or Mxfp8Weights as w13, pass w2=None")
         if w13.device != x.device:
-            raise ValueError("packed weights live on another device")
+            raise ValueError("the weights live on another device")
         Ep, I = w13.Ep, w13.I
     for name, t in (("x", x), ("a13", a13), ("b13", b13), ("a2", a2), ("b2", b2)) + \
-            (() if packed else (("w13", w13), ("w2", w2))):
+            (() if packed or mx else (("w13", w13), ("w2", w2))):
         _dev_tensor(t, name, dt)
     _dev_tensor(logits, "logits", torch.float32)
     _dev_tensor(adapter_ids, "adapter_ids", torch.int32)
     T, H = x.shape
-    if packed and w13.H != H:
-        raise ValueError(f"packed weights are for H={w13.H}, x has H={H}")
-    if not packed:
+    if (packed or mx) and w13.H != H:
+        raise ValueError(f"the weights are for H={w13.H}, x has H={H}")
+    if not (packed or mx):
         Ep, twoI, _ = w13.shape
         I = twoI // 2
     E = logits.shape[1]
@@ -275,7 +297,7 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     nbytes = moe_lora_workspace_bytes(dims)
     ws = (workspace or Workspace()).get(nbytes, x.device)
     ids_out, w_out = routing_out if routing_out is not None else (None, None)
-    w13_ptr, w2_ptr = (w13.w13.data_ptr(), w13.w2.data_ptr()) if packed else (w13.data_ptr(), w2.data_ptr())
+    w13_ptr, w2_ptr = (w13.w13.data_ptr(), w13.w2.data_ptr()) if packed or mx else (w13.data_ptr(), w2.data_ptr())
     args = MoeLoraArgs(x.data_ptr(), logits.data_ptr(), adapter_ids.data_ptr() if adapter_ids is not None else None,
                        w13_ptr, w2_ptr,
                        *(t.data_ptr() if t is not None else None for t in (a13, b13, a2, b2)),
@@ -283,7 +305,8 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
                        ids_out.data_ptr() if ids_out is not None else None,
                        w_out.data_ptr() if w_out is not None else None,
                        ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None,
-                       1 if packed else 0)
+                       1 if packed else 0, 1 if mx else 0,
+                       w13.w13_scale.data_ptr() if mx else None, w13.w2_scale.data_ptr() if mx else None)
     with torch.cuda.device(x.device):
         rc = lib().moe_lora_forward(ctypes.byref(dims), ctypes.byref(args), _stream(x.device))
     if rc != MOE_LORA_OK:
@@ -291,9 +314,10 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     return out
 
 
-def forward_inputs(inp, *, lora: bool = True, packed: Optional[PackedWeights] = None, **kw) -> torch.Tensor:
+def forward_inputs(inp, *, lora: bool = True, packed=None, **kw) -> torch.Tensor:
     """moe_lora_forward over a synth.LayerInputs bundle already on the GPU
-    (with `packed`, the packed copies of its w13 and w2 are read instead)."""
+    (with `packed`, a PackedWeights or Mxfp8Weights, those weights are read
+    instead of its w13 and w2)."""
     s = inp.shape
     use = lora and s.lora
     w13, w2 = (packed, None) if packed is not None else (inp.w13, inp.w2)

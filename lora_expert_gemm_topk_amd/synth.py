@@ -202,6 +202,28 @@ def make_inputs(shape: LayerShape, recipe: Recipe = Recipe(), seed: int = 0,
                        a13, b13, a2, b2, extra)
 
 
+def mxfp8_quantize(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Expert weights as MXFP8 inputs: blocks of 32 consecutive elements of
+    the last axis share one E8M0 scale byte s, chosen as the smallest power
+    of two 2^(s-127) with max|block| / 2^(s-127) <= 448 (the largest E4M3
+    value), and every element becomes the E4M3 code of w / 2^(s-127)
+    (torch's float8_e4m3fn rounding).  Returns (codes, scales) as uint8
+    tensors on w's device, shapes [..., K] and [..., K/32].  This prepares
+    inputs; the layer itself only ever decodes them."""
+    K = w.shape[-1]
+    if K % 32:
+        raise ValueError("the last axis must be a multiple of 32")
+    wb = w.float().reshape(*w.shape[:-1], K // 32, 32)
+    amax = wb.abs().amax(dim=-1)
+    e = torch.ceil(torch.log2(torch.clamp(amax, min=1e-30) / 448.0))
+    e = torch.where(amax / torch.exp2(e) > 448.0, e + 1, e)  # guard log2 rounding
+    e = torch.clamp(e, -126, 127)
+    q = (wb / torch.exp2(e).unsqueeze(-1)).to(torch.float8_e4m3fn)
+    codes = q.view(torch.uint8).reshape(w.shape).contiguous()
+    scales = (e + 127).to(torch.uint8).contiguous()
+    return codes, scales
+
+
 # ---------------------------------------------------------------------------
 # Named workloads.  Sizes are the ones the layer is measured and checked on.
 # ---------------------------------------------------------------------------

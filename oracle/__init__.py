@@ -65,6 +65,8 @@ def _load():
     lib.oracle_forward.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, f32, i32, i32,
                                    vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i32]
     lib.oracle_forward.restype = i32
+    lib.oracle_mxfp8_decode.argtypes = [i64, i64, vp, vp, vp]
+    lib.oracle_mxfp8_decode.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -195,3 +197,30 @@ def forward_inputs(inp, tokens=None, lora: bool = True, nthreads: int = 0):
                    inp.a2 if use else None, inp.b2 if use else None,
                    K=s.K, S=s.S, rsf=s.rsf, renormalize=s.renormalize, tokens=tokens,
                    nthreads=nthreads)
+
+
+def mxfp8_decode(codes, scales) -> np.ndarray:
+    """MXFP8 weights -> fp64 (same shape as `codes`): FP8 E4M3 codes times
+    2^(scale - 127), one E8M0 scale byte per 32 elements of the last axis."""
+    c = _np(codes, np.uint8)
+    sc = _np(scales, np.uint8)
+    K = c.shape[-1]
+    rows = c.size // K
+    if K % 32 or sc.shape[-1] != K // 32 or sc.size != rows * (K // 32):
+        raise ValueError("scales must hold one byte per 32 elements of the last axis")
+    out = np.empty(c.shape, np.float64)
+    rc = _load().oracle_mxfp8_decode(rows, K, _ptr(c), _ptr(sc), _ptr(out))
+    if rc != 0:
+        raise ValueError("MXFP8 decode: NaN code or scale byte outside [1, 254]")
+    return out
+
+
+def mxfp8_to_bf16(codes, scales):
+    """mxfp8_decode rounded to bf16, checked to be exact (E4M3 has three
+    mantissa bits, so every decoded weight of a normal range is a bf16)."""
+    import torch
+    v = mxfp8_decode(codes, scales)
+    t = torch.from_numpy(v).to(torch.bfloat16)
+    if not np.array_equal(t.to(torch.float64).numpy(), v):
+        raise ValueError("MXFP8 weights outside the exact bf16 range")
+    return t

@@ -32,6 +32,16 @@
  *          and expand (B) sit on both the gate_up and the down projection
  *          (AWS post summary, "image analysis", diagram).
  *
+ *  mxfp8   decode of MXFP8 expert weights (the experts module of the ROCm
+ *          path in the PR 46545 analysis, "code analysis" part 2, is the
+ *          mxfp8 one; the pages do not define the format, and the reading
+ *          taken is the MX one): every element is an FP8 E4M3 code (sign,
+ *          4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+ *          subnormal, exponent 15 with mantissa 7 is NaN, no infinities)
+ *          times 2^(s - 127) for the E8M0 scale byte s of its block of 32
+ *          consecutive elements along the reduction.  The layer forward then
+ *          runs on the decoded weights unchanged.
+ *
  * Floating point inputs arrive either as fp32 or as raw bf16 bit patterns
  * (uint16); both are widened exactly to fp64 before use.
  */
@@ -401,4 +411,39 @@ int oracle_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* One FP8 E4M3 code as a double; NaN for the two NaN codes. */
+static double e4m3_value(uint8_t b)
+{
+    const int sign = b >> 7, ex = (b >> 3) & 15, man = b & 7;
+    double v;
+    if (ex == 15 && man == 7)
+        return NAN;
+    if (ex == 0)
+        v = ldexp((double)man, -9);              /* (man / 8) * 2^(1 - 7) */
+    else
+        v = ldexp(8.0 + (double)man, ex - 10);   /* (1 + man / 8) * 2^(ex - 7) */
+    return sign ? -v : v;
+}
+
+/* MXFP8 rows -> fp64: out[r][k] = e4m3(codes[r][k]) * 2^(scales[r][k/32] - 127).
+ * K must be a multiple of 32.  Returns -1 for a NaN code or a scale byte
+ * outside [1, 254] (NaN scale 255; 0 is left out as the layer's
+ * precondition), else 0. */
+int oracle_mxfp8_decode(int64_t rows, int64_t K, const uint8_t *codes, const uint8_t *scales, double *out)
+{
+    int64_t r, k;
+    if (K % 32 != 0)
+        return -1;
+    for (r = 0; r < rows; ++r) {
+        for (k = 0; k < K; ++k) {
+            const uint8_t s = scales[r * (K / 32) + k / 32];
+            const double v = e4m3_value(codes[r * K + k]);
+            if (s == 0 || s == 255 || isnan(v))
+                return -1;
+            out[r * K + k] = ldexp(v, (int)s - 127);
+        }
+    }
+    return 0;
 }

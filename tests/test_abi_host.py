@@ -132,6 +132,25 @@ def test_check_args_weights_packed_flag():
     assert ml.moe_lora_check_args(_dims(dtype="f32"), _args(weights_packed=1)) == ml.MOE_LORA_EUNSUPPORTED
 
 
+def test_check_args_mxfp8_flag():
+    d = _dims()                                   # decode shape: streaming GEMM, H = I = 2880
+    sc = dict(w13_scale=0xb000, w2_scale=0xc000)
+    assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_OK
+    assert ml.moe_lora_check_args(d, _args(weights_mxfp8=2, **sc)) == ml.MOE_LORA_EINVAL
+    assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, w13_scale=0xb000)) == ml.MOE_LORA_EINVAL
+    # bf16 only, not with packed weights, H and I multiples of 32, streaming GEMM only
+    assert ml.moe_lora_check_args(_dims(dtype="f32"), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
+    assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, weights_packed=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
+    assert ml.moe_lora_check_args(_dims(H=2888), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
+    assert ml.moe_lora_check_args(_dims(I=2888), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
+    big = _dims(T=4096, L=32, r=32)
+    assert ml.moe_lora_plan_query(big)["gemm_kind"] == 2
+    assert ml.moe_lora_check_args(big, _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
+    assert ml.moe_lora_check_args(_dims(T=4096, L=32, r=32, block_m=32), _args(weights_mxfp8=1, **sc)) == 0
+    # the flag off ignores the scale pointers
+    assert ml.moe_lora_check_args(d, _args()) == ml.MOE_LORA_OK
+
+
 def test_packed_weight_bytes_formula():
     # w13: E+S experts x 16*ceil(I/128) groups x ceil(H/32) slabs x 1 KiB;
     # w2: E+S experts x 16*ceil(H/256) groups x ceil(I/32) slabs x 1 KiB
