@@ -8,7 +8,10 @@ line.  The default workload is the GPT-OSS-20B-shaped decode layer
 without LoRA); the prefill layer (T=4096, 32 adapters of rank 32) is measured
 beside it and reported under "prefill".  Expert weights are packed once with
 moe_lora_pack_weights before timing (as a model would at load time);
---row-major times the row-major weights instead.
+--row-major times the row-major weights instead.  Reported beside them
+(never as the headline value): the tiny fp32 layer, the shared-expert
+fusion sweep against its unfused comparator, the heavy skewed prefill, and
+the decode layer with its expert weights given as MXFP8.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--row-major]
 """
@@ -281,6 +284,52 @@ def report_config(name: str, steps: int, warmup: int, packed: bool = True) -> di
     return res
 
 
+def report_mxfp8(name: str, steps: int, warmup: int) -> dict:
+    """A bf16 workload with its expert weights given as MXFP8 (E4M3 codes and
+    one E8M0 scale per 32 elements, drawn from the same seeded bf16 weights):
+    per-iteration median/p10/p90, the layer's HBM fraction with the weights
+    counted at 1 + 1/32 bytes per element, the gate_up and down kernels
+    timed by stage events, and the bf16 layer on the same inputs beside it."""
+    shape, recipe = synth.workload(name)
+    inp = synth.make_inputs(shape, recipe, seed=0, device="cuda")
+    c13, s13 = synth.mxfp8_quantize(inp.w13.cpu())
+    c2, s2 = synth.mxfp8_quantize(inp.w2.cpu())
+    mxw = ml.Mxfp8Weights(c13.cuda(), s13.cuda(), c2.cuda(), s2.cuda())
+    del c13, s13, c2, s2
+    out = torch.empty((shape.T, shape.H), dtype=inp.x.dtype, device="cuda")
+    ws = ml.Workspace()
+    ids = torch.empty((shape.T, shape.Kp), dtype=torch.int32, device="cuda")
+    wts = torch.empty((shape.T, shape.Kp), dtype=torch.float32, device="cuda")
+
+    def call(ev=None):
+        ml.forward_inputs(inp, out=out, workspace=ws, routing_out=(ids, wts), packed=mxw, stage_events=ev)
+
+    call()
+    torch.cuda.synchronize()
+    wk = work(shape, ids.cpu().numpy(), inp.adapter_ids.cpu().numpy())
+    wbf16 = wk["experts"] * 3 * shape.I * shape.H * 2          # touched w13 + w2 at 2 bytes per element
+    bytes_layer = wk["bytes_layer"] - wbf16 + wbf16 / 2 * (1 + 1 / 32)
+    t = per_iteration(call, steps, warmup)
+    se = StageEvents(steps)
+    for i in range(steps):
+        call(se.arrays[i])
+    torch.cuda.synchronize()
+    stage = se.stage_ms()
+    se.close()
+    sec = t["median_ms"] * 1e-3
+    gu_bytes = wk["bytes_gate_up"] - wk["experts"] * 2 * shape.I * shape.H * (2 - (1 + 1 / 32))
+    pw = ml.PackedWeights(inp.w13, inp.w2)
+    tb = per_iteration(lambda: ml.forward_inputs(inp, out=out, workspace=ws, packed=pw), steps, warmup)
+    res = {"tokens_per_s": shape.T / sec, **t, "weights": "mxfp8 (E4M3, E8M0 scale per 32)", "dtype": "bf16",
+           "bytes": bytes_layer, "hbm_frac": bytes_layer / sec / HBM_PEAK,
+           "gate_up_us": stage["gate_up"] * 1e3, "down_us": stage["down"] * 1e3,
+           "gate_up_hbm_frac": gu_bytes / (stage["gate_up"] * 1e-3) / HBM_PEAK,
+           "bf16_packed_median_ms": tb["median_ms"], "speedup_vs_bf16": tb["median_ms"] / t["median_ms"]}
+    del inp, mxw, pw
+    torch.cuda.empty_cache()
+    return res
+
+
 REPORTED = ("tiny_fp32_T16", "shared_fused_T1", "shared_fused_T32", "shared_fused_T128", "heavy_skewed_T8192")
 
 
@@ -423,6 +472,9 @@ def main() -> int:
             print(f"bench: reported {name}", file=sys.stderr, flush=True)
             result["reported"][name] = report_config(name, max(20, args.steps), max(5, args.warmup),
                                                      packed=not args.row_major)
+        print("bench: reported gptoss_decode_T64 with MXFP8 weights", file=sys.stderr, flush=True)
+        result["reported"]["gptoss_decode_T64_mxfp8"] = report_mxfp8("gptoss_decode_T64", max(20, args.steps),
+                                                                     max(5, args.warmup))
     print(json.dumps(result), flush=True)
     return 0
 

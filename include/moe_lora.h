@@ -149,15 +149,17 @@ typedef struct moe_lora_plan {
  *     fusion path in the secrett2633 analysis of vLLM PR 46545, "code
  *     analysis" part 2): w13 [E+S, 2I, H] and w2 [E+S, H, I] hold one FP8
  *     E4M3 code per element (1 byte, 16-byte aligned), w13_scale
- *     [E+S, 2I, H/32] and w2_scale [E+S, H, I/32] one E8M0 scale byte per
- *     32 consecutive elements along the reduction; element = code *
+ *     [E+S, 2I, H/32] and w2_scale [E+S, H, I/32] (16-byte aligned) one
+ *     E8M0 scale byte per 32 consecutive elements along the reduction;
+ *     element = code *
  *     2^(scale - 127).  Activations, LoRA stacks and the output stay bf16,
  *     and the products run in bf16 on the exactly converted weights.
  *     Preconditions (not checked on the device): scale bytes in [1, 254],
  *     codes not NaN (0x7F, 0xFF).  Needs dtype bf16, weights_packed = 0,
- *     H and I multiples of 32 and the streaming GEMM (plan gemm_kind 1; for
- *     many rows per expert pass block_m 16 or 32), else
- *     MOE_LORA_EUNSUPPORTED; NULL scales give MOE_LORA_EINVAL. */
+ *     H and I multiples of 32 and at most 8192, and the streaming GEMM
+ *     (plan gemm_kind 1; for many rows per expert pass block_m 16 or 32),
+ *     else MOE_LORA_EUNSUPPORTED; NULL or misaligned scales give
+ *     MOE_LORA_EINVAL. */
 typedef struct moe_lora_args {
     const void *hidden;
     const float *router_logits;

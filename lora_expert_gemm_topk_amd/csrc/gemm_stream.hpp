@@ -29,6 +29,9 @@
 
 namespace moelora {
 
+// MXFP8 weights: most 32-element blocks per weight row (K <= 8192)
+constexpr int kMxMaxBlocks = 256;
+
 struct GemmParams {
     const uint16_t *in;          // gate_up: x [T, Kdim]; down: h [cap, Kdim] (LDS-tiled kernel: h packed)
     const int32_t *sorted_ids;   // [cap]
@@ -96,6 +99,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
     constexpr int MS = BW / 16, NS = BT / 16;
     constexpr int LDW = BW + 4;
     __shared__ float buf[2][BT][LDW];
+    // MXFP8: the scale bytes of the tile's BW weight rows, staged once
+    __shared__ __attribute__((aligned(16))) uint8_t mx_sc[MX ? BW * kMxMaxBlocks : 16];
 
     const int b = blockIdx.y;
     const int npp = p.counters[0];
@@ -135,14 +140,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
         wrow[ms] = p.W + ((int64_t)e * rows_per_expert + (wok[ms] ? grow : 0)) * Kd;
     }
     }
-    // MXFP8: the same rows as byte rows, and their scale rows
-    const uint8_t *wrow8[MS], *srow[MS];
+    // MXFP8: the same rows as byte rows
+    const uint8_t *wrow8[MS];
     if constexpr (MX) {
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
             const int64_t row = (wrow[ms] - p.W) / Kd;  // e * rows_per_expert + row within the expert
             wrow8[ms] = reinterpret_cast<const uint8_t *>(p.W) + row * Kd;
-            srow[ms] = p.Wscale + row * (Kd / 32);
         }
     }
     const uint16_t *xrow[NS];
@@ -167,7 +171,6 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
     constexpr int KC = MX ? 128 : 64;     // reduction per chunk
     const int nch = (int)((Kd + KC - 1) / KC);
     u32x4 wa[2][MS][2], xa[2][NS][XQ];
-    uint32_t sa[2][MS];
     auto load_mx = [&](int buf_i, int c) {
         const int64_t k0 = (int64_t)c * 128 + g * 32;  // block 4c + g (K is a multiple of 32)
         const bool kin = k0 < Kd;
@@ -176,17 +179,20 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
             const bool ok = wok[ms] && kin;
             wa[buf_i][ms][0] = ld16(wrow8[ms] + k0, ok);
             wa[buf_i][ms][1] = ld16(wrow8[ms] + k0 + 16, ok);
-            sa[buf_i][ms] = ok ? (uint32_t)srow[ms][k0 >> 5] : 127u;
         }
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
             for (int q = 0; q < XQ; ++q) xa[buf_i][ns][q] = ld16(xrow[ns] + k0 + 8 * q, xok[ns] && kin);
     };
-    auto compute_mx = [&](int buf_i) {
+    auto compute_mx = [&](int buf_i, int c) {
+        const int64_t k0 = (int64_t)c * 128 + g * 32;
+        const bool kin = k0 < Kd;
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
-            const float sc = __uint_as_float(sa[buf_i][ms] << 23);  // 2^(scale - 127)
+            // the block's scale from the staged copy (past K: any scale, the codes there are zero)
+            const uint32_t sb = kin ? (uint32_t)mx_sc[(ms * 16 + l16) * (int)(Kd / 32) + (int)(k0 >> 5)] : 127u;
+            const float sc = __uint_as_float(sb << 23);  // 2^(scale - 127)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 // codes 8s .. 8s+7 of the lane's 32: dwords 2s and 2s+1
@@ -229,9 +235,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
             xa[buf_i][ns][1] = ld16(xrow[ns] + k0 + 8, xok[ns] && k_hi);
         }
     };
-    auto compute = [&](int buf_i) {
+    auto compute = [&](int buf_i, int c) {
         if constexpr (MX) {
-            compute_mx(buf_i);
+            compute_mx(buf_i, c);
             return;
         }
 #pragma unroll
@@ -245,13 +251,38 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
     };
     int c = w;
     if (c < nch) load(0, c);
+    if constexpr (MX) {
+        // Stage the scale rows while the first chunk is in flight.  A
+        // fragment's 16 weight rows are consecutive rows of w13/w2 (rows start
+        // at multiples of 16 and K is a multiple of 32), so their scales are
+        // 16 * nblk contiguous bytes starting on a 16-byte boundary: copied
+        // in 16-byte pieces to mx_sc[ms][row][block].
+        const int nblk = (int)(Kd / 32);
+        for (int i = (int)threadIdx.x; i < MS * nblk; i += 256) {
+            const int ms = i / nblk, q = i - ms * nblk;
+            int col0, grow0;
+            if (GU) {
+                col0 = i0 + (ms % (MS / 2)) * 16;
+                grow0 = ms / (MS / 2) ? N + col0 : col0;
+            } else {
+                col0 = i0 + ms * 16;
+                grow0 = col0;
+            }
+            if (col0 < N) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                    p.Wscale + ((int64_t)e * rows_per_expert + grow0) * nblk + (int64_t)q * 16);
+                *reinterpret_cast<u32x4 *>(mx_sc + ms * 16 * nblk + q * 16) = v;
+            }
+        }
+        __syncthreads();
+    }
     while (c < nch) {
         if (c + 4 < nch) load(1, c + 4);
-        compute(0);
+        compute(0, c);
         c += 4;
         if (c >= nch) break;
         if (c + 4 < nch) load(0, c + 4);
-        compute(1);
+        compute(1, c);
         c += 4;
     }
 

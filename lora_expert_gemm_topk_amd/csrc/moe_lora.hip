@@ -508,8 +508,10 @@ int moe_lora_check_args(const moe_lora_dims *d, const moe_lora_args *a) {
     if (a->weights_packed && d->dtype != MOE_LORA_BF16) return MOE_LORA_EUNSUPPORTED;
     if (a->weights_mxfp8 != 0 && a->weights_mxfp8 != 1) return MOE_LORA_EINVAL;
     if (a->weights_mxfp8) {
-        if (!a->w13_scale || !a->w2_scale) return MOE_LORA_EINVAL;
-        if (d->dtype != MOE_LORA_BF16 || a->weights_packed || d->H % 32 != 0 || d->I % 32 != 0 || p.kind != 1)
+        if (!a->w13_scale || !a->w2_scale || !aligned(a->w13_scale, 16) || !aligned(a->w2_scale, 16))
+            return MOE_LORA_EINVAL;
+        if (d->dtype != MOE_LORA_BF16 || a->weights_packed || d->H % 32 != 0 || d->I % 32 != 0 || p.kind != 1 ||
+            d->H > 32 * kMxMaxBlocks || d->I > 32 * kMxMaxBlocks)
             return MOE_LORA_EUNSUPPORTED;
     }
     return MOE_LORA_OK;

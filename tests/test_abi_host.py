@@ -138,6 +138,8 @@ def test_check_args_mxfp8_flag():
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_OK
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=2, **sc)) == ml.MOE_LORA_EINVAL
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, w13_scale=0xb000)) == ml.MOE_LORA_EINVAL
+    assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, w13_scale=0xb004, w2_scale=0xc000)) == ml.MOE_LORA_EINVAL
+    assert ml.moe_lora_check_args(_dims(H=8224), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
     # bf16 only, not with packed weights, H and I multiples of 32, streaming GEMM only
     assert ml.moe_lora_check_args(_dims(dtype="f32"), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, weights_packed=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
