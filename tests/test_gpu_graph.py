@@ -4,7 +4,8 @@ The forward neither synchronises the host nor allocates, and clears its
 counters with kernels (no memset nodes), so a captured call can be replayed.
 Each replay is checked bit for bit against an eager call on the same inputs,
 with eager work and host synchronisation between the replays, for the
-streaming and the LDS-tiled plans and with packed weights.
+streaming and the LDS-tiled plans, with packed weights and with MXFP8
+weights.
 """
 from __future__ import annotations
 
@@ -17,11 +18,20 @@ from lora_expert_gemm_topk_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,bm,packed", [(48, 0, False), (64, 0, True), (600, 128, True), (1, 0, False)])
+def _weights(inp, packed):
+    if packed == "mx":
+        c13, s13 = synth.mxfp8_quantize(inp.w13.cpu())
+        c2, s2 = synth.mxfp8_quantize(inp.w2.cpu())
+        return ml.Mxfp8Weights(c13.cuda(), s13.cuda(), c2.cuda(), s2.cuda())
+    return ml.PackedWeights(inp.w13, inp.w2) if packed else None
+
+
+@pytest.mark.parametrize("T,bm,packed", [(48, 0, False), (64, 0, True), (600, 128, True), (1, 0, False),
+                                         (64, 0, "mx"), (7, 32, "mx")])
 def test_graph_replay_equals_eager(T, bm, packed):
     shape = synth.LayerShape(T=T, H=256, I=192, E=8, K=2, S=1, L=3, r=16, rsf=2.5)
     inp = synth.make_inputs(shape, synth.Recipe(adapters="uniform_all"), seed=T, device="cuda")
-    pw = ml.PackedWeights(inp.w13, inp.w2) if packed else None
+    pw = _weights(inp, packed)
     ws = ml.Workspace()
     out = torch.empty((T, shape.H), dtype=torch.bfloat16, device="cuda")
     ref = ml.forward_inputs(inp, block_m=bm, packed=pw).clone()   # eager, own workspace
