@@ -89,10 +89,11 @@ __device__ __forceinline__ void lora_expand_add(const GemmParams &p, int e, int 
 // FP8 E4M3 code, and one E8M0 scale byte per 32-element block along K; the
 // element is code * 2^(scale - 127).  The reduction then runs in 128-wide
 // chunks: lane (row, g) loads the 32 codes of block 4c + g (whole 128-byte
-// row segments per 4 lanes) and its scale, converts them with the hardware's
-// scaled FP8 -> bf16 conversion (exact: E4M3 has 3 mantissa bits) and feeds
-// the same bf16 MFMAs; the matching 32 activations are that lane's 64 bytes
-// of x.  Weight bytes per layer call halve.
+// row segments per 4 lanes), takes the block's scale from a copy of the
+// tile's scale rows staged in LDS once per workgroup, converts the codes with
+// the hardware's scaled FP8 -> bf16 conversion (exact: E4M3 has 3 mantissa
+// bits) and feeds the same bf16 MFMAs; the matching 32 activations are that
+// lane's 64 bytes of x.  Weight bytes per layer call halve.
 template <int BW, int BT, bool GU, bool WP, bool MX = false>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
     static_assert(!(MX && WP), "MXFP8 weights are read row-major");
