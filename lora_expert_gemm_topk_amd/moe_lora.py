@@ -261,7 +261,8 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     """The fused MoE-LoRA layer on the GPU (enqueued on the current stream).
 
     Shapes: x [T,H], logits [T,E] f32, adapter_ids [T] i32 (-1 = none),
-    w13 [E+S,2I,H], w2 [E+S,H,I] (or w13 = PackedWeights of both, w2 = None),
+    w13 [E+S,2I,H], w2 [E+S,H,I] (or w13 = PackedWeights or Mxfp8Weights of
+    both, w2 = None),
     a13 [L,E+S,r,H], b13 [L,E+S,2I,r],
     a2 [L,E+S,r,I], b2 [L,E+S,H,r]; x, weights and out share one dtype
     (bf16 or f32).  routing_out = (ids [T,K+S] i32, weights [T,K+S] f32)
