@@ -228,6 +228,25 @@ int moe_lora_align(const moe_lora_dims *dims, const int32_t *topk_ids, const int
 /* The whole layer (steps 1-3), enqueued on `stream`. */
 int moe_lora_forward(const moe_lora_dims *dims, const moe_lora_args *args, void *stream);
 
+/* Check of the input preconditions moe_lora_forward does not check on the
+ * device, for debugging a caller: every router logit finite; with LoRA
+ * active every adapter id in [-1, L); with weights_mxfp8 every scale byte in
+ * [1, 254] and no NaN code (0x7F, 0xFF).  Reads the same `args` as
+ * moe_lora_forward (only router_logits, adapter_ids, w13, w2 and the scale
+ * pointers) and uses the first 2 KiB of args->workspace as scratch.
+ * Enqueued on `stream` (two small launches, no host synchronisation):
+ * when the stream reaches it, *status (device int32, caller-owned) holds the
+ * OR of MOE_LORA_BAD_LOGIT, MOE_LORA_BAD_ADAPTER and MOE_LORA_BAD_MXFP8
+ * for the violations found, 0 when none.  Returns MOE_LORA_OK, or
+ * MOE_LORA_EINVAL / MOE_LORA_EUNSUPPORTED / MOE_LORA_EWORKSPACE from the
+ * same checks as moe_lora_check_args (a workspace of at least 2 KiB), or
+ * MOE_LORA_EINVAL for a null `status`; MOE_LORA_EHIP on a launch failure.
+ * T = 0 writes 0 to *status. */
+#define MOE_LORA_BAD_LOGIT 1
+#define MOE_LORA_BAD_ADAPTER 2
+#define MOE_LORA_BAD_MXFP8 4
+int moe_lora_check_inputs(const moe_lora_dims *dims, const moe_lora_args *args, int32_t *status, void *stream);
+
 /* Packed expert weights (bf16 only).  An optional one-time re-layout of w13
  * and w2 (for example at model load) into the order the GEMM kernels read:
  * rows in groups of 16 and the reduction dimension in slabs of 32, one

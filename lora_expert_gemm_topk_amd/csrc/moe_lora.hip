@@ -26,6 +26,7 @@
 
 #include "moe_lora.h"
 #include "align.hpp"
+#include "check.hpp"
 #include "combine.hpp"
 #include "fp32_path.hpp"
 #include "gemm_stream.hpp"
@@ -564,6 +565,42 @@ int moe_lora_pack_weights(const moe_lora_dims *d, const void *w13, const void *w
     }
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "pack launch");
+}
+
+int moe_lora_check_inputs(const moe_lora_dims *d, const moe_lora_args *a, int32_t *status, void *stream) {
+    const int rc = moe_lora_check_args(d, a);
+    if (rc != MOE_LORA_OK) return rc;
+    if (!status) return MOE_LORA_EINVAL;
+    Plan p;
+    make_plan(d, &p);
+    hipStream_t st = (hipStream_t)stream;
+    CheckParams cp{};
+    cp.status = status;
+    if (d->T > 0) {
+        if (a->workspace_bytes < sizeof(int32_t) * kCheckBlocks) return MOE_LORA_EWORKSPACE;
+        cp.partial = (int32_t *)a->workspace;
+        cp.logits = a->router_logits;
+        cp.n_logits = (int64_t)d->T * d->E;
+        cp.adapter_ids = p.lora ? a->adapter_ids : nullptr;
+        cp.n_adapters = p.lora ? d->T : 0;
+        cp.L = (int)p.La;
+        if (a->weights_mxfp8) {
+            const int64_t Ep = p.Ep, H = d->H, I = d->I;
+            cp.mx[0] = (const uint8_t *)a->w13;
+            cp.n_mx[0] = Ep * 2 * I * H;
+            cp.mx[1] = (const uint8_t *)a->w13_scale;
+            cp.n_mx[1] = Ep * 2 * I * (H / 32);
+            cp.mx[2] = (const uint8_t *)a->w2;
+            cp.n_mx[2] = Ep * H * I;
+            cp.mx[3] = (const uint8_t *)a->w2_scale;
+            cp.n_mx[3] = Ep * H * (I / 32);
+        }
+        hipLaunchKernelGGL(check_inputs_kernel, dim3(kCheckBlocks), dim3(256), 0, st, cp);
+    }
+    // with T = 0 the reduction alone writes a zero status
+    hipLaunchKernelGGL(check_inputs_reduce_kernel, dim3(1), dim3(256), 0, st, cp);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "check_inputs launch");
 }
 
 int moe_lora_route(const moe_lora_dims *d, const float *logits, int32_t *topk_ids, float *topk_weights,

@@ -23,11 +23,14 @@ MOE_LORA_EWORKSPACE = -3
 MOE_LORA_EHIP = -4
 MOE_LORA_F32 = 0
 MOE_LORA_BF16 = 1
+MOE_LORA_BAD_LOGIT = 1
+MOE_LORA_BAD_ADAPTER = 2
+MOE_LORA_BAD_MXFP8 = 4
 STAGES = ("route", "align", "shrink13", "gate_up", "shrink2", "down", "combine")
 
 EXPORTED = ("moe_lora_plan_query", "moe_lora_workspace_bytes", "moe_lora_check_args", "moe_lora_route",
             "moe_lora_align", "moe_lora_forward", "moe_lora_packed_weight_bytes", "moe_lora_pack_weights",
-            "moe_lora_strerror")
+            "moe_lora_strerror", "moe_lora_check_inputs")
 
 
 class MoeLoraDims(ctypes.Structure):
@@ -93,6 +96,8 @@ def lib():
     L.moe_lora_packed_weight_bytes.restype = ctypes.c_size_t
     L.moe_lora_pack_weights.argtypes = [P(MoeLoraDims), vp, vp, vp, vp, vp]
     L.moe_lora_pack_weights.restype = ctypes.c_int
+    L.moe_lora_check_inputs.argtypes = [P(MoeLoraDims), P(MoeLoraArgs), vp, vp]
+    L.moe_lora_check_inputs.restype = ctypes.c_int
     L.moe_lora_strerror.argtypes = [ctypes.c_int]
     L.moe_lora_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -269,6 +274,42 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     receives the routing decisions when given.  stage_events: optional
     ctypes array of 2*len(STAGES) hipEvent_t handles recorded around each
     stage on the launch stream."""
+    dims, args, out, _ws = _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, K=K, S=S, rsf=rsf,
+                                       renormalize=renormalize, out=out, workspace=workspace, block_m=block_m,
+                                       lora_block_m=lora_block_m, split_k=split_k, routing_out=routing_out,
+                                       stage_events=stage_events)
+    with torch.cuda.device(x.device):
+        rc = lib().moe_lora_forward(ctypes.byref(dims), ctypes.byref(args), _stream(x.device))
+    if rc != MOE_LORA_OK:
+        raise MoeLoraError(rc, "moe_lora_forward")
+    return out
+
+
+def moe_lora_check_inputs(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optional[torch.Tensor],
+                          w13: torch.Tensor, w2: torch.Tensor, a13=None, b13=None, a2=None, b2=None, *,
+                          K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1,
+                          workspace: Optional[Workspace] = None, status: Optional[torch.Tensor] = None,
+                          **kw) -> torch.Tensor:
+    """Checks the device-side preconditions of moe_lora_forward on the same
+    arguments (finite logits, adapter ids in [-1, L), valid MXFP8 scales and
+    codes).  Returns the device int32 status word (enqueued on the current
+    stream): the OR of the MOE_LORA_BAD_* flags found, 0 when none."""
+    dims, args, _out, _ws = _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, K=K, S=S, rsf=rsf,
+                                        renormalize=renormalize, out=None, workspace=workspace, **kw)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=x.device)
+    _dev_tensor(status, "status", torch.int32)
+    with torch.cuda.device(x.device):
+        rc = lib().moe_lora_check_inputs(ctypes.byref(dims), ctypes.byref(args), _ptr(status), _stream(x.device))
+    if rc != MOE_LORA_OK:
+        raise MoeLoraError(rc, "moe_lora_check_inputs")
+    return status
+
+
+def _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K, S, rsf, renormalize, out, workspace,
+                block_m=0, lora_block_m=0, split_k=0, routing_out=None, stage_events=None):
+    """Marshals the layer's tensors (shapes as for moe_lora_forward) into
+    (dims, args, out, workspace tensor)."""
     dt = x.dtype
     packed = isinstance(w13, PackedWeights)
     mx = isinstance(w13, Mxfp8Weights)
@@ -291,6 +332,17 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
         I = twoI // 2
     E = logits.shape[1]
     L, r = (a13.shape[0], a13.shape[2]) if a13 is not None else (0, 0)
+    want = {"logits": (logits, (T, E)), "out": (out, (T, H))}
+    if not (packed or mx):
+        want.update(w13=(w13, (E + S, 2 * I, H)), w2=(w2, (E + S, H, I)))
+    elif Ep != E + S:
+        raise ValueError(f"the weights hold {Ep} experts, E+S = {E + S}")
+    if a13 is not None:
+        want.update(adapter_ids=(adapter_ids, (T,)), a13=(a13, (L, E + S, r, H)), b13=(b13, (L, E + S, 2 * I, r)),
+                    a2=(a2, (L, E + S, r, I)), b2=(b2, (L, E + S, H, r)))
+    for name, (t, shp) in want.items():
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
     dims = make_dims(T, H, I, E, K, S, L, r, rsf, renormalize, dt, block_m, lora_block_m, split_k)
     if out is None:
         out = torch.empty((T, H), dtype=dt, device=x.device)
@@ -308,11 +360,7 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
                        ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None,
                        1 if packed else 0, 1 if mx else 0,
                        w13.w13_scale.data_ptr() if mx else None, w13.w2_scale.data_ptr() if mx else None)
-    with torch.cuda.device(x.device):
-        rc = lib().moe_lora_forward(ctypes.byref(dims), ctypes.byref(args), _stream(x.device))
-    if rc != MOE_LORA_OK:
-        raise MoeLoraError(rc, "moe_lora_forward")
-    return out
+    return dims, args, out, ws
 
 
 def forward_inputs(inp, *, lora: bool = True, packed=None, **kw) -> torch.Tensor:

@@ -178,3 +178,18 @@ def test_pack_weights_rejects_without_device():
                                    None) == ml.MOE_LORA_EUNSUPPORTED
     # nothing to do is fine (no launch)
     assert L.moe_lora_pack_weights(ctypes.byref(d), None, None, None, None, None) == ml.MOE_LORA_OK
+
+
+def test_check_inputs_rejects_without_device():
+    L = mm.lib()
+    d = _dims()
+    st = ctypes.c_void_p(0x20000)
+    # the same argument checks as moe_lora_check_args, then a null status
+    assert L.moe_lora_check_inputs(ctypes.byref(d), ctypes.byref(_args(hidden=None)), st, None) == \
+        ml.MOE_LORA_EINVAL
+    assert L.moe_lora_check_inputs(ctypes.byref(_dims(r=12)), ctypes.byref(_args()), st, None) == \
+        ml.MOE_LORA_EUNSUPPORTED
+    need = ml.moe_lora_workspace_bytes(d)
+    assert L.moe_lora_check_inputs(ctypes.byref(d), ctypes.byref(_args(workspace_bytes=need - 1)), st, None) == \
+        ml.MOE_LORA_EWORKSPACE
+    assert L.moe_lora_check_inputs(ctypes.byref(d), ctypes.byref(_args()), None, None) == ml.MOE_LORA_EINVAL
