@@ -294,8 +294,9 @@ def moe_lora_check_inputs(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Op
     arguments (finite logits, adapter ids in [-1, L), valid MXFP8 scales and
     codes).  Returns the device int32 status word (enqueued on the current
     stream): the OR of the MOE_LORA_BAD_* flags found, 0 when none."""
+    # the check writes no output: x stands in for `out`, which only has to pass the argument checks
     dims, args, _out, _ws = _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, K=K, S=S, rsf=rsf,
-                                        renormalize=renormalize, out=None, workspace=workspace, **kw)
+                                        renormalize=renormalize, out=x, workspace=workspace, **kw)
     if status is None:
         status = torch.empty(1, dtype=torch.int32, device=x.device)
     _dev_tensor(status, "status", torch.int32)
