@@ -5,7 +5,8 @@ counters with kernels (no memset nodes), so a captured call can be replayed.
 Each replay is checked bit for bit against an eager call on the same inputs,
 with eager work and host synchronisation between the replays, for the
 streaming and the LDS-tiled plans, with packed weights and with MXFP8
-weights.
+weights.  The input check is captured too and replayed over changing
+buffer contents.
 """
 from __future__ import annotations
 
@@ -54,3 +55,39 @@ def test_graph_replay_equals_eager(T, bm, packed):
         eager = ml.forward_inputs(inp, block_m=bm, packed=pw, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(eager.view(torch.int16), ref.view(torch.int16)), f"eager after replay {i}"
+
+
+def test_graph_replay_of_the_input_check():
+    """moe_lora_check_inputs captured once: each replay reports the values the
+    buffers hold at that replay (bad values planted and removed between
+    replays by eager copies)."""
+    shape = synth.LayerShape(T=40, H=256, I=192, E=8, K=2, S=1, L=3, r=16, rsf=2.5)
+    inp = synth.make_inputs(shape, synth.Recipe(adapters="uniform_all"), seed=5, device="cuda")
+    ws = ml.Workspace()
+    st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+
+    def check():
+        ml.moe_lora_check_inputs(inp.x, inp.logits, inp.adapter_ids, inp.w13, inp.w2, inp.a13, inp.b13, inp.a2,
+                                 inp.b2, K=shape.K, S=shape.S, rsf=shape.rsf, workspace=ws, status=st)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        check()                                                     # sizes the workspace
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        check()
+    lg0, ad0 = inp.logits.clone(), inp.adapter_ids.clone()
+    for i, (plant, want) in enumerate([(None, 0), ("logit", 1), ("adapter", 2), ("both", 3), (None, 0)]):
+        inp.logits.copy_(lg0)
+        inp.adapter_ids.copy_(ad0)
+        if plant in ("logit", "both"):
+            inp.logits[3, 1] = float("nan")
+        if plant in ("adapter", "both"):
+            inp.adapter_ids[9] = shape.L
+        st.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st.item()) == want, f"replay {i} ({plant})"
