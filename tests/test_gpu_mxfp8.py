@@ -25,6 +25,8 @@ CASES = [
     dict(T=33, H=128, I=96, E=5, K=2, S=0, L=0, r=0, block_m=32),
     dict(T=1, H=192, I=64, E=9, K=8, S=1, L=0, r=0, rsf=2.5),
     dict(T=7, H=64, I=64, E=4, K=1, S=0, L=2, r=8, block_m=16),   # one 128-wide chunk of K at most
+    dict(T=9, H=8192, I=64, E=4, K=2, S=0, L=2, r=16),    # gate_up at the largest K (256 scale blocks per row)
+    dict(T=9, H=64, I=8192, E=4, K=2, S=1, L=2, r=8),     # down at the largest K
 ]
 
 
