@@ -136,6 +136,13 @@ SMALL = [
     dict(T=200, H=128, I=128, E=5, K=3, S=0, L=0, r=0, dtype="bf16", block_m=128),
     # 64 slots per token: the most the router launch takes the gate_up shrink for
     dict(T=8, H=64, I=64, E=100, K=63, S=1, L=3, r=8, rsf=2.0, dtype="bf16"),
+    # the largest rank (128, in 16-row LoRA items) on both GEMM kinds and on the fp32 path
+    dict(T=40, H=256, I=192, E=6, K=2, S=1, L=3, r=128, rsf=2.5, dtype="bf16", block_m=16),
+    dict(T=300, H=256, I=192, E=4, K=2, S=0, L=3, r=128, dtype="bf16", block_m=128),
+    dict(T=24, H=128, I=64, E=4, K=2, S=0, L=2, r=128, dtype="f32"),
+    # a wide, ragged hidden size (12296 = 8 * 1537, not a multiple of 32) on both GEMM kinds
+    dict(T=24, H=12296, I=64, E=4, K=2, S=0, L=2, r=16, dtype="bf16", block_m=16),
+    dict(T=260, H=12296, I=64, E=4, K=2, S=0, L=2, r=16, dtype="bf16", block_m=128),
 ]
 
 
