@@ -29,6 +29,8 @@ ROUTE_CASES = [
     dict(T=16, E=4, K=2), dict(T=64, E=32, K=4), dict(T=4096, E=32, K=4),
     dict(T=128, E=64, K=8, S=1, rsf=2.5), dict(T=33, E=300, K=5), dict(T=3, E=1000, K=64, S=2),
     dict(T=50, E=12, K=3, renorm=0), dict(T=1, E=1, K=1), dict(T=8192, E=128, K=8, zipf=True),
+    # K = E: every expert selected, in value order
+    dict(T=20, E=8, K=8), dict(T=7, E=64, K=64, S=1, rsf=2.0), dict(T=9, E=40, K=40, renorm=0),
 ]
 
 
@@ -136,6 +138,9 @@ SMALL = [
     dict(T=200, H=128, I=128, E=5, K=3, S=0, L=0, r=0, dtype="bf16", block_m=128),
     # 64 slots per token: the most the router launch takes the gate_up shrink for
     dict(T=8, H=64, I=64, E=100, K=63, S=1, L=3, r=8, rsf=2.0, dtype="bf16"),
+    # K = E: every pair of a token on a different expert, all experts on every token
+    dict(T=12, H=64, I=64, E=4, K=4, S=0, L=2, r=8, dtype="bf16"),
+    dict(T=300, H=128, I=96, E=3, K=3, S=1, L=2, r=16, rsf=2.5, dtype="bf16", block_m=128),
     # the largest rank (128, in 16-row LoRA items) on both GEMM kinds and on the fp32 path
     dict(T=40, H=256, I=192, E=6, K=2, S=1, L=3, r=128, rsf=2.5, dtype="bf16", block_m=16),
     dict(T=300, H=256, I=192, E=4, K=2, S=0, L=3, r=128, dtype="bf16", block_m=128),
