@@ -171,6 +171,10 @@ def moe_lora_align(topk_ids: torch.Tensor, adapter_ids: Optional[torch.Tensor], 
     lora_items [max_items, 4], num_items [1] and the plan, all device tensors."""
     _dev_tensor(topk_ids, "topk_ids", torch.int32)
     _dev_tensor(adapter_ids, "adapter_ids", torch.int32)
+    if tuple(topk_ids.shape) != (dims.T, dims.K + dims.S):
+        raise ValueError(f"topk_ids has shape {tuple(topk_ids.shape)}, expected {(dims.T, dims.K + dims.S)}")
+    if adapter_ids is not None and tuple(adapter_ids.shape) != (dims.T,):
+        raise ValueError(f"adapter_ids has shape {tuple(adapter_ids.shape)}, expected {(dims.T,)}")
     plan = moe_lora_plan_query(dims)
     dev = topk_ids.device
     sorted_ids = torch.empty(plan["sorted_capacity"], dtype=torch.int32, device=dev)
