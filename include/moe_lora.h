@@ -35,7 +35,8 @@
  *     until the stream reaches the call.
  *   - Return value: MOE_LORA_OK, or a negative code below.  Nothing is
  *     enqueued when argument checking fails.  Preconditions NOT checked on
- *     the device: router logits are finite; adapter ids lie in [-1, L).
+ *     the device by the layer: router logits are finite; adapter ids lie in
+ *     [-1, L) (moe_lora_check_inputs tests both on request).
  *   - T may be 0: the call is a no-op returning MOE_LORA_OK.
  *   - Concurrent calls are safe when they use distinct workspaces.
  */
@@ -229,12 +230,16 @@ int moe_lora_align(const moe_lora_dims *dims, const int32_t *topk_ids, const int
 int moe_lora_forward(const moe_lora_dims *dims, const moe_lora_args *args, void *stream);
 
 /* Check of the input preconditions moe_lora_forward does not check on the
- * device, for debugging a caller: every router logit finite; with LoRA
+ * device, for debugging a caller.  The logits feed the top-k softmax of step
+ * 1 and each adapter id picks one of the L adapters (or none) of step 3
+ * (sources above); the MXFP8 conditions are those of the weight format
+ * under moe_lora_args.weights_mxfp8.  Checked: every router logit finite; with LoRA
  * active every adapter id in [-1, L); with weights_mxfp8 every scale byte in
  * [1, 254] and no NaN code (0x7F, 0xFF).  Reads the same `args` as
  * moe_lora_forward (only router_logits, adapter_ids, w13, w2 and the scale
  * pointers) and uses the first 2 KiB of args->workspace as scratch.
- * Enqueued on `stream` (two small launches, no host synchronisation):
+ * Enqueued on `stream` (two small launches, no host synchronisation, no
+ * allocation, so it can be captured in a graph like the forward):
  * when the stream reaches it, *status (device int32, caller-owned) holds the
  * OR of MOE_LORA_BAD_LOGIT, MOE_LORA_BAD_ADAPTER and MOE_LORA_BAD_MXFP8
  * for the violations found, 0 when none.  Returns MOE_LORA_OK, or
