@@ -144,7 +144,8 @@ typedef struct moe_lora_plan {
  *     launches nothing), so the caller can time each kernel on the stream it
  *     runs on.  Stages: see MOE_LORA_STAGE_*.
  *   weights_packed: 0 = w13 and w2 as above; 1 = w13 and w2 are the packed
- *     copies written by moe_lora_pack_weights (bf16 only).
+ *     copies written by moe_lora_pack_weights (bf16), or with weights_mxfp8
+ *     the packed codes written by moe_lora_pack_mxfp8_weights.
  *   weights_mxfp8: 0 = w13 and w2 in dtype as above; 1 = MXFP8 expert
  *     weights (MX block scaling, the precision of the ROCm shared-expert
  *     fusion path in the secrett2633 analysis of vLLM PR 46545, "code
@@ -156,7 +157,7 @@ typedef struct moe_lora_plan {
  *     2^(scale - 127).  Activations, LoRA stacks and the output stay bf16,
  *     and the products run in bf16 on the exactly converted weights.
  *     Preconditions (not checked on the device): scale bytes in [1, 254],
- *     codes not NaN (0x7F, 0xFF).  Needs dtype bf16, weights_packed = 0,
+ *     codes not NaN (0x7F, 0xFF).  Needs dtype bf16,
  *     H and I multiples of 32 and at most 8192, and the streaming GEMM
  *     (plan gemm_kind 1; for many rows per expert pass block_m 16 or 32),
  *     else MOE_LORA_EUNSUPPORTED; NULL or misaligned scales give
@@ -251,6 +252,28 @@ int moe_lora_forward(const moe_lora_dims *dims, const moe_lora_args *args, void 
 #define MOE_LORA_BAD_ADAPTER 2
 #define MOE_LORA_BAD_MXFP8 4
 int moe_lora_check_inputs(const moe_lora_dims *dims, const moe_lora_args *args, int32_t *status, void *stream);
+
+/* Packed MXFP8 codes.  An optional one-time re-layout of the E4M3 code
+ * matrices of moe_lora_args.weights_mxfp8 (w13 [E+S,2I,H], w2 [E+S,H,I],
+ * uint8): for every 16 consecutive rows of an expert and every 128-wide
+ * chunk c of the reduction, one 2 KiB block whose byte 16*(64*q + 16*g + r)
+ * starts the 16 codes 128c + 32g + 16q .. +15 of row r (q in {0,1}, g in
+ * 0..3, zeros past the reduction length), the order in which the streaming
+ * GEMM loads them.  With weights_packed = 1 and weights_mxfp8 = 1, w13 and
+ * w2 point at these copies (the scales stay row-major); results are
+ * bit-identical to the row-major codes.
+ *   moe_lora_packed_mxfp8_bytes: bytes of the packed w13 (which = 0) or w2
+ *   (which = 1); 0 when the shape has no MXFP8 form (H or I not a multiple
+ *   of 32) or another value of `which`.
+ *   moe_lora_pack_mxfp8_weights: enqueues the copy on `stream`; a NULL
+ *   source with a NULL destination skips that matrix.  MOE_LORA_EINVAL for
+ *   a source without a destination (or the reverse) or a pointer not 16-byte
+ *   aligned, MOE_LORA_EUNSUPPORTED for H or I not a multiple of 32, the
+ *   dims' own error codes, MOE_LORA_EHIP on a launch failure.  Buffers are
+ *   caller-owned device memory. */
+size_t moe_lora_packed_mxfp8_bytes(const moe_lora_dims *dims, int which);
+int moe_lora_pack_mxfp8_weights(const moe_lora_dims *dims, const void *w13, const void *w2, void *w13_packed,
+                                void *w2_packed, void *stream);
 
 /* Packed expert weights (bf16 only).  An optional one-time re-layout of w13
  * and w2 (for example at model load) into the order the GEMM kernels read:

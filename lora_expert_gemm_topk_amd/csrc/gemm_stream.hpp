@@ -96,7 +96,6 @@ __device__ __forceinline__ void lora_expand_add(const GemmParams &p, int e, int 
 // lane's 64 bytes of x.  Weight bytes per layer call halve.
 template <int BW, int BT, bool GU, bool WP, bool MX = false>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
-    static_assert(!(MX && WP), "MXFP8 weights are read row-major");
     constexpr int MS = BW / 16, NS = BT / 16;
     constexpr int LDW = BW + 4;
     __shared__ float buf[2][BT][LDW];
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
     const uint16_t *wrow[MS];
     bool wok[MS];
     const int64_t nslab_w = (Kd + kSlabK - 1) / kSlabK;
-    if constexpr (WP) {
+    if constexpr (WP && !MX) {
         // the packed group count covers every tile of the grid
         const int64_t G = GU ? packed_w13_groups(N) : packed_w2_groups(N);
 #pragma unroll
@@ -141,13 +140,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
         wrow[ms] = p.W + ((int64_t)e * rows_per_expert + (wok[ms] ? grow : 0)) * Kd;
     }
     }
-    // MXFP8: the same rows as byte rows
+    // MXFP8: the same rows as byte rows; with packed codes (WP) the lane's
+    // place in its fragment's 2 KiB chunk blocks
     const uint8_t *wrow8[MS];
     if constexpr (MX) {
+        const int64_t nchp = packed_mx_chunks(Kd);
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
             const int64_t row = (wrow[ms] - p.W) / Kd;  // e * rows_per_expert + row within the expert
-            wrow8[ms] = reinterpret_cast<const uint8_t *>(p.W) + row * Kd;
+            if constexpr (WP)
+                wrow8[ms] = reinterpret_cast<const uint8_t *>(p.W) + ((row >> 4) * nchp * 2048 + lane * 16);
+            else
+                wrow8[ms] = reinterpret_cast<const uint8_t *>(p.W) + row * Kd;
         }
     }
     const uint16_t *xrow[NS];
@@ -178,8 +182,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
             const bool ok = wok[ms] && kin;
-            wa[buf_i][ms][0] = ld16(wrow8[ms] + k0, ok);
-            wa[buf_i][ms][1] = ld16(wrow8[ms] + k0 + 16, ok);
+            if constexpr (WP) {
+                wa[buf_i][ms][0] = ld16(wrow8[ms] + (int64_t)c * 2048, ok);
+                wa[buf_i][ms][1] = ld16(wrow8[ms] + (int64_t)c * 2048 + 1024, ok);
+            } else {
+                wa[buf_i][ms][0] = ld16(wrow8[ms] + k0, ok);
+                wa[buf_i][ms][1] = ld16(wrow8[ms] + k0 + 16, ok);
+            }
         }
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
     __syncthreads();
 
     // Epilogue on the finished tile buf[1][token][feature].
-    if (GU && WP) {
+    if (GU && WP && !MX) {
         // tile rows 8qp .. 8qp+7 = gate f, gate f+1, up f, up f+1, gate f+2,
         // gate f+3, up f+2, up f+3 with f = i0 + 4qp
         constexpr int QP = BW / 8;

@@ -452,8 +452,13 @@ void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, con
         // MXFP8 weights: the streaming kernel only (checked by moe_lora_check_args)
         const int tile = GU ? kStreamBW / 2 : kStreamBW;
         const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
-        if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, false, true>), grid, block, 0, st, gp);
-        else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, false, true>), grid, block, 0, st, gp);
+        if (wp) {
+            if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, true, true>), grid, block, 0, st, gp);
+            else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, true, true>), grid, block, 0, st, gp);
+        } else {
+            if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, false, true>), grid, block, 0, st, gp);
+            else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, false, true>), grid, block, 0, st, gp);
+        }
         return;
     }
     if (wp) launch_gemm_wp<GU, true>(pl, gp, tiles, ntiles, st);
@@ -511,7 +516,7 @@ int moe_lora_check_args(const moe_lora_dims *d, const moe_lora_args *a) {
     if (a->weights_mxfp8) {
         if (!a->w13_scale || !a->w2_scale || !aligned(a->w13_scale, 16) || !aligned(a->w2_scale, 16))
             return MOE_LORA_EINVAL;
-        if (d->dtype != MOE_LORA_BF16 || a->weights_packed || d->H % 32 != 0 || d->I % 32 != 0 || p.kind != 1 ||
+        if (d->dtype != MOE_LORA_BF16 || d->H % 32 != 0 || d->I % 32 != 0 || p.kind != 1 ||
             d->H > 32 * kMxMaxBlocks || d->I > 32 * kMxMaxBlocks)
             return MOE_LORA_EUNSUPPORTED;
     }
@@ -567,6 +572,43 @@ int moe_lora_pack_weights(const moe_lora_dims *d, const void *w13, const void *w
     return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "pack launch");
 }
 
+size_t moe_lora_packed_mxfp8_bytes(const moe_lora_dims *d, int which) {
+    Plan p;
+    if (make_plan(d, &p) != MOE_LORA_OK || d->H % 32 != 0 || d->I % 32 != 0) return 0;
+    if (which == 0) return (size_t)(p.Ep * 2 * d->I / 16) * packed_mx_chunks(d->H) * 2048;
+    if (which == 1) return (size_t)(p.Ep * d->H / 16) * packed_mx_chunks(d->I) * 2048;
+    return 0;
+}
+
+int moe_lora_pack_mxfp8_weights(const moe_lora_dims *d, const void *w13, const void *w2, void *w13_packed,
+                                void *w2_packed, void *stream) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc != MOE_LORA_OK) return rc;
+    if (d->H % 32 != 0 || d->I % 32 != 0) return MOE_LORA_EUNSUPPORTED;
+    if ((w13 == nullptr) != (w13_packed == nullptr) || (w2 == nullptr) != (w2_packed == nullptr))
+        return MOE_LORA_EINVAL;
+    const void *ptrs[] = {w13, w2, w13_packed, w2_packed};
+    for (const void *ptr : ptrs)
+        if (ptr && !aligned(ptr, 16)) return MOE_LORA_EINVAL;
+    if (!w13 && !w2) return MOE_LORA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    for (int which = 0; which < 2; ++which) {
+        const void *src = which ? w2 : w13;
+        if (!src) continue;
+        PackMxParams pm;
+        pm.src = (const uint8_t *)src;
+        pm.dst = (uint8_t *)(which ? w2_packed : w13_packed);
+        pm.K = (int)(which ? d->I : d->H);
+        pm.nch = (int)packed_mx_chunks(pm.K);
+        pm.pieces = (int64_t)moe_lora_packed_mxfp8_bytes(d, which) / 16;
+        const int64_t blocks = (pm.pieces + 255) / 256;
+        hipLaunchKernelGGL(pack_mx_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st, pm);
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "pack mxfp8 launch");
+}
+
 int moe_lora_check_inputs(const moe_lora_dims *d, const moe_lora_args *a, int32_t *status, void *stream) {
     const int rc = moe_lora_check_args(d, a);
     if (rc != MOE_LORA_OK) return rc;
@@ -587,11 +629,11 @@ int moe_lora_check_inputs(const moe_lora_dims *d, const moe_lora_args *a, int32_
         if (a->weights_mxfp8) {
             const int64_t Ep = p.Ep, H = d->H, I = d->I;
             cp.mx[0] = (const uint8_t *)a->w13;
-            cp.n_mx[0] = Ep * 2 * I * H;
+            cp.n_mx[0] = a->weights_packed ? (int64_t)moe_lora_packed_mxfp8_bytes(d, 0) : Ep * 2 * I * H;
             cp.mx[1] = (const uint8_t *)a->w13_scale;
             cp.n_mx[1] = Ep * 2 * I * (H / 32);
             cp.mx[2] = (const uint8_t *)a->w2;
-            cp.n_mx[2] = Ep * H * I;
+            cp.n_mx[2] = a->weights_packed ? (int64_t)moe_lora_packed_mxfp8_bytes(d, 1) : Ep * H * I;
             cp.mx[3] = (const uint8_t *)a->w2_scale;
             cp.n_mx[3] = Ep * H * (I / 32);
         }

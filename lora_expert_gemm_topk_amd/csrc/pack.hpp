@@ -48,6 +48,34 @@ __global__ __launch_bounds__(256) void pack_x_kernel(PackXParams p) { pack_x_gro
 __host__ __device__ inline int64_t packed_w13_groups(int64_t I) { return 16 * ((I + 127) / 128); }
 __host__ __device__ inline int64_t packed_w2_groups(int64_t H) { return 16 * ((H + 255) / 256); }
 
+// Packed MXFP8 codes (see moe_lora_pack_mxfp8_weights): for every 16
+// consecutive rows of an expert's code matrix and every 128-wide chunk c of
+// K, one 2 KiB block [q][lane][16 bytes] with lane = 16 g + r holding codes
+// 128 c + 32 g + 16 q .. + 15 of row r (zeros past K).  That is the per-lane
+// order of the streaming GEMM's MXFP8 fragment loads, so each of its load
+// instructions reads 1 KiB contiguously.
+__host__ __device__ inline int64_t packed_mx_chunks(int64_t K) { return (K + 127) / 128; }
+
+struct PackMxParams {
+    const uint8_t *src;  // [rows_total, K] row-major codes (rows_total a multiple of 16)
+    uint8_t *dst;        // [rows_total / 16][chunks][2 KiB]
+    int64_t pieces;      // 16-byte pieces of dst
+    int K, nch;
+};
+
+__global__ __launch_bounds__(256) void pack_mx_kernel(PackMxParams p) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < p.pieces; i += (int64_t)gridDim.x * 256) {
+        const int64_t grp = i / ((int64_t)p.nch * 128);
+        const int rem = (int)(i - grp * p.nch * 128);
+        const int c = rem >> 7, q = (rem >> 6) & 1, lane = rem & 63;
+        const int64_t row = grp * 16 + (lane & 15);
+        const int k = 128 * c + 32 * (lane >> 4) + 16 * q;  // K is a multiple of 32: a piece is all in or all out
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (k < p.K) v = *reinterpret_cast<const u32x4 *>(p.src + row * p.K + k);
+        *reinterpret_cast<u32x4 *>(p.dst + i * 16) = v;
+    }
+}
+
 struct PackWParams {
     const uint16_t *src;  // [E', rows_src, K] row-major
     uint16_t *dst;        // [E'][G][nslab] blocks

@@ -30,7 +30,8 @@ STAGES = ("route", "align", "shrink13", "gate_up", "shrink2", "down", "combine")
 
 EXPORTED = ("moe_lora_plan_query", "moe_lora_workspace_bytes", "moe_lora_check_args", "moe_lora_route",
             "moe_lora_align", "moe_lora_forward", "moe_lora_packed_weight_bytes", "moe_lora_pack_weights",
-            "moe_lora_strerror", "moe_lora_check_inputs")
+            "moe_lora_strerror", "moe_lora_check_inputs",
+            "moe_lora_packed_mxfp8_bytes", "moe_lora_pack_mxfp8_weights")
 
 
 class MoeLoraDims(ctypes.Structure):
@@ -96,6 +97,10 @@ def lib():
     L.moe_lora_packed_weight_bytes.restype = ctypes.c_size_t
     L.moe_lora_pack_weights.argtypes = [P(MoeLoraDims), vp, vp, vp, vp, vp]
     L.moe_lora_pack_weights.restype = ctypes.c_int
+    L.moe_lora_packed_mxfp8_bytes.argtypes = [P(MoeLoraDims), ctypes.c_int]
+    L.moe_lora_packed_mxfp8_bytes.restype = ctypes.c_size_t
+    L.moe_lora_pack_mxfp8_weights.argtypes = [P(MoeLoraDims), vp, vp, vp, vp, vp]
+    L.moe_lora_pack_mxfp8_weights.restype = ctypes.c_int
     L.moe_lora_check_inputs.argtypes = [P(MoeLoraDims), P(MoeLoraArgs), vp, vp]
     L.moe_lora_check_inputs.restype = ctypes.c_int
     L.moe_lora_strerror.argtypes = [ctypes.c_int]
@@ -193,6 +198,11 @@ def moe_lora_align(topk_ids: torch.Tensor, adapter_ids: Optional[torch.Tensor], 
                 lora_items=items[:plan["max_items"]], num_items=nitems, plan=plan)
 
 
+def moe_lora_packed_mxfp8_bytes(dims: MoeLoraDims, which: int) -> int:
+    """Bytes of the packed MXFP8 codes of w13 (which=0) or w2 (which=1); 0 if none."""
+    return int(lib().moe_lora_packed_mxfp8_bytes(ctypes.byref(dims), int(which)))
+
+
 def moe_lora_packed_weight_bytes(dims: MoeLoraDims, which: int) -> int:
     """Bytes of the packed w13 (which=0) or w2 (which=1); 0 if unsupported."""
     return int(lib().moe_lora_packed_weight_bytes(ctypes.byref(dims), int(which)))
@@ -259,6 +269,26 @@ class Mxfp8Weights:
         self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
         self.Ep, self.I, self.H = Ep, I, H
         self.device = w13.device
+        self.packed = False
+
+    def pack(self) -> "Mxfp8Weights":
+        """A copy whose codes are in the packed order of
+        moe_lora_pack_mxfp8_weights (same scales, bit-identical results)."""
+        dims = make_dims(1, self.H, self.I, self.Ep, 1)
+        n13, n2 = moe_lora_packed_mxfp8_bytes(dims, 0), moe_lora_packed_mxfp8_bytes(dims, 1)
+        if not n13 or not n2:
+            raise ValueError("no packed MXFP8 form for this shape")
+        p13 = torch.empty(n13, dtype=torch.uint8, device=self.device)
+        p2 = torch.empty(n2, dtype=torch.uint8, device=self.device)
+        with torch.cuda.device(self.device):
+            rc = lib().moe_lora_pack_mxfp8_weights(ctypes.byref(dims), _ptr(self.w13), _ptr(self.w2), _ptr(p13),
+                                                   _ptr(p2), _stream(self.device))
+        if rc != MOE_LORA_OK:
+            raise MoeLoraError(rc, "moe_lora_pack_mxfp8_weights")
+        out = Mxfp8Weights.__new__(Mxfp8Weights)
+        out.w13, out.w13_scale, out.w2, out.w2_scale = p13, self.w13_scale, p2, self.w2_scale
+        out.Ep, out.I, out.H, out.device, out.packed = self.Ep, self.I, self.H, self.device, True
+        return out
 
 
 def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optional[torch.Tensor],
@@ -363,7 +393,7 @@ def _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K, S, rsf,
                        ids_out.data_ptr() if ids_out is not None else None,
                        w_out.data_ptr() if w_out is not None else None,
                        ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None,
-                       1 if packed else 0, 1 if mx else 0,
+                       1 if packed or (mx and w13.packed) else 0, 1 if mx else 0,
                        w13.w13_scale.data_ptr() if mx else None, w13.w2_scale.data_ptr() if mx else None)
     return dims, args, out, ws
 

@@ -140,9 +140,9 @@ def test_check_args_mxfp8_flag():
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, w13_scale=0xb000)) == ml.MOE_LORA_EINVAL
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, w13_scale=0xb004, w2_scale=0xc000)) == ml.MOE_LORA_EINVAL
     assert ml.moe_lora_check_args(_dims(H=8224), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
-    # bf16 only, not with packed weights, H and I multiples of 32, streaming GEMM only
+    # bf16 only, H and I multiples of 32, streaming GEMM only; packed codes allowed
     assert ml.moe_lora_check_args(_dims(dtype="f32"), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
-    assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, weights_packed=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
+    assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, weights_packed=1, **sc)) == ml.MOE_LORA_OK
     assert ml.moe_lora_check_args(_dims(H=2888), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
     assert ml.moe_lora_check_args(_dims(I=2888), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
     big = _dims(T=4096, L=32, r=32)
@@ -193,3 +193,26 @@ def test_check_inputs_rejects_without_device():
     assert L.moe_lora_check_inputs(ctypes.byref(d), ctypes.byref(_args(workspace_bytes=need - 1)), st, None) == \
         ml.MOE_LORA_EWORKSPACE
     assert L.moe_lora_check_inputs(ctypes.byref(d), ctypes.byref(_args()), None, None) == ml.MOE_LORA_EINVAL
+
+
+def test_packed_mxfp8_bytes_formula():
+    # one 2 KiB block per 16 rows and 128-wide chunk of the reduction
+    for (H, I, E, S) in ((2880, 2880, 32, 0), (64, 8192, 4, 1), (8192, 64, 128, 0), (96, 160, 5, 1)):
+        d = _dims(H=H, I=I, E=E, S=S, K=1)
+        Ep = E + S
+        assert mm.moe_lora_packed_mxfp8_bytes(d, 0) == Ep * (2 * I // 16) * -(-H // 128) * 2048
+        assert mm.moe_lora_packed_mxfp8_bytes(d, 1) == Ep * (H // 16) * -(-I // 128) * 2048
+        assert mm.moe_lora_packed_mxfp8_bytes(d, 2) == 0
+    assert mm.moe_lora_packed_mxfp8_bytes(_dims(H=2888), 0) == 0   # H not a multiple of 32
+
+
+def test_pack_mxfp8_rejects_without_device():
+    L = mm.lib()
+    d = _dims()
+    vp = ctypes.c_void_p
+    assert L.moe_lora_pack_mxfp8_weights(ctypes.byref(d), vp(0x1000), None, None, None, None) == ml.MOE_LORA_EINVAL
+    assert L.moe_lora_pack_mxfp8_weights(ctypes.byref(d), vp(0x1008), None, vp(0x2000), None, None) == \
+        ml.MOE_LORA_EINVAL
+    assert L.moe_lora_pack_mxfp8_weights(ctypes.byref(_dims(H=2888)), vp(0x1000), None, vp(0x2000), None,
+                                         None) == ml.MOE_LORA_EUNSUPPORTED
+    assert L.moe_lora_pack_mxfp8_weights(ctypes.byref(d), None, None, None, None, None) == ml.MOE_LORA_OK

@@ -90,3 +90,45 @@ def test_mxfp8_rejects_the_tiled_path():
     with pytest.raises(ml.MoeLoraError) as ei:
         ml.forward_inputs(inp, packed=mxw, block_m=128)
     assert ei.value.code == ml.MOE_LORA_EUNSUPPORTED
+
+
+def _pack_by_definition(codes: np.ndarray) -> np.ndarray:
+    """The packed code layout written out: per 16 rows and 128-wide chunk c,
+    byte 16*(64q + 16g + r) + i holds code 128c + 32g + 16q + i of row r."""
+    rows, K = codes.reshape(-1, codes.shape[-1]).shape
+    nch = -(-K // 128)
+    src = np.zeros((rows, nch * 128), np.uint8)
+    src[:, :K] = codes.reshape(rows, K)
+    out = src.reshape(rows // 16, 16, nch, 4, 2, 16)          # [grp][r][c][g][q][i]
+    return out.transpose(0, 2, 4, 3, 1, 5).reshape(-1)        # [grp][c][q][g][r][i]
+
+
+@pytest.mark.parametrize("c", CASES[:2] + CASES[5:], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_mxfp8_packed_codes_layout_and_forward(c):
+    """Packed codes match the layout by definition byte for byte, and the
+    forward over them equals the forward over the row-major codes bit for bit."""
+    c = dict(c)
+    bm = c.pop("block_m", 0)
+    shape = synth.LayerShape(**c)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=shape.T + 7)
+    say("mxfp8 packed", c, bm)
+    mxw, _, _ = _mx(inp)
+    pk = mxw.pack()
+    torch.cuda.synchronize()
+    assert np.array_equal(pk.w13.cpu().numpy(), _pack_by_definition(mxw.w13.cpu().numpy()))
+    assert np.array_equal(pk.w2.cpu().numpy(), _pack_by_definition(mxw.w2.cpu().numpy()))
+    a = ml.forward_inputs(inp, packed=mxw, block_m=bm).clone()
+    b = ml.forward_inputs(inp, packed=pk, block_m=bm)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_mxfp8_packed_gptoss_decode_full_size():
+    inp = inputs("gptoss_decode_T64", seed=0)
+    say("mxfp8 packed gptoss_decode_T64")
+    mxw, _, _ = _mx(inp)
+    pk = mxw.pack()
+    a = ml.forward_inputs(inp, packed=mxw).clone()
+    b = ml.forward_inputs(inp, packed=pk)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
