@@ -22,6 +22,8 @@ HIPCC_FLAGS = [
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    # an inline-asm statement that clobbers a reserved register fails the build
+    "-Werror=inline-asm",
 ]
 
 

@@ -123,9 +123,20 @@ __device__ __forceinline__ int lds_off(int row, int c) {
 // disjoint from the slab being filled.  The K loop orders these copies
 // itself (wait_vm_barrier); since loads retire in order for vmcnt, copies the
 // compiler does not know of only make its own vmcnt waits stricter.
+// M0 is a register the compiler reserves (it may hold a value of its own
+// across this statement), so the statement saves it in a scratch SGPR, sets
+// the LDS address, issues the copy (which reads M0 at issue) and restores
+// it: to the compiler M0 is unchanged.
 __device__ __forceinline__ void dma16(const void *g, __attribute__((address_space(3))) unsigned char *dst) {
     const uint32_t m0v = (uint32_t)(uintptr_t)dst;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g) : "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0v), "v"(g));
 }
 
 // Barrier for LDS data only: waits for this wave's LDS accesses, not for its
