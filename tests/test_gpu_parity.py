@@ -393,3 +393,86 @@ def test_separate_gate_up_slices_as_rank_2r(block_m):
     assert_close(out, ref, synth.BF16, "separate gate/up slices")
     _, rel = errs(out.double() - base.double(), ref - oracle.forward_inputs(inp, lora=False))
     assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"
+
+
+# ------------------------------------------------ heavy skewed (many adapters)
+
+def _adapter_cover_sample(adapter_ids: np.ndarray, ids: np.ndarray, hot: int, n_hot: int, n_adapters: int):
+    """Tokens for an element-by-element check: the first and last token,
+    `n_hot` tokens routed to expert `hot`, one token for each of the first
+    `n_adapters` adapter ids present (ascending) and two without an adapter."""
+    T = adapter_ids.shape[0]
+    pick = {0, T - 1}
+    hot_tok = np.nonzero((ids == hot).any(axis=1))[0]
+    pick.update(hot_tok[np.linspace(0, hot_tok.size - 1, n_hot).astype(int)].tolist())
+    for a in np.unique(adapter_ids)[:n_adapters + 1]:
+        toks = np.nonzero(adapter_ids == a)[0]
+        pick.update(toks[[0, -1]].tolist() if a < 0 else [int(toks[toks.size // 2])])
+    return np.array(sorted(pick))
+
+
+def test_heavy_skewed_full_size():
+    """heavy_skewed_T8192 (T=8192, H=4096, I=1536, 128 experts top-8 with a
+    Zipf-skewed router bias, 64 Zipf(1.1) adapters of rank 64, 10% of tokens
+    without LoRA) at full size with the packed weights the benchmark uses:
+    routing and alignment bit for bit over all 65536 pairs, the layer
+    element by element on tokens of the hottest expert and of 24 distinct
+    adapters, and the LoRA delta on those tokens."""
+    inp = inputs("heavy_skewed_T8192")
+    s = inp.shape
+    pw = ml.PackedWeights(inp.w13, inp.w2)
+    say("heavy_skewed_T8192 full size (packed weights)")
+    ids = torch.empty((s.T, s.Kp), dtype=torch.int32, device=DEV)
+    w = torch.empty((s.T, s.Kp), dtype=torch.float32, device=DEV)
+    out = ml.forward_inputs(inp, packed=pw, routing_out=(ids, w))
+    base = ml.forward_inputs(inp, packed=pw, lora=False)
+    torch.cuda.synchronize()
+    oids, ow = oracle.route(inp.logits.cpu().numpy(), s.K, s.S, s.rsf)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.array_equal(_bits(w), ow.view(np.int32))
+    dims = ml.make_dims(s.T, s.H, s.I, s.E, s.K, s.S, s.L, s.r, s.rsf)
+    g = ml.moe_lora_align(ids, inp.adapter_ids, dims)
+    torch.cuda.synchronize()
+    ad = inp.adapter_ids.cpu().numpy()
+    o = oracle.align(oids, ad, s.Ep, s.L, g["plan"]["block_m"], g["plan"]["lora_block_m"])
+    assert int(g["num_post_pad"].item()) == o["num_post_pad"]
+    assert np.array_equal(g["sorted_ids"].cpu().numpy(), o["sorted_ids"])
+    assert np.array_equal(g["block_expert"].cpu().numpy(), o["block_expert"])
+    assert int(g["num_items"].item()) == o["num_items"]
+    assert np.array_equal(g["lora_items"].cpu().numpy(), o["items"])
+    hot = int(np.argmax(np.bincount(oids.reshape(-1), minlength=s.Ep)))
+    tok = _adapter_cover_sample(ad, oids, hot, 16, 24)
+    assert np.unique(ad[tok][ad[tok] >= 0]).size >= 16 and (oids[tok] == hot).any(axis=1).sum() >= 16
+    del pw
+    host = inp.to("cpu")
+    ref = oracle.forward_inputs(host, tokens=tok)
+    sel = torch.from_numpy(tok).to(DEV)
+    assert_close(out[sel], ref, s.dtype, "heavy_skewed_T8192")
+    ref0 = oracle.forward_inputs(host, tokens=tok, lora=False)
+    _, rel = errs(out[sel].double() - base[sel].double(), ref - ref0)
+    assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"
+
+
+def test_heavy_skewed_reduced_all_tokens():
+    """The heavy workload's structure at a size the oracle checks on every
+    token: 2048 tokens, 32 experts top-8 with the Zipf router bias, 64
+    Zipf(1.1) adapters of rank 64 (10% without LoRA), 256-row token tiles.
+    Each tile then holds dozens of adapters, which drives the LoRA expand
+    over a long adapter list in both tiled GEMMs."""
+    shape = synth.LayerShape(T=2048, H=256, I=256, E=32, K=8, L=64, r=64)
+    inp = inputs(shape, synth.Recipe(adapters="zipf", none_frac=0.10, logits="zipf_bias"), seed=8)
+    say("heavy reduced, every token")
+    dims = ml.make_dims(shape.T, shape.H, shape.I, shape.E, shape.K, 0, shape.L, shape.r, block_m=256)
+    assert ml.moe_lora_plan_query(dims)["gemm_kind"] == 2
+    out = ml.forward_inputs(inp, block_m=256)
+    base = ml.forward_inputs(inp, lora=False, block_m=256)
+    torch.cuda.synchronize()
+    # the tiles really hold many adapters: adapters per expert group (upper bound of a tile's list)
+    oids, _ = oracle.route(inp.logits.cpu().numpy(), shape.K)
+    ad = np.repeat(inp.adapter_ids.cpu().numpy(), shape.K)
+    per_expert = [np.unique(ad[(oids.reshape(-1) == e) & (ad >= 0)]).size for e in range(shape.E)]
+    assert max(per_expert) >= 40
+    ref = oracle.forward_inputs(inp)
+    assert_close(out, ref, shape.dtype, "heavy reduced")
+    _, rel = errs(out.double() - base.double(), ref - oracle.forward_inputs(inp, lora=False))
+    assert rel <= LORA_DELTA_RELL2, f"LoRA delta rel-L2 {rel:.3e}"
