@@ -11,6 +11,9 @@ passed as their raw 16-bit patterns and widened exactly inside the C code.
 Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
   route    pinned: brute-force sort on tiny inputs, library top-k/softmax,
            printed shared-slot layout, closed-form hand example
+  route_bias  pinned: brute-force sort of fp64 keys on tiny inputs, library
+           sigmoid/softmax + top-k, zero-bias reductions to the plain
+           router, forced choice by a dominant bias, bias-free weights
   align    pinned: brute-force stable sort, counting invariants
   forward  pinned: dense all-experts brute force, plain SwiGLU MLP special
            case, merged-LoRA closed form, shared-slot identity, hand example
@@ -62,7 +65,9 @@ def _load():
     lib.oracle_align.argtypes = [i64, i64, i64, i64, i64, i64, vp, vp, vp, i64, vp, i64, vp, vp,
                                  i64, vp]
     lib.oracle_align.restype = i32
-    lib.oracle_forward.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, f32, i32, i32,
+    lib.oracle_route_bias.argtypes = [i64, i64, i64, i64, f32, i32, i32, vp, vp, vp, vp]
+    lib.oracle_route_bias.restype = i32
+    lib.oracle_forward.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp,
                                    vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i32]
     lib.oracle_forward.restype = i32
     lib.oracle_mxfp8_decode.argtypes = [i64, i64, vp, vp, vp]
@@ -114,6 +119,29 @@ def route(logits, K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1):
     return ids, w
 
 
+SCORING = {None: -1, "softmax": 0, "sigmoid": 1}
+
+
+def route_bias(logits, K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1, scoring: str = "sigmoid",
+               bias=None):
+    """Biased top-K routing: fp64 scores (sigmoid, or softmax over all E),
+    choice by score + bias, weights from the unbiased scores of the chosen
+    experts (renormalized over them when renormalize=1), S shared slots
+    appended.  -> (ids int32 [T, K+S], weights f32 [T, K+S])."""
+    lg = _np(logits, np.float32)
+    T, E = lg.shape
+    b = None if bias is None else _np(bias, np.float32)
+    if b is not None and b.shape != (E,):
+        raise ValueError("bias must have one fp32 value per routed expert")
+    ids = np.empty((T, K + S), np.int32)
+    w = np.empty((T, K + S), np.float32)
+    rc = _load().oracle_route_bias(T, E, K, S, float(rsf), int(renormalize), SCORING[scoring], _ptr(lg), _ptr(b),
+                                   _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError(f"oracle_route_bias failed: {rc}")
+    return ids, w
+
+
 def max_blocks(P: int, Ep: int, bm: int) -> int:
     return int(_load().oracle_max_blocks(P, Ep, bm))
 
@@ -146,8 +174,12 @@ def align(topk_ids, adapter_ids, Ep: int, La: int, bm: int, lbm: int):
 
 
 def forward(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K: int, S: int = 0,
-            rsf: float = 1.0, renormalize: int = 1, tokens=None, nthreads: int = 0):
+            rsf: float = 1.0, renormalize: int = 1, tokens=None, nthreads: int = 0, scoring=None,
+            bias=None):
     """Layer output in fp64, rows for `tokens` (all tokens if None).
+
+    scoring=None routes with the plain router (route); "softmax" or
+    "sigmoid" with the biased router (route_bias), `bias` [E] fp32 or None.
 
     x [T,H], w13 [E+S,2I,H], w2 [E+S,H,I] and the LoRA stacks
     a13 [L,E+S,r,H], b13 [L,E+S,2I,r], a2 [L,E+S,r,I], b2 [L,E+S,H,r] are all
@@ -179,8 +211,11 @@ def forward(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K: int, S: int
         tk = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
         ntok = tk.shape[0]
     out = np.zeros((ntok, H), np.float64)
-    rc = _load().oracle_forward(T, H, I, E, K, S, L, r, float(rsf), int(renormalize), dt,
-                                _ptr(xa), _ptr(lg), _ptr(ad), _ptr(w13a), _ptr(w2a), _ptr(a13a),
+    b = None if bias is None else _np(bias, np.float32)
+    if scoring is None and b is not None:
+        raise ValueError("a bias needs scoring='softmax' or 'sigmoid'")
+    rc = _load().oracle_forward(T, H, I, E, K, S, L, r, float(rsf), int(renormalize), dt, SCORING[scoring],
+                                _ptr(b), _ptr(xa), _ptr(lg), _ptr(ad), _ptr(w13a), _ptr(w2a), _ptr(a13a),
                                 _ptr(b13a), _ptr(a2a), _ptr(b2a), _ptr(tk), ntok, _ptr(out),
                                 int(nthreads))
     if rc != 0:
@@ -188,7 +223,7 @@ def forward(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K: int, S: int
     return out
 
 
-def forward_inputs(inp, tokens=None, lora: bool = True, nthreads: int = 0):
+def forward_inputs(inp, tokens=None, lora: bool = True, nthreads: int = 0, scoring=None, bias=None):
     """oracle.forward over a synth.LayerInputs bundle."""
     s = inp.shape
     use = lora and s.lora
@@ -196,7 +231,7 @@ def forward_inputs(inp, tokens=None, lora: bool = True, nthreads: int = 0):
                    inp.a13 if use else None, inp.b13 if use else None,
                    inp.a2 if use else None, inp.b2 if use else None,
                    K=s.K, S=s.S, rsf=s.rsf, renormalize=s.renormalize, tokens=tokens,
-                   nthreads=nthreads)
+                   nthreads=nthreads, scoring=scoring, bias=bias)
 
 
 def mxfp8_decode(codes, scales) -> np.ndarray:

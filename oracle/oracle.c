@@ -18,6 +18,9 @@
  *          shared ids start at the routed expert count and every shared slot
  *          carries one constant weight; "lessons" item 2: that weight is
  *          1/routed_scaling_factor.)
+ *  route (biased variant) sigmoid or full-softmax expert scores in fp64, a
+ *          per-expert bias added for the choice only, the weights taken from
+ *          the unbiased scores of the chosen experts (route_token_bias).
  *  align   stable counting sort of the (token, slot) pairs by expert, the
  *          expert count being the number of stacked w13 rows (same analysis,
  *          "code analysis" part 2), each expert group padded to a multiple of
@@ -114,6 +117,92 @@ static void route_token(const float *l, int64_t E, int64_t K, int64_t S, float r
         w[K + q] = 1.0f / rsf;
     }
     (void)Kp;
+}
+
+/* Biased router (the router module named in the PR 46545 analysis, "code
+ * analysis" part 1, is a top-k router with a bias; the page does not define
+ * it, and the reading taken is the plainest one that keeps the routing
+ * weights meaningful):
+ *   score  s_e = 1 / (1 + exp(-l_e))                      scoring = sigmoid
+ *          s_e = exp(l_e - m) / sum_e' exp(l_e' - m)       scoring = softmax
+ *          (m the largest logit, the sum in expert index order)
+ *   key    k_e = s_e + b_e    (b the per-expert bias, 0 when absent)
+ *   choose K experts by repeated "largest key not yet taken, lower expert
+ *          index on an exact tie"; slot order = selection order
+ *   weight w_j = s_j / sum_{j' < K} s_j'   (renormalize = 1, slot order)
+ *          w_j = s_j                       (renormalize = 0)
+ * The bias steers the choice only; the weights use the unbiased scores.
+ * Everything is fp64; each weight is rounded once to fp32.  Shared slots
+ * are appended as in route_token. */
+static void route_token_bias(const float *l, const float *bias, int64_t E, int64_t K, int64_t S, float rsf,
+                             int renorm, int scoring, int32_t *ids, float *w, unsigned char *taken,
+                             double *score)
+{
+    double den = 1.0, m = 0.0;
+    if (scoring == 0) {
+        m = (double)l[0];
+        for (int64_t e = 1; e < E; ++e)
+            if ((double)l[e] > m)
+                m = (double)l[e];
+        den = 0.0;
+        for (int64_t e = 0; e < E; ++e)
+            den += exp((double)l[e] - m);
+    }
+    for (int64_t e = 0; e < E; ++e)
+        score[e] = scoring == 0 ? exp((double)l[e] - m) / den : 1.0 / (1.0 + exp(-(double)l[e]));
+    memset(taken, 0, (size_t)E);
+    for (int64_t j = 0; j < K; ++j) {
+        int64_t best = -1;
+        double bk = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            if (taken[e])
+                continue;
+            double k = score[e] + (bias ? (double)bias[e] : 0.0);
+            if (best < 0 || k > bk) {
+                best = e;
+                bk = k;
+            }
+        }
+        taken[best] = 1;
+        ids[j] = (int32_t)best;
+    }
+    double s = 0.0;
+    for (int64_t j = 0; j < K; ++j)
+        s += score[ids[j]];
+    for (int64_t j = 0; j < K; ++j)
+        w[j] = (float)(renorm ? score[ids[j]] / s : score[ids[j]]);
+    for (int64_t q = 0; q < S; ++q) {
+        ids[K + q] = (int32_t)(E + q);
+        w[K + q] = 1.0f / rsf;
+    }
+}
+
+/* scoring: -1 = the plain router (route_token; bias must be NULL), 0 =
+ * softmax scores, 1 = sigmoid scores (route_token_bias; bias may be NULL). */
+int oracle_route_bias(int64_t T, int64_t E, int64_t K, int64_t S, float rsf, int renorm, int scoring,
+                      const float *logits, const float *bias, int32_t *topk_ids, float *topk_w)
+{
+    if (T < 0 || E <= 0 || K <= 0 || K > E || S < 0 || scoring < -1 || scoring > 1 ||
+        (scoring < 0 && bias != NULL))
+        return -1;
+    unsigned char *taken = (unsigned char *)malloc((size_t)E);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(E > K ? E : K));
+    if (!taken || !sc) {
+        free(taken);
+        free(sc);
+        return -2;
+    }
+    int64_t Kp = K + S;
+    for (int64_t t = 0; t < T; ++t) {
+        if (scoring < 0)
+            route_token(logits + t * E, E, K, S, rsf, renorm, topk_ids + t * Kp, topk_w + t * Kp, taken, sc);
+        else
+            route_token_bias(logits + t * E, bias, E, K, S, rsf, renorm, scoring, topk_ids + t * Kp,
+                             topk_w + t * Kp, taken, sc);
+    }
+    free(taken);
+    free(sc);
+    return 0;
 }
 
 int oracle_route(int64_t T, int64_t E, int64_t K, int64_t S, float rsf, int renorm,
@@ -324,16 +413,19 @@ static void expert_mlp(int64_t H, int64_t I, int64_t Ep, int64_t r, int dtype,
 /* Full layer output for the tokens listed in `tokens` (all T when tokens is
  * NULL), written as fp64 rows of `out` in list order.  LoRA is applied when
  * L > 0, r > 0 and adapter_ids is non-NULL; adapter -1 means no LoRA.
- * Routing is recomputed here from the logits (same rule as oracle_route).
+ * Routing is recomputed here from the logits: the plain router for
+ * scoring = -1 (bias NULL), else the biased router of oracle_route_bias.
  * nthreads <= 0 uses the OpenMP default. */
 int oracle_forward(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, int64_t S,
-                   int64_t L, int64_t r, float rsf, int renorm, int dtype,
+                   int64_t L, int64_t r, float rsf, int renorm, int dtype, int scoring,
+                   const float *bias,
                    const void *x, const float *logits, const int32_t *adapter_ids,
                    const void *w13, const void *w2, const void *a13, const void *b13,
                    const void *a2, const void *b2,
                    const int64_t *tokens, int64_t ntok, double *out, int nthreads)
 {
-    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E || S < 0 || rsf <= 0.0f)
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || K > E || S < 0 || rsf <= 0.0f ||
+        scoring < -1 || scoring > 1 || (scoring < 0 && bias != NULL))
         return -1;
     int lora = (L > 0 && r > 0 && adapter_ids != NULL && a13 && b13 && a2 && b2);
     int64_t Ep = E + S, Kp = K + S;
@@ -353,7 +445,7 @@ int oracle_forward(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, int64_
         double *hv = (double *)malloc(sizeof(double) * (size_t)I);
         double *uv = (double *)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
         double *y = (double *)malloc(sizeof(double) * (size_t)H);
-        double *ex = (double *)malloc(sizeof(double) * (size_t)K);
+        double *ex = (double *)malloc(sizeof(double) * (size_t)(E > K ? E : K));
         unsigned char *taken = (unsigned char *)malloc((size_t)E);
         int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)Kp);
         float *w = (float *)malloc(sizeof(float) * (size_t)Kp);
@@ -374,7 +466,10 @@ int oracle_forward(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, int64_
                     xv[hh] = ld(x, t * H + hh, dtype);
                     o[hh] = 0.0;
                 }
-                route_token(logits + t * E, E, K, S, rsf, renorm, ids, w, taken, ex);
+                if (scoring < 0)
+                    route_token(logits + t * E, E, K, S, rsf, renorm, ids, w, taken, ex);
+                else
+                    route_token_bias(logits + t * E, bias, E, K, S, rsf, renorm, scoring, ids, w, taken, ex);
                 int64_t a = lora ? adapter_ids[t] : -1;
                 if (a < -1 || a >= L) {
 #pragma omp atomic write

@@ -2,7 +2,8 @@
 
 These are written differently from the oracle on purpose:
   * routing sorts every logit with Python's sort by (-value, index) and takes
-    the softmax with scipy;
+    the softmax with scipy (the biased router: scipy's expit/softmax scores,
+    the same sort on score + bias);
   * alignment is a Python stable sort of the pair list by its key;
   * the layer computes EVERY expert for EVERY token densely (numpy einsum in
     fp64) and combines them through a dense [T, E'] gate matrix, so a wrong
@@ -35,6 +36,29 @@ def route(logits, K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1):
         else:
             p = softmax(lg[t])[order]
         w[t, :K] = p.astype(np.float32)
+        for q in range(S):
+            ids[t, K + q] = E + q
+            w[t, K + q] = np.float32(1.0) / np.float32(rsf)
+    return ids, w
+
+
+def route_bias(logits, K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1, scoring: str = "sigmoid",
+               bias=None):
+    """Biased router written with library routines: scipy's expit / softmax
+    for the fp64 scores, Python's sort by (-(score + bias), index) for the
+    choice, weights from the unbiased scores."""
+    from scipy.special import expit
+    lg = np.asarray(to_f64(logits), dtype=np.float64)
+    T, E = lg.shape
+    b = np.zeros(E) if bias is None else np.asarray(bias, dtype=np.float32).astype(np.float64)
+    ids = np.zeros((T, K + S), np.int32)
+    w = np.zeros((T, K + S), np.float32)
+    for t in range(T):
+        sc = expit(lg[t]) if scoring == "sigmoid" else softmax(lg[t])
+        order = sorted(range(E), key=lambda e: (-(float(sc[e]) + float(b[e])), e))[:K]
+        ids[t, :K] = order
+        sel = sc[order]
+        w[t, :K] = (sel / sel.sum() if renormalize else sel).astype(np.float32)
         for q in range(S):
             ids[t, K + q] = E + q
             w[t, K + q] = np.float32(1.0) / np.float32(rsf)

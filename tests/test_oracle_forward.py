@@ -190,3 +190,21 @@ def test_separate_gate_up_lora_as_rank_2r():
     ids, w = bf.route(inp.logits.numpy(), s.K)
     ref = bf.layer_dense(inp.x, W13m, W2m, bf.gate_matrix(ids, w, s.Ep), rsf=s.rsf)
     assert _rel(out, ref) < 1e-12
+
+
+@pytest.mark.parametrize("scoring", ["sigmoid", "softmax"])
+def test_forward_biased_router_vs_dense_bruteforce(scoring):
+    """The layer with the biased router (the router module the PR 46545
+    analysis names, read as in oracle.route_bias): the oracle's forward
+    against the dense brute force gated by the brute-force biased routing."""
+    inp = _small(T=10, H=24, I=20, E=6, K=3, S=1, L=3, r=4, rsf=2.5, dtype=synth.BF16)
+    s = inp.shape
+    bias = np.array([0.3, -0.2, 0.0, 0.5, -0.4, 0.1], np.float32)
+    out = oracle.forward_inputs(inp, scoring=scoring, bias=bias)
+    ids, w = bf.route_bias(inp.logits.numpy(), s.K, s.S, s.rsf, 1, scoring, bias)
+    G = bf.gate_matrix(ids, w, s.Ep)
+    ref = bf.layer_dense(inp.x, inp.w13, inp.w2, G, inp.adapter_ids.numpy(), inp.a13, inp.b13,
+                         inp.a2, inp.b2, rsf=s.rsf)
+    assert _rel(out, ref) < 1e-12
+    # the bias changes the routing of some tokens here, so the output differs from the plain router's
+    assert _rel(out, oracle.forward_inputs(inp)) > 1e-3
