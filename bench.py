@@ -192,17 +192,20 @@ MALL_FLUSH_BYTES = 512 << 20   # > 2x the 256 MB MALL
 def per_iteration(call, steps: int, warmup: int, flush_bytes: int = 0) -> dict:
     """Time `call` `steps` times, each between its own pair of HIP events on
     the current stream; with flush_bytes, a scratch buffer of that size is
-    written between iterations (outside the events) so that a small
-    footprint cannot stay resident in the MALL.  Returns mean, median, p10
-    and p90 in ms."""
-    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    read between iterations (outside the events) so that a small footprint
+    cannot stay resident in the MALL.  The flush only reads (a sum over the
+    buffer, written once beforehand): a flush that writes would leave the
+    MALL full of dirty lines whose write-back then lands inside the next
+    timed call.  Returns mean, median, p10 and p90 in ms."""
+    scratch = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda") if flush_bytes else None
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
         if scratch is not None:
-            scratch.fill_(1)
+            torch.sum(scratch, dim=0, out=sink)
         a.record()
         call()
         b.record()
@@ -370,7 +373,12 @@ def cpu_baseline(m: dict, budget_tokens: int, min_wall_s: float = 10.0, max_reps
     host = m["inp"].to("cpu")
     n = min(s.T, budget_tokens)
     tokens = np.arange(n)
-    threads = min(os.cpu_count() or 1, 16)
+    # every CPU thread this process may use (its affinity set), unless the
+    # host's OpenMP setting gives it a smaller share (16 threads per GPU on
+    # the measurement hosts)
+    host_cpus = len(os.sched_getaffinity(0))
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(host_cpus, omp) if omp > 0 else host_cpus
     reps, wall = 0, 0.0
     while reps < max_reps and (reps == 0 or wall < min_wall_s):
         t0 = time.perf_counter()
@@ -379,7 +387,18 @@ def cpu_baseline(m: dict, budget_tokens: int, min_wall_s: float = 10.0, max_reps
         reps += 1
     return {"value": n * reps / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {s.T} tokens of one {m['name']} layer call, {reps} repetitions "
-                      f"(fp64 oracle, OpenMP)", "wall_s": wall}
+                      f"(fp64 oracle, OpenMP)", "wall_s": wall, "host_cpus": host_cpus,
+            "omp_num_threads": omp or None, "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_calibration(mib: int, reps: int) -> None:

@@ -93,6 +93,17 @@ extern "C" {
  *      to 32 rows and cut into tiles of at most block_m rows
  *   lora_block_m  rows per LoRA shrink work item; 0 = library choice, else
  *      16 or 32 (32 needs r <= 64)
+ *   router  MOE_LORA_ROUTER_TOPK (0): top-K of the logits, weights as under
+ *      renormalize.  MOE_LORA_ROUTER_BIAS_SOFTMAX (1) / _SIGMOID (2): the
+ *      biased top-k router.  The PR 46545 analysis ("code analysis" part 1)
+ *      names a biased top-k router module without defining it; the reading
+ *      implemented: fp64 score s_e per expert (softmax over all E logits,
+ *      or the sigmoid of the logit), the K experts with the largest
+ *      s_e + bias_e chosen (lower index on an exact tie, slot order =
+ *      choice order), weights = the unbiased scores of the chosen experts,
+ *      divided by their slot-order sum when renormalize = 1, rounded once
+ *      to fp32.  The bias (moe_lora_args.expert_bias, may be NULL = 0)
+ *      steers the choice only
  *   split_k  K-splits of the LoRA shrink; 0 = library choice, else 1..16.
  *      Applies to the streaming GEMM only: with the LDS-tiled GEMM the
  *      shrink runs unsplit (the plan reports 1).  With 0 on the streaming
@@ -108,7 +119,12 @@ typedef struct moe_lora_dims {
     int32_t block_m;
     int32_t lora_block_m;
     int32_t split_k;
+    int32_t router;
 } moe_lora_dims;
+
+#define MOE_LORA_ROUTER_TOPK 0
+#define MOE_LORA_ROUTER_BIAS_SOFTMAX 1
+#define MOE_LORA_ROUTER_BIAS_SIGMOID 2
 
 /* What the library will do for a given moe_lora_dims (filled by
  * moe_lora_plan_query).  block_m / lora_block_m / max_blocks /
@@ -161,7 +177,14 @@ typedef struct moe_lora_plan {
  *     H and I multiples of 32 and at most 8192, and the streaming GEMM
  *     (plan gemm_kind 1; for many rows per expert pass block_m 16 or 32),
  *     else MOE_LORA_EUNSUPPORTED; NULL or misaligned scales give
- *     MOE_LORA_EINVAL. */
+ *     MOE_LORA_EINVAL.
+ *   expert_bias [E] f32: the per-expert bias of the biased router
+ *     (dims.router 1 or 2; NULL = all zero); must be NULL with router 0.
+ *   sorted_ids_out [sorted_capacity], block_expert_out [max_blocks],
+ *     num_post_pad_out [1] (i32, sizes from moe_lora_plan_query, 4-byte
+ *     aligned): optional (NULL = kept in the workspace) outputs of the
+ *     alignment step, in the layout moe_lora_align documents; the layer
+ *     then uses these buffers in place of its workspace copies. */
 typedef struct moe_lora_args {
     const void *hidden;
     const float *router_logits;
@@ -182,6 +205,10 @@ typedef struct moe_lora_args {
     int32_t weights_mxfp8;
     const void *w13_scale;
     const void *w2_scale;
+    const float *expert_bias;
+    int32_t *sorted_ids_out;
+    int32_t *block_expert_out;
+    int32_t *num_post_pad_out;
 } moe_lora_args;
 
 /* Validate dims and describe the plan.  Pure host code: touches no device
@@ -199,15 +226,27 @@ size_t moe_lora_workspace_bytes(const moe_lora_dims *dims);
 int moe_lora_check_args(const moe_lora_dims *dims, const moe_lora_args *args);
 
 /* Step 1 alone: top-K routing plus shared-slot append.
- *   logits [T,E] f32 in; topk_ids [T,K+S] i32 and topk_weights [T,K+S] f32
- *   out.  Selection order: larger logit first, lower expert index on an
- *   exact tie (+0 == -0); slot order = selection order.  Weights: fp64
- *   softmax rounded once to fp32.  Only T, E, K, S, routed_scaling_factor
- *   and renormalize of `dims` are read. */
-int moe_lora_route(const moe_lora_dims *dims, const float *logits, int32_t *topk_ids,
-                   float *topk_weights, void *stream);
+ *   logits [T,E] f32 in; expert_bias [E] f32 in (biased router only, may be
+ *   NULL; must be NULL with router 0); topk_ids [T,K+S] i32 and
+ *   topk_weights [T,K+S] f32 out.  Router 0: larger logit first, lower
+ *   expert index on an exact tie (+0 == -0); slot order = selection order;
+ *   weights: fp64 softmax rounded once to fp32.  Routers 1 and 2: see
+ *   moe_lora_dims.router.  Only T, E, K, S, routed_scaling_factor,
+ *   renormalize and router of `dims` are read. */
+int moe_lora_route(const moe_lora_dims *dims, const float *logits, const float *expert_bias,
+                   int32_t *topk_ids, float *topk_weights, void *stream);
 
 /* Step 2 alone: alignment of the pairs f = t*(K+S) + j by expert.
+ * The pages fix only the expert count (the number of stacked w13 rows, PR
+ * 46545 analysis, "code analysis" part 2); the order inside an expert, the
+ * padding and the LoRA work list are this library's layout, chosen so that
+ * one sorted list serves the base GEMM (contiguous, padded expert groups)
+ * and the LoRA shrink/expand (contiguous (adapter, expert) runs) at once.
+ * In particular there are no separate LoRA-sorted arrays (a second sorted
+ * id list, block adapter/expert maps and padded count per LoRA block): the
+ * (adapter, expert) runs inside sorted_ids, listed by lora_items, take their
+ * place.  moe_lora_forward can write the same sorted_ids, block_expert and
+ * num_post_pad to caller buffers (moe_lora_args.*_out).
  *   topk_ids [T,K+S] i32 in (values in [0, E+S)); adapter_ids [T] i32 in
  *   (ignored when LoRA is inactive).
  *   sorted_ids [sorted_capacity]: pairs of expert 0, then expert 1, ...;
@@ -234,7 +273,8 @@ int moe_lora_forward(const moe_lora_dims *dims, const moe_lora_args *args, void 
  * device, for debugging a caller.  The logits feed the top-k softmax of step
  * 1 and each adapter id picks one of the L adapters (or none) of step 3
  * (sources above); the MXFP8 conditions are those of the weight format
- * under moe_lora_args.weights_mxfp8.  Checked: every router logit finite; with LoRA
+ * under moe_lora_args.weights_mxfp8.  Checked: every router logit (and
+ * every expert_bias value, when given) finite (MOE_LORA_BAD_LOGIT); with LoRA
  * active every adapter id in [-1, L); with weights_mxfp8 every scale byte in
  * [1, 254] and no NaN code (0x7F, 0xFF).  Reads the same `args` as
  * moe_lora_forward (only router_logits, adapter_ids, w13, w2 and the scale

@@ -50,6 +50,7 @@ struct AlignParams {
     int32_t *sorted_adapter;  // optional [cap]
     int32_t *block_expert;
     int32_t *npp_out;
+    int32_t *npp_copy = nullptr;  // optional second copy of the padded row count (a caller's buffer)
     int32_t *nitems_out;
     int32_t *items;
     int32_t *tmp;         // [P] global scratch (used when the keys do not fit in LDS)
@@ -260,6 +261,7 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
     }
     if (tid == 0) {
         *p.npp_out = npp;
+        if (p.npp_copy) *p.npp_copy = npp;
         *p.nitems_out = nitems;
     }
 }
@@ -684,6 +686,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p) {
     }
     if (tid == 0) {
         *p.npp_out = npp;
+        if (p.npp_copy) *p.npp_copy = npp;
         *p.nitems_out = nitems;
     }
 }

@@ -1,5 +1,6 @@
 // Check of the input preconditions that the layer itself does not check on
-// the device (moe_lora_check_inputs): router logits finite, adapter ids in
+// the device (moe_lora_check_inputs): router logits (and the biased
+// router's expert bias) finite, adapter ids in
 // [-1, L), and for MXFP8 weights scale bytes in [1, 254] (E8M0: 0xFF is NaN,
 // 0x00 the smallest power of two, outside the range the encoder writes) and
 // no NaN code (E4M3: S.1111.111).  Two launches, no atomics: every workgroup
@@ -18,6 +19,8 @@ constexpr int kCheckBlocks = 512;
 struct CheckParams {
     const float *logits;         // [n_logits] f32
     int64_t n_logits;
+    const float *bias = nullptr; // [n_bias] f32 (biased router) or null
+    int64_t n_bias = 0;
     const int32_t *adapter_ids;  // [n_adapters] or null
     int64_t n_adapters;
     int L;
@@ -48,6 +51,8 @@ __global__ __launch_bounds__(256) void check_inputs_kernel(CheckParams p) {
     int flag = 0;
     for (int64_t i = i0; i < p.n_logits; i += stride)
         if (!isfinite(p.logits[i])) flag |= MOE_LORA_BAD_LOGIT;
+    for (int64_t i = i0; i < p.n_bias; i += stride)
+        if (!isfinite(p.bias[i])) flag |= MOE_LORA_BAD_LOGIT;
     for (int64_t i = i0; i < p.n_adapters; i += stride) {
         const int a = p.adapter_ids[i];
         if (a < -1 || a >= p.L) flag |= MOE_LORA_BAD_ADAPTER;

@@ -83,6 +83,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
         return MOE_LORA_EINVAL;
     if (!(std::isfinite(d->routed_scaling_factor) && d->routed_scaling_factor > 0.0f)) return MOE_LORA_EINVAL;
     if (d->renormalize != 0 && d->renormalize != 1) return MOE_LORA_EINVAL;
+    if (d->router < MOE_LORA_ROUTER_TOPK || d->router > MOE_LORA_ROUTER_BIAS_SIGMOID) return MOE_LORA_EINVAL;
     if (d->dtype != MOE_LORA_F32 && d->dtype != MOE_LORA_BF16) return MOE_LORA_EUNSUPPORTED;
     if (d->E > 1024 || d->K > 64 || d->S > 64) return MOE_LORA_EUNSUPPORTED;
     if (d->H % 8 != 0 || d->I % 8 != 0) return MOE_LORA_EUNSUPPORTED;
@@ -242,8 +243,11 @@ void set_kernel_attributes() {
     }
 }
 
-RouteParams route_params(const moe_lora_dims *d, const float *logits, int32_t *ids, float *w) {
+RouteParams route_params(const moe_lora_dims *d, const float *logits, const float *bias, int32_t *ids,
+                         float *w) {
     RouteParams rp;
+    rp.scoring = d->router == MOE_LORA_ROUTER_TOPK ? -1 : (d->router == MOE_LORA_ROUTER_BIAS_SOFTMAX ? 0 : 1);
+    rp.bias = bias;
     rp.logits = logits;
     rp.T = (int)d->T;
     rp.E = (int)d->E;
@@ -267,7 +271,7 @@ void launch_route_shrink_vpl(const RouteParams &rp, const RowShrinkParams &sp, h
 // Router and gate_up shrink in one launch (plan.row_shrink): s13 by pair.
 void launch_route_shrink(const Plan &pl, const moe_lora_dims *d, const moe_lora_args *a, int32_t *ids, float *w,
                          float *s13, hipStream_t st) {
-    const RouteParams rp = route_params(d, a->router_logits, ids, w);
+    const RouteParams rp = route_params(d, a->router_logits, a->expert_bias, ids, w);
     RowShrinkParams sp{};
     sp.in = (const uint16_t *)a->hidden;
     sp.A = (const uint16_t *)a->a13;
@@ -287,8 +291,9 @@ void launch_route_shrink(const Plan &pl, const moe_lora_dims *d, const moe_lora_
     else launch_route_shrink_vpl<16>(rp, sp, st);
 }
 
-int launch_route(const moe_lora_dims *d, const float *logits, int32_t *ids, float *w, hipStream_t st) {
-    const RouteParams rp = route_params(d, logits, ids, w);
+int launch_route(const moe_lora_dims *d, const float *logits, const float *bias, int32_t *ids, float *w,
+                 hipStream_t st) {
+    const RouteParams rp = route_params(d, logits, bias, ids, w);
     const dim3 grid((unsigned)((rp.T + 3) / 4)), block(256);
     const int E = rp.E;
     if (E <= 64) hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, st, rp);
@@ -303,7 +308,7 @@ int launch_route(const moe_lora_dims *d, const float *logits, int32_t *ids, floa
 int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
                  int32_t *sorted, int32_t *sorted_adapter, int32_t *bexp, int32_t *npp, int32_t *items,
                  int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles,
-                 hipStream_t st) {
+                 hipStream_t st, int32_t *npp_copy = nullptr) {
     std::call_once(g_attr_once, set_kernel_attributes);
     if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
     AlignParams ap;
@@ -315,6 +320,7 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
     ap.sorted_adapter = sorted_adapter;
     ap.block_expert = bexp;
     ap.npp_out = npp;
+    ap.npp_copy = npp_copy;
     ap.nitems_out = nitems;
     ap.items = pl.lora ? items : nullptr;
     ap.tmp = tmp;
@@ -509,6 +515,10 @@ int moe_lora_check_args(const moe_lora_dims *d, const moe_lora_args *a) {
             if (!aligned(ptr, 16)) return MOE_LORA_EINVAL;
     }
     if (!aligned(a->workspace, 256)) return MOE_LORA_EINVAL;
+    if (a->expert_bias && d->router == MOE_LORA_ROUTER_TOPK) return MOE_LORA_EINVAL;
+    const void *outs[] = {a->sorted_ids_out, a->block_expert_out, a->num_post_pad_out, a->expert_bias};
+    for (const void *ptr : outs)
+        if (ptr && !aligned(ptr, 4)) return MOE_LORA_EINVAL;
     if (a->workspace_bytes < p.total) return MOE_LORA_EWORKSPACE;
     if (a->weights_packed != 0 && a->weights_packed != 1) return MOE_LORA_EINVAL;
     if (a->weights_packed && d->dtype != MOE_LORA_BF16) return MOE_LORA_EUNSUPPORTED;
@@ -623,6 +633,8 @@ int moe_lora_check_inputs(const moe_lora_dims *d, const moe_lora_args *a, int32_
         cp.partial = (int32_t *)a->workspace;
         cp.logits = a->router_logits;
         cp.n_logits = (int64_t)d->T * d->E;
+        cp.bias = a->expert_bias;
+        cp.n_bias = a->expert_bias ? d->E : 0;
         cp.adapter_ids = p.lora ? a->adapter_ids : nullptr;
         cp.n_adapters = p.lora ? d->T : 0;
         cp.L = (int)p.La;
@@ -645,17 +657,19 @@ int moe_lora_check_inputs(const moe_lora_dims *d, const moe_lora_args *a, int32_
     return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "check_inputs launch");
 }
 
-int moe_lora_route(const moe_lora_dims *d, const float *logits, int32_t *topk_ids, float *topk_weights,
-                   void *stream) {
+int moe_lora_route(const moe_lora_dims *d, const float *logits, const float *expert_bias, int32_t *topk_ids,
+                   float *topk_weights, void *stream) {
     if (!d) return MOE_LORA_EINVAL;
     if (d->T < 0 || d->E <= 0 || d->K <= 0 || d->K > d->E || d->S < 0) return MOE_LORA_EINVAL;
+    if (d->router < MOE_LORA_ROUTER_TOPK || d->router > MOE_LORA_ROUTER_BIAS_SIGMOID) return MOE_LORA_EINVAL;
+    if (expert_bias && d->router == MOE_LORA_ROUTER_TOPK) return MOE_LORA_EINVAL;
     if (d->E > 1024 || d->K > 64 || d->S > 64) return MOE_LORA_EUNSUPPORTED;
     if (!(std::isfinite(d->routed_scaling_factor) && d->routed_scaling_factor > 0.0f)) return MOE_LORA_EINVAL;
     if (d->renormalize != 0 && d->renormalize != 1) return MOE_LORA_EINVAL;
     if (d->T == 0) return MOE_LORA_OK;
     if (!logits || !topk_ids || !topk_weights) return MOE_LORA_EINVAL;
     hipStream_t st = (hipStream_t)stream;
-    launch_route(d, logits, topk_ids, topk_weights, st);
+    launch_route(d, logits, expert_bias, topk_ids, topk_weights, st);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "route launch");
 }
@@ -693,9 +707,10 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     char *ws = (char *)a->workspace;
     int32_t *ids = a->topk_ids_out ? a->topk_ids_out : (int32_t *)(ws + p.o_ids);
     float *wts = a->topk_weights_out ? a->topk_weights_out : (float *)(ws + p.o_w);
-    int32_t *sorted = (int32_t *)(ws + p.o_sorted);
+    // the alignment goes to the caller's buffers when they are given
+    int32_t *sorted = a->sorted_ids_out ? a->sorted_ids_out : (int32_t *)(ws + p.o_sorted);
     int32_t *sadp = (int32_t *)(ws + p.o_sadp);
-    int32_t *bexp = (int32_t *)(ws + p.o_bexp);
+    int32_t *bexp = a->block_expert_out ? a->block_expert_out : (int32_t *)(ws + p.o_bexp);
     int32_t *cnt = (int32_t *)(ws + p.o_cnt);
     int32_t *items = (int32_t *)(ws + p.o_items);
     int32_t *tmp = (int32_t *)(ws + p.o_tmp);
@@ -712,12 +727,12 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     int32_t *tiles = (int32_t *)(ws + p.o_tiles);
     mark(2 * MOE_LORA_STAGE_ROUTE);
     if (p.row_shrink) launch_route_shrink(p, d, a, ids, wts, s13, st);
-    else launch_route(d, a->router_logits, ids, wts, st);
+    else launch_route(d, a->router_logits, a->expert_bias, ids, wts, st);
     mark(2 * MOE_LORA_STAGE_ROUTE + 1);
     mark(2 * MOE_LORA_STAGE_ALIGN);
     int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt, items,
                           cnt + 1, tmp,
-                          p.kind == 2 ? tiles : nullptr, cnt + 2, st);
+                          p.kind == 2 ? tiles : nullptr, cnt + 2, st, a->num_post_pad_out);
     if (r2 != MOE_LORA_OK) return r2;
     // the tiled GEMM reads x gathered and packed per sorted row; with LoRA
     // the pack shares one launch with the gate_up shrink (stage SHRINK13)

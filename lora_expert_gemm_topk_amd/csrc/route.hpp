@@ -8,6 +8,16 @@
 // S shared slots follow with ids E..E+S-1 and the constant weight 1/rsf
 // (secrett2633 analysis of vLLM PR 46545, "code analysis" part 1 and
 // "lessons" item 2).
+//
+// Biased variant (the router module that analysis names in "code analysis"
+// part 1 is a top-k router with a bias; the page gives no formula, and the
+// reading implemented is): fp64 score s_e per expert, the sigmoid of the
+// logit or the softmax over all E logits (exp of logit minus the largest,
+// divided by the sum over experts in index order); the choice takes the K
+// largest keys s_e + b_e (b the per-expert fp32 bias, 0 when absent), lower
+// index on an exact tie; the weights are the unbiased scores of the chosen
+// experts, divided by their slot-order sum when renormalizing, rounded once
+// to fp32.  The bias steers the choice only.
 #pragma once
 
 #include "common.hpp"
@@ -21,17 +31,95 @@ struct RouteParams {
     int renorm;
     int32_t *ids;         // [T, K+S]
     float *wts;           // [T, K+S]
+    int scoring = -1;     // -1: plain top-k of the logits; 0: biased, softmax scores; 1: biased, sigmoid scores
+    const float *bias = nullptr;  // [E] (biased router only; nullptr = zero bias)
 };
 
-struct Cand {
-    float v;
+template <typename V>
+struct CandT {
+    V v;
     int i;  // expert index; INT_MAX = none
 };
+typedef CandT<float> Cand;
 
-__device__ __forceinline__ bool better(const Cand &a, const Cand &b) {
+template <typename V>
+__device__ __forceinline__ bool better(const CandT<V> &a, const CandT<V> &b) {
     if (b.i == 0x7fffffff) return a.i != 0x7fffffff;
     if (a.i == 0x7fffffff) return false;
     return a.v > b.v || (a.v == b.v && a.i < b.i);
+}
+
+// Biased router for token t (see the file comment): returns to lane j the
+// expert id of slot j like route_one_token.
+template <int VPL>
+__device__ int route_one_token_bias(const RouteParams &rp, int t, bool write) {
+    const int lane = lane_id();
+    const int E = rp.E, K = rp.K, S = rp.S;
+    const float *l = rp.logits + (int64_t)t * E;
+    double sc[VPL], key[VPL];
+    bool live[VPL];
+    double m = 0.0, den = 1.0;
+    if (rp.scoring == 0) {
+        // largest logit (exact), then the index-order sum every lane takes alike
+        float mx = -__builtin_huge_valf();
+        for (int e = 0; e < E; ++e) mx = fmaxf(mx, l[e]);
+        m = (double)mx;
+        den = 0.0;
+        for (int e = 0; e < E; ++e) den += exp((double)l[e] - m);
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int e = lane + 64 * j;
+        live[j] = e < E;
+        const double lv = live[j] ? (double)l[e] : 0.0;
+        sc[j] = rp.scoring == 0 ? exp(lv - m) / den : 1.0 / (1.0 + exp(-lv));
+        key[j] = sc[j] + ((live[j] && rp.bias) ? (double)rp.bias[e] : 0.0);
+    }
+    double mys = 0.0;
+    int myi = -1;
+    for (int s = 0; s < K; ++s) {
+        CandT<double> c{0.0, 0x7fffffff};
+        double cs = 0.0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            CandT<double> d{key[j], lane + 64 * j};
+            if (live[j] && better(d, c)) {
+                c = d;
+                cs = sc[j];
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            CandT<double> o{__shfl_xor(c.v, off, 64), __shfl_xor(c.i, off, 64)};
+            const double os = __shfl_xor(cs, off, 64);
+            if (better(o, c)) {
+                c = o;
+                cs = os;
+            }
+        }
+        if ((c.i & 63) == lane) {
+#pragma unroll
+            for (int j = 0; j < VPL; ++j)
+                if (j == (c.i >> 6)) live[j] = false;
+        }
+        if (lane == s) {
+            mys = cs;
+            myi = c.i;
+        }
+    }
+    double sum = 0.0;
+    for (int j = 0; j < K; ++j) sum += __shfl(mys, j, 64);
+    const int Kp = K + S;
+    if (write && lane < K) {
+        rp.ids[(int64_t)t * Kp + lane] = myi;
+        rp.wts[(int64_t)t * Kp + lane] = (float)(rp.renorm ? mys / sum : mys);
+    }
+    if (write && lane < S) {
+        rp.ids[(int64_t)t * Kp + K + lane] = E + lane;
+        rp.wts[(int64_t)t * Kp + K + lane] = rp.shared_w;
+    }
+    if (lane >= K) myi = (lane < Kp) ? E + (lane - K) : -1;
+    return myi;
 }
 
 // Route token t with the whole wavefront; writes ids and weights of its K+S
@@ -39,6 +127,7 @@ __device__ __forceinline__ bool better(const Cand &a, const Cand &b) {
 // slot j (-1 for j >= K+S; slots beyond lane 63 are written but not returned).
 template <int VPL>
 __device__ int route_one_token(const RouteParams &rp, int t, bool write = true) {
+    if (rp.scoring >= 0) return route_one_token_bias<VPL>(rp, t, write);
     const int lane = lane_id();
     const int E = rp.E, K = rp.K, S = rp.S;
     const float *l = rp.logits + (int64_t)t * E;

@@ -27,6 +27,8 @@ MOE_LORA_BAD_LOGIT = 1
 MOE_LORA_BAD_ADAPTER = 2
 MOE_LORA_BAD_MXFP8 = 4
 STAGES = ("route", "align", "shrink13", "gate_up", "shrink2", "down", "combine")
+# dims.router: the plain top-k router, or the biased router with softmax or sigmoid scores
+ROUTERS = {"topk": 0, "bias_softmax": 1, "bias_sigmoid": 2}
 
 EXPORTED = ("moe_lora_plan_query", "moe_lora_workspace_bytes", "moe_lora_check_args", "moe_lora_route",
             "moe_lora_align", "moe_lora_forward", "moe_lora_packed_weight_bytes", "moe_lora_pack_weights",
@@ -39,7 +41,7 @@ class MoeLoraDims(ctypes.Structure):
                 ("K", ctypes.c_int64), ("S", ctypes.c_int64), ("L", ctypes.c_int64), ("r", ctypes.c_int64),
                 ("routed_scaling_factor", ctypes.c_float), ("renormalize", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("block_m", ctypes.c_int32), ("lora_block_m", ctypes.c_int32),
-                ("split_k", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("router", ctypes.c_int32)]
 
 
 class MoeLoraPlan(ctypes.Structure):
@@ -57,7 +59,9 @@ class MoeLoraArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("topk_ids_out", ctypes.c_void_p),
                 ("topk_weights_out", ctypes.c_void_p), ("stage_events", ctypes.c_void_p),
                 ("weights_packed", ctypes.c_int32), ("weights_mxfp8", ctypes.c_int32),
-                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("expert_bias", ctypes.c_void_p),
+                ("sorted_ids_out", ctypes.c_void_p), ("block_expert_out", ctypes.c_void_p),
+                ("num_post_pad_out", ctypes.c_void_p)]
 
 
 class MoeLoraError(RuntimeError):
@@ -87,7 +91,7 @@ def lib():
     L.moe_lora_workspace_bytes.restype = ctypes.c_size_t
     L.moe_lora_check_args.argtypes = [P(MoeLoraDims), P(MoeLoraArgs)]
     L.moe_lora_check_args.restype = ctypes.c_int
-    L.moe_lora_route.argtypes = [P(MoeLoraDims), vp, vp, vp, vp]
+    L.moe_lora_route.argtypes = [P(MoeLoraDims), vp, vp, vp, vp, vp]
     L.moe_lora_route.restype = ctypes.c_int
     L.moe_lora_align.argtypes = [P(MoeLoraDims), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.moe_lora_align.restype = ctypes.c_int
@@ -110,11 +114,12 @@ def lib():
 
 
 def make_dims(T, H, I, E, K, S=0, L=0, r=0, rsf=1.0, renormalize=1, dtype="bf16", block_m=0,
-              lora_block_m=0, split_k=0) -> MoeLoraDims:
+              lora_block_m=0, split_k=0, router="topk") -> MoeLoraDims:
     dt = {"bf16": MOE_LORA_BF16, "f32": MOE_LORA_F32, torch.bfloat16: MOE_LORA_BF16,
           torch.float32: MOE_LORA_F32}.get(dtype, dtype)
     return MoeLoraDims(int(T), int(H), int(I), int(E), int(K), int(S), int(L), int(r), float(rsf),
-                       int(renormalize), int(dt), int(block_m), int(lora_block_m), int(split_k))
+                       int(renormalize), int(dt), int(block_m), int(lora_block_m), int(split_k),
+                       int(ROUTERS.get(router, router)))
 
 
 def moe_lora_strerror(code: int) -> str:
@@ -157,15 +162,21 @@ def _dev_tensor(t, name, dtype=None):
     return t
 
 
-def moe_lora_route(logits: torch.Tensor, K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1):
-    """Top-K routing + shared-slot append on the GPU -> (topk_ids int32, topk_weights f32)."""
+def moe_lora_route(logits: torch.Tensor, K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1,
+                   router: str = "topk", expert_bias: Optional[torch.Tensor] = None):
+    """Top-K routing + shared-slot append on the GPU -> (topk_ids int32, topk_weights f32).
+    router "bias_softmax" / "bias_sigmoid" selects the biased router (expert_bias [E] f32 or None)."""
     _dev_tensor(logits, "logits", torch.float32)
+    _dev_tensor(expert_bias, "expert_bias", torch.float32)
     T, E = logits.shape
-    dims = make_dims(T, 8, 8, E, K, S, 0, 0, rsf, renormalize)
+    if expert_bias is not None and tuple(expert_bias.shape) != (E,):
+        raise ValueError(f"expert_bias has shape {tuple(expert_bias.shape)}, expected {(E,)}")
+    dims = make_dims(T, 8, 8, E, K, S, 0, 0, rsf, renormalize, router=router)
     ids = torch.empty((T, K + S), dtype=torch.int32, device=logits.device)
     w = torch.empty((T, K + S), dtype=torch.float32, device=logits.device)
     with torch.cuda.device(logits.device):
-        rc = lib().moe_lora_route(ctypes.byref(dims), _ptr(logits), _ptr(ids), _ptr(w), _stream(logits.device))
+        rc = lib().moe_lora_route(ctypes.byref(dims), _ptr(logits), _ptr(expert_bias), _ptr(ids), _ptr(w),
+                                  _stream(logits.device))
     if rc != MOE_LORA_OK:
         raise MoeLoraError(rc, "moe_lora_route")
     return ids, w
@@ -296,7 +307,8 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
                      K: int, S: int = 0, rsf: float = 1.0, renormalize: int = 1,
                      out: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
                      block_m: int = 0, lora_block_m: int = 0, split_k: int = 0,
-                     routing_out: Optional[tuple] = None, stage_events=None) -> torch.Tensor:
+                     routing_out: Optional[tuple] = None, stage_events=None, router: str = "topk",
+                     expert_bias: Optional[torch.Tensor] = None, align_out: Optional[tuple] = None) -> torch.Tensor:
     """The fused MoE-LoRA layer on the GPU (enqueued on the current stream).
 
     Shapes: x [T,H], logits [T,E] f32, adapter_ids [T] i32 (-1 = none),
@@ -307,11 +319,14 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     (bf16 or f32).  routing_out = (ids [T,K+S] i32, weights [T,K+S] f32)
     receives the routing decisions when given.  stage_events: optional
     ctypes array of 2*len(STAGES) hipEvent_t handles recorded around each
-    stage on the launch stream."""
+    stage on the launch stream.  router / expert_bias: see moe_lora_route.
+    align_out = (sorted_ids, block_expert, num_post_pad) int32 device
+    tensors of the plan's sizes receives the alignment when given."""
     dims, args, out, _ws = _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, K=K, S=S, rsf=rsf,
                                        renormalize=renormalize, out=out, workspace=workspace, block_m=block_m,
                                        lora_block_m=lora_block_m, split_k=split_k, routing_out=routing_out,
-                                       stage_events=stage_events)
+                                       stage_events=stage_events, router=router, expert_bias=expert_bias,
+                                       align_out=align_out)
     with torch.cuda.device(x.device):
         rc = lib().moe_lora_forward(ctypes.byref(dims), ctypes.byref(args), _stream(x.device))
     if rc != MOE_LORA_OK:
@@ -342,7 +357,8 @@ def moe_lora_check_inputs(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Op
 
 
 def _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K, S, rsf, renormalize, out, workspace,
-                block_m=0, lora_block_m=0, split_k=0, routing_out=None, stage_events=None):
+                block_m=0, lora_block_m=0, split_k=0, routing_out=None, stage_events=None, router="topk",
+                expert_bias=None, align_out=None):
     """Marshals the layer's tensors (shapes as for moe_lora_forward) into
     (dims, args, out, workspace tensor)."""
     dt = x.dtype
@@ -359,6 +375,7 @@ def _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K, S, rsf,
         _dev_tensor(t, name, dt)
     _dev_tensor(logits, "logits", torch.float32)
     _dev_tensor(adapter_ids, "adapter_ids", torch.int32)
+    _dev_tensor(expert_bias, "expert_bias", torch.float32)
     T, H = x.shape
     if (packed or mx) and w13.H != H:
         raise ValueError(f"the weights are for H={w13.H}, x has H={H}")
@@ -367,7 +384,7 @@ def _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K, S, rsf,
         I = twoI // 2
     E = logits.shape[1]
     L, r = (a13.shape[0], a13.shape[2]) if a13 is not None else (0, 0)
-    want = {"logits": (logits, (T, E)), "out": (out, (T, H))}
+    want = {"logits": (logits, (T, E)), "out": (out, (T, H)), "expert_bias": (expert_bias, (E,))}
     if not (packed or mx):
         want.update(w13=(w13, (E + S, 2 * I, H)), w2=(w2, (E + S, H, I)))
     elif Ep != E + S:
@@ -378,7 +395,14 @@ def _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K, S, rsf,
     for name, (t, shp) in want.items():
         if t is not None and tuple(t.shape) != shp:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
-    dims = make_dims(T, H, I, E, K, S, L, r, rsf, renormalize, dt, block_m, lora_block_m, split_k)
+    dims = make_dims(T, H, I, E, K, S, L, r, rsf, renormalize, dt, block_m, lora_block_m, split_k, router)
+    if align_out is not None:
+        plan = moe_lora_plan_query(dims)
+        for name, t, n in zip(("sorted_ids", "block_expert", "num_post_pad"), align_out,
+                              (plan["sorted_capacity"], plan["max_blocks"], 1)):
+            _dev_tensor(t, name, torch.int32)
+            if t.numel() != n:
+                raise ValueError(f"{name} must hold {n} int32 values, got {t.numel()}")
     if out is None:
         out = torch.empty((T, H), dtype=dt, device=x.device)
     _dev_tensor(out, "out", dt)
@@ -389,12 +413,15 @@ def _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, *, K, S, rsf,
     args = MoeLoraArgs(x.data_ptr(), logits.data_ptr(), adapter_ids.data_ptr() if adapter_ids is not None else None,
                        w13_ptr, w2_ptr,
                        *(t.data_ptr() if t is not None else None for t in (a13, b13, a2, b2)),
-                       out.data_ptr(), ws.data_ptr(), ws.numel(),
+                       out.data_ptr(), ws.data_ptr() if ws is not None else None,
+                       ws.numel() if ws is not None else 0,
                        ids_out.data_ptr() if ids_out is not None else None,
                        w_out.data_ptr() if w_out is not None else None,
                        ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None,
                        1 if packed or (mx and w13.packed) else 0, 1 if mx else 0,
-                       w13.w13_scale.data_ptr() if mx else None, w13.w2_scale.data_ptr() if mx else None)
+                       w13.w13_scale.data_ptr() if mx else None, w13.w2_scale.data_ptr() if mx else None,
+                       expert_bias.data_ptr() if expert_bias is not None else None,
+                       *((t.data_ptr() for t in align_out) if align_out is not None else (None,) * 3))
     return dims, args, out, ws
 
 

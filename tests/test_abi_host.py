@@ -216,3 +216,29 @@ def test_pack_mxfp8_rejects_without_device():
     assert L.moe_lora_pack_mxfp8_weights(ctypes.byref(_dims(H=2888)), vp(0x1000), None, vp(0x2000), None,
                                          None) == ml.MOE_LORA_EUNSUPPORTED
     assert L.moe_lora_pack_mxfp8_weights(ctypes.byref(d), None, None, None, None, None) == ml.MOE_LORA_OK
+
+
+def test_router_and_alignment_outputs_checked_on_host():
+    d = _dims()
+    # router outside {0, 1, 2}; a bias with the plain top-k router
+    with pytest.raises(ml.MoeLoraError) as ei:
+        ml.moe_lora_plan_query(_dims(router=3))
+    assert ei.value.code == ml.MOE_LORA_EINVAL
+    assert ml.moe_lora_check_args(d, _args(expert_bias=0xd000)) == ml.MOE_LORA_EINVAL
+    for r in ("bias_softmax", "bias_sigmoid"):
+        db = _dims(router=r)
+        assert ml.moe_lora_check_args(db, _args(expert_bias=0xd000)) == ml.MOE_LORA_OK
+        assert ml.moe_lora_check_args(db, _args()) == ml.MOE_LORA_OK         # no bias = zero bias
+        assert ml.moe_lora_check_args(db, _args(expert_bias=0xd002)) == ml.MOE_LORA_EINVAL
+    # optional alignment outputs: any 4-byte aligned buffer, misaligned rejected
+    ok = dict(sorted_ids_out=0xe000, block_expert_out=0xf000, num_post_pad_out=0xf800)
+    assert ml.moe_lora_check_args(d, _args(**ok)) == ml.MOE_LORA_OK
+    for name in ok:
+        assert ml.moe_lora_check_args(d, _args(**{**ok, name: ok[name] + 2})) == ml.MOE_LORA_EINVAL, name
+    L = mm.lib()
+    vp = ctypes.c_void_p
+    assert L.moe_lora_route(ctypes.byref(d), vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), None) == \
+        ml.MOE_LORA_EINVAL
+    assert L.moe_lora_route(ctypes.byref(_dims(router=5)), vp(0x1000), None, vp(0x3000), vp(0x4000), None) == \
+        ml.MOE_LORA_EINVAL
+
