@@ -269,6 +269,23 @@ int moe_lora_align(const moe_lora_dims *dims, const int32_t *topk_ids, const int
 /* The whole layer (steps 1-3), enqueued on `stream`. */
 int moe_lora_forward(const moe_lora_dims *dims, const moe_lora_args *args, void *stream);
 
+/* moe_lora_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc.  The layer's scratch is a fixed device array of
+ * MOE_LORA_STATIC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU,
+ * created when the library is first used on that GPU and held until the
+ * process ends; args->workspace and args->workspace_bytes are ignored.  The
+ * call allocates nothing and otherwise behaves as moe_lora_forward (same
+ * arguments, checks, kernels and bits).  The stream must belong to the
+ * current device.  Returns MOE_LORA_EWORKSPACE when the plan's workspace
+ * (moe_lora_workspace_bytes) exceeds the array, before anything is
+ * enqueued.  Every call on one GPU uses the same array: calls that can run
+ * at the same time on one GPU (other streams, other host threads without
+ * ordering) race and must be serialised by the caller; a call may follow
+ * another on the same stream freely. */
+#define MOE_LORA_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_lora_forward_static(const moe_lora_dims *dims, const moe_lora_args *args, void *stream);
+
 /* Check of the input preconditions moe_lora_forward does not check on the
  * device, for debugging a caller.  The logits feed the top-k softmax of step
  * 1 and each adapter id picks one of the L adapters (or none) of step 3

@@ -37,6 +37,13 @@
 
 using namespace moelora;
 
+// Scratch of moe_lora_forward_static: the layer's workspace for callers that
+// cannot allocate.  One copy per GPU, allocated with the code object when the
+// library is first used on that GPU and held until the process ends.  In
+// host code this name is only a stand-in for the symbol: kernels get the
+// device address that hipGetSymbolAddress returns (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[MOE_LORA_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int64_t kLdsBytes = 160 * 1024;
@@ -878,6 +885,49 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     }
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_LORA_OK : hip_fail(e, "forward launch");
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+int scratch_ptr(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return MOE_LORA_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr || !aligned(ptr, 256)) return hip_fail(hipErrorInvalidSymbol, "scratch address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_LORA_OK;
+}
+}  // namespace
+
+int moe_lora_forward_static(const moe_lora_dims *d, const moe_lora_args *a, void *stream) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc != MOE_LORA_OK) return rc;
+    if (!a) return MOE_LORA_EINVAL;
+    if (d->T == 0) return MOE_LORA_OK;
+    if (p.total > (size_t)MOE_LORA_STATIC_SCRATCH_BYTES) return MOE_LORA_EWORKSPACE;
+    moe_lora_args b = *a;
+    // argument checks first (pure host), with a stand-in for the scratch address
+    b.workspace = (void *)(uintptr_t)256;
+    b.workspace_bytes = MOE_LORA_STATIC_SCRATCH_BYTES;
+    const int rc2 = moe_lora_check_args(d, &b);
+    if (rc2 != MOE_LORA_OK) return rc2;
+    const int rc3 = scratch_ptr(&b.workspace);
+    if (rc3 != MOE_LORA_OK) return rc3;
+    return moe_lora_forward(d, &b, stream);
 }
 
 const char *moe_lora_strerror(int code) {

@@ -33,7 +33,8 @@ ROUTERS = {"topk": 0, "bias_softmax": 1, "bias_sigmoid": 2}
 EXPORTED = ("moe_lora_plan_query", "moe_lora_workspace_bytes", "moe_lora_check_args", "moe_lora_route",
             "moe_lora_align", "moe_lora_forward", "moe_lora_packed_weight_bytes", "moe_lora_pack_weights",
             "moe_lora_strerror", "moe_lora_check_inputs",
-            "moe_lora_packed_mxfp8_bytes", "moe_lora_pack_mxfp8_weights")
+            "moe_lora_packed_mxfp8_bytes", "moe_lora_pack_mxfp8_weights", "moe_lora_forward_static")
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeLoraDims(ctypes.Structure):
@@ -97,6 +98,8 @@ def lib():
     L.moe_lora_align.restype = ctypes.c_int
     L.moe_lora_forward.argtypes = [P(MoeLoraDims), P(MoeLoraArgs), vp]
     L.moe_lora_forward.restype = ctypes.c_int
+    L.moe_lora_forward_static.argtypes = [P(MoeLoraDims), P(MoeLoraArgs), vp]
+    L.moe_lora_forward_static.restype = ctypes.c_int
     L.moe_lora_packed_weight_bytes.argtypes = [P(MoeLoraDims), ctypes.c_int]
     L.moe_lora_packed_weight_bytes.restype = ctypes.c_size_t
     L.moe_lora_pack_weights.argtypes = [P(MoeLoraDims), vp, vp, vp, vp, vp]
@@ -332,6 +335,36 @@ def moe_lora_forward(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optiona
     if rc != MOE_LORA_OK:
         raise MoeLoraError(rc, "moe_lora_forward")
     return out
+
+
+def moe_lora_forward_static(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optional[torch.Tensor],
+                            w13, w2, a13=None, b13=None, a2=None, b2=None, *, K: int, S: int = 0,
+                            rsf: float = 1.0, renormalize: int = 1, out: Optional[torch.Tensor] = None,
+                            **kw) -> torch.Tensor:
+    """moe_lora_forward through the entry point that allocates nothing: the
+    library's fixed per-GPU scratch array (STATIC_SCRATCH_BYTES) stands in for
+    the workspace.  Same arguments as moe_lora_forward (no workspace).  `out`
+    is allocated here when not given; pass it for a call that must not
+    allocate."""
+    if out is None:
+        out = torch.empty((x.shape[0], x.shape[1]), dtype=x.dtype, device=x.device)
+    dims, args, out, _ws = _layer_args(x, logits, adapter_ids, w13, w2, a13, b13, a2, b2, K=K, S=S, rsf=rsf,
+                                       renormalize=renormalize, out=out, workspace=_NO_WORKSPACE, **kw)
+    with torch.cuda.device(x.device):
+        rc = lib().moe_lora_forward_static(ctypes.byref(dims), ctypes.byref(args), _stream(x.device))
+    if rc != MOE_LORA_OK:
+        raise MoeLoraError(rc, "moe_lora_forward_static")
+    return out
+
+
+class _NoWorkspace:
+    """Workspace stand-in for moe_lora_forward_static: no buffer at all."""
+
+    def get(self, nbytes, device):
+        return None
+
+
+_NO_WORKSPACE = _NoWorkspace()
 
 
 def moe_lora_check_inputs(x: torch.Tensor, logits: torch.Tensor, adapter_ids: Optional[torch.Tensor],

@@ -242,3 +242,21 @@ def test_router_and_alignment_outputs_checked_on_host():
     assert L.moe_lora_route(ctypes.byref(_dims(router=5)), vp(0x1000), None, vp(0x3000), vp(0x4000), None) == \
         ml.MOE_LORA_EINVAL
 
+
+def test_forward_static_rejects_on_host():
+    """The no-allocation entry point checks sizes and arguments before it
+    touches a device: a plan larger than the fixed scratch gives
+    MOE_LORA_EWORKSPACE, a null input MOE_LORA_EINVAL, T = 0 is a no-op."""
+    L = mm.lib()
+    prefill = _dims(T=4096, L=32, r=32)
+    assert ml.moe_lora_workspace_bytes(prefill) > mm.STATIC_SCRATCH_BYTES
+    assert L.moe_lora_forward_static(ctypes.byref(prefill), ctypes.byref(_args()), None) == ml.MOE_LORA_EWORKSPACE
+    d = _dims()
+    assert ml.moe_lora_workspace_bytes(d) <= mm.STATIC_SCRATCH_BYTES
+    assert L.moe_lora_forward_static(ctypes.byref(d), ctypes.byref(_args(hidden=None)), None) == ml.MOE_LORA_EINVAL
+    assert L.moe_lora_forward_static(ctypes.byref(_dims(r=12)), ctypes.byref(_args()), None) == \
+        ml.MOE_LORA_EUNSUPPORTED
+    assert L.moe_lora_forward_static(ctypes.byref(_dims(T=0)), ctypes.byref(_args(hidden=None)), None) == 0
+    # the workspace fields are ignored: no workspace pointer is needed
+    assert L.moe_lora_forward_static(ctypes.byref(d), ctypes.byref(_args(workspace=None, workspace_bytes=0,
+                                                                          hidden=None)), None) == ml.MOE_LORA_EINVAL
