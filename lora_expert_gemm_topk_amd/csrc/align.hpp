@@ -43,6 +43,10 @@
 
 namespace moelora {
 
+// Fixed part of a tiled-GEMM work item's estimated cost, in units of one
+// 32-row column tile's MFMA work (see align_finish).
+constexpr int kTileCostFixed = 5;
+
 struct AlignParams {
     const int32_t *topk_ids;
     const int32_t *adapter_ids;
@@ -55,6 +59,12 @@ struct AlignParams {
     int32_t *items;
     int32_t *tmp;         // [P] global scratch (used when the keys do not fit in LDS)
     int32_t *tiles;       // optional GEMM token tiles [max_tiles][4]
+    // with tiles: per tiled GEMM g (0 = gate_up, 1 = down) the XCD ranges of
+    // its work items, xsplit[16 g + x] for x = 0..8 (see align_finish)
+    int32_t *xsplit = nullptr;
+    int nwt[2] = {0, 0};   // weight tiles of each GEMM
+    int xcap[2] = {0, 0};  // most items one XCD may take (its share of the grid)
+    int cus = 256;         // compute units of the device
     int32_t *ntiles_out;  // [3]: tile count, most tiles of one expert, experts with tiles
     int T, P, Kp, Ep, La, bm, lbm;
     int cap, max_blocks, max_items;
@@ -78,7 +88,7 @@ __device__ __forceinline__ int clamp_expert(int e, int Ep) { return min(max(e, 0
 __host__ __device__ inline int64_t align_lds_fixed_ints(int NW, int Ep, int La) {
     const int64_t nk = (int64_t)Ep * (La + 1);
     const int64_t tk = (Ep > La + 1 ? Ep : La + 1) + 1;
-    int64_t n = (int64_t)NW * (La + 1) + (int64_t)NW * Ep + 2 * (int64_t)Ep + 1 + tk + 80;
+    int64_t n = (int64_t)NW * (La + 1) + (int64_t)NW * Ep + 2 * (int64_t)Ep + 1 + tk + 80 + (Ep + 1);
     if (La > 0) n += 2 * nk + 1;
     return n;
 }
@@ -142,7 +152,7 @@ __device__ __forceinline__ uint16_t *align_keys(int *lds, int NW, int Ep, int La
 // (pairs per (expert, adapter+1) key) in LDS; tk, scr and itemOff are LDS
 // scratch.  Run by one whole workgroup.
 __device__ void align_finish(const AlignParams &p, const int *offE, const int *totE, int *tk, int *scr,
-                             const int *cnt2, int *itemOff, int npp) {
+                             const int *cnt2, int *itemOff, int npp, int *cst) {
     const int NW = (int)(blockDim.x >> 6);
     const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -220,6 +230,82 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
             p.ntiles_out[1] = scr[20];
             p.ntiles_out[2] = scr[21];
         }
+        // XCD ranges of the tiled GEMMs' work.  The GEMM's logical order is
+        // expert-major (expert, weight tile, token tile), and each XCD takes
+        // one contiguous range of it.  The ranges are cut at equal estimated
+        // cost rather than equal item count: an item's cost is taken as
+        // kTileCostFixed + its 32-row column tiles (the weight slabs stream
+        // through the CU whatever the token count; the MFMA work grows with
+        // it), which follows the measured per-tile K-loop times of the
+        // GPT-OSS prefill (tiles of 192 and 256 rows) closely.  With fewer
+        // than 6 items per CU the rounding of each XCD's items to whole rounds
+        // of its CUs outweighs their cost differences, and the ranges hold
+        // equal item counts instead (measured on the GPT-OSS prefill: down,
+        // 3.8 items per CU, 308 us with equal counts against 322 us by cost;
+        // gate_up, 7.4 per CU, 587 against 541 us).  cst[Ep+1] is LDS
+        // scratch for the per-expert cost prefix.
+        if (p.xsplit != nullptr) {
+            for (int e = tid; e < Ep; e += nt) {
+                const int pad = offE[e + 1] - offE[e], len = tile_len(pad);
+                const int nt_e = len == 0 ? 0 : (pad + len - 1) / len;
+                cst[e] = nt_e == 0 ? 0
+                                   : (nt_e - 1) * (kTileCostFixed + len / 32) +
+                                         (kTileCostFixed + (pad - (nt_e - 1) * len) / 32);
+            }
+            __syncthreads();
+            const int totc = block_excl_scan(cst, Ep, scr);
+            if (tid < 16) {
+                const int g = tid >> 3, x = tid & 7;
+                const int64_t nwt = p.nwt[g];
+                int item = 0;
+                if (x > 0 && totc > 0) {
+                    const int64_t target = (int64_t)x * nwt * totc / 8;
+                    int lo = 0, hi = Ep - 1;  // last e with nwt * cst[e] <= target
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if (nwt * cst[mid] <= target) lo = mid;
+                        else hi = mid - 1;
+                    }
+                    const int e = lo;
+                    const int se = (e + 1 < Ep ? cst[e + 1] : totc) - cst[e];
+                    const int pad = offE[e + 1] - offE[e], len = tile_len(pad);
+                    const int nt_e = len == 0 ? 0 : (pad + len - 1) / len;
+                    if (se > 0 && nt_e > 0) {
+                        const int64_t r = target - nwt * cst[e];
+                        const int64_t wt = min<int64_t>(r / se, nwt - 1);
+                        const int64_t rr = r - wt * se;
+                        const int tt = (int)min<int64_t>(rr / (kTileCostFixed + len / 32), nt_e - 1);
+                        item = (int)(nwt * tk[e] + wt * nt_e + tt);
+                    } else {
+                        item = (int)(nwt * tk[e]);
+                    }
+                }
+                const int live = p.nwt[g] * ntiles;
+                if (live < 6 * p.cus) {
+                    const int q = live / 8, rem = live % 8;
+                    item = x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q;
+                }
+                scr[24 + tid] = item;
+            }
+            __syncthreads();
+            if (tid < 2) {
+                // monotone, every range within the XCD's share of the grid
+                const int g = tid, cap = p.xcap[g];
+                const int live = p.nwt[g] * ntiles;
+                int prev = 0;
+                p.xsplit[16 * g] = 0;
+                for (int x = 1; x < 8; ++x) {
+                    int v = scr[24 + 8 * g + x];
+                    v = max(v, prev);
+                    v = min(v, prev + cap);
+                    v = max(v, live - (8 - x) * cap);
+                    v = min(v, live);
+                    p.xsplit[16 * g + x] = v;
+                    prev = v;
+                }
+                p.xsplit[16 * g + 8] = live;
+            }
+        }
     }
 
     // ---- LoRA work items: (adapter >= 0, expert) runs cut to lbm rows ------
@@ -284,7 +370,8 @@ __device__ void align_body(const AlignParams &p, int *lds) {
     int *totE = offE + Ep + 1;           // [Ep]
     int *tk = totE + Ep;                 // [TK]
     int *scr = tk + TK;                  // [80]
-    int *cnt2 = scr + 80;                // [NK]      (La > 0)
+    int *cst = scr + 80;                 // [Ep+1]    tile cost prefix (align_finish)
+    int *cnt2 = cst + Ep + 1;            // [NK]      (La > 0)
     int *itemOff = cnt2 + NK;            // [NK+1]    (La > 0)
     uint16_t *eL = align_keys(lds, NW, Ep, La);  // [P] expert of pair f
     uint16_t *oL = eL + P;                       // [P] order after the adapter pass
@@ -393,7 +480,7 @@ __device__ void align_body(const AlignParams &p, int *lds) {
         }
     }
 
-    align_finish(p, offE, totE, tk, scr, cnt2, itemOff, npp);
+    align_finish(p, offE, totE, tk, scr, cnt2, itemOff, npp, cst);
 }
 
 // ---- multi-workgroup alignment -------------------------------------------
@@ -458,7 +545,7 @@ __global__ __launch_bounds__(256) void align_colscan_kernel(AlignParams p) {
 __host__ __device__ inline int64_t align_scan_lds_ints(int Ep, int La) {
     const int64_t nk = (int64_t)Ep * (La + 1);
     const int64_t tk = (Ep > La + 1 ? Ep : La + 1) + 1;
-    return 2 * nk + 1 + 2 * (int64_t)Ep + 1 + tk + 80;
+    return 2 * nk + 1 + 2 * (int64_t)Ep + 1 + tk + 80 + (Ep + 1);
 }
 
 // one workgroup
@@ -474,6 +561,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
     int *totE = offE + Ep + 1;       // [Ep]
     int *tk = totE + Ep;             // [TK]
     int *scr = tk + TK;              // [80]
+    int *cst = scr + 80;             // [Ep+1] tile cost prefix of align_finish
     for (int k = tid; k < NK; k += nt) cnt2[k] = p.ktot[k];
     __syncthreads();
     for (int e = tid; e < Ep; e += nt) {
@@ -495,7 +583,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
             run += cnt2[e * A1 + a1];
         }
     }
-    align_finish(p, offE, totE, tk, scr, cnt2, itemOff, npp);
+    align_finish(p, offE, totE, tk, scr, cnt2, itemOff, npp, cst);
 }
 
 // grid nb, block 256, LDS NK ints: the next position of each key.  All four

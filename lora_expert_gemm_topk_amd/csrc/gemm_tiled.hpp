@@ -154,7 +154,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // block like the tokens) instead of row-major.
 template <int BW, int BT, bool GU, bool WP>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int32_t *__restrict__ tiles,
-                                                         const int32_t *__restrict__ n_tiles, int n_wtiles) {
+                                                         const int32_t *__restrict__ n_tiles, int n_wtiles,
+                                                         const int32_t *__restrict__ xsplit) {
     constexpr int MT = BW / 64, NT = BT / 64;          // 32x32 tiles per wave
     constexpr int ROWS = BW + BT;                       // LDS rows per stage
     constexpr int STAGE_BYTES = ROWS * 64;
@@ -163,8 +164,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // Logical order: expert-major, then weight tile, then the expert's token
     // tiles.  Expert e owns logical [n_wtiles*t0, n_wtiles*(t0+nt)) where t0 is
     // its first token tile and nt its tile count (both stored in every tile).
-    // Only the first n_wtiles * n_tiles workgroups have work; the XCD remap
-    // runs over exactly that many so every XCD gets an equal share.
+    // XCD x (the workgroups with blockIdx mod 8 = x) takes the contiguous
+    // range [xsplit[x], xsplit[x+1]), cut by the alignment at equal
+    // estimated cost (tiles of fewer rows cost less), so the XCDs finish
+    // together; workgroups past their XCD's range exit at once.
     //
     // When the load is skewed (one expert holds more than twice the mean tile
     // count of the experts with tiles) the per-XCD ranges would carry very
@@ -173,14 +176,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // whole chip instead (measured on a Zipf-skewed 128-expert prefill: 11-13%
     // faster; on uniform routing the XCD ranges are faster by ~12% on down).
     const int live = n_wtiles * n_tiles[0];
-    if ((int)blockIdx.x >= live) return;
     const bool skewed = 2 * n_tiles[0] < n_tiles[1] * n_tiles[2];
     int wt, ti;
     if (skewed) {
+        if ((int)blockIdx.x >= live) return;
         wt = (int)blockIdx.x % n_wtiles;
         ti = (int)blockIdx.x / n_wtiles;
     } else {
-        const int logical = xcd_logical((int)blockIdx.x, live);
+        const int x = (int)blockIdx.x & 7;
+        const int logical = xsplit[x] + (int)(blockIdx.x >> 3);
+        if (logical >= xsplit[x + 1]) return;
         const int tq = logical / n_wtiles;
         const int4 tq_tile = reinterpret_cast<const int4 *>(tiles)[tq];
         const int t0 = tq_tile.w, ntl = tq_tile.y >> 16;

@@ -71,6 +71,7 @@ struct Plan {
     bool lora = false;
     // workspace offsets (bytes)
     size_t o_ids = 0, o_w = 0, o_sorted = 0, o_sadp = 0, o_bexp = 0, o_cnt = 0, o_items = 0, o_tmp = 0, o_tiles = 0;
+    size_t o_queue = 0;
     size_t o_s13 = 0, o_s2 = 0, o_h = 0, o_y2 = 0, o_xp = 0, total = 0;
     size_t align_total = 0;  // tmp + nothing else, for moe_lora_align
 };
@@ -217,6 +218,7 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     p.o_items = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_items, 1));
     p.o_tmp = take(sizeof(int32_t) * p.tmp_ints);
     p.o_tiles = take(sizeof(int32_t) * 4 * std::max<int64_t>(p.max_tiles, 1));
+    p.o_queue = take(p.kind == 2 ? sizeof(int32_t) * 32 : 0);  // XCD ranges: gate_up's, then down's
     p.o_s13 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
     p.o_s2 = take(lora ? sizeof(float) * p.split * p.cap * d->r : 0);
     // room for h packed (the tiled GEMM's layout): whole 32-wide slabs
@@ -311,11 +313,46 @@ int launch_route(const moe_lora_dims *d, const float *logits, const float *bias,
     return MOE_LORA_OK;
 }
 
+// Weight rows per tile of the LDS-tiled kernel.  256 (16 MFMAs per 8
+// fragment reads per wave) measured fastest for both projections of the
+// GPT-OSS-20B prefill layer even where N is not a multiple of the tile; 128
+// only when N is too small to fill wider tiles.  (Both are whole multiples of
+// the 128-row half tiles the packed weight layout is padded to.)
+int tiled_bw(int N, bool gu) {
+    const int feats = gu ? N * 2 : N;
+    return feats <= 128 ? 128 : 256;
+}
+
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Weight tiles of the tiled gate_up (gu) or down GEMM.
+int tiled_nwt(const moe_lora_dims *d, bool gu) {
+    const int N = (int)(gu ? d->I : d->H);
+    const int bw = tiled_bw(N, gu);
+    const int per = gu ? bw / 2 : bw;
+    return (N + per - 1) / per;
+}
+
+// Work items one XCD may take: twice its equal share of the most items the
+// GEMM can have, so that ranges cut at equal cost always fit the grid.
+int64_t tiled_xcap(const Plan &pl, int n_wt) { return 2 * (((int64_t)n_wt * pl.max_tiles + 7) / 8); }
+
 // Alignment: one workgroup below the multi-workgroup threshold, else four launches.
 int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
                  int32_t *sorted, int32_t *sorted_adapter, int32_t *bexp, int32_t *npp, int32_t *items,
                  int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles,
-                 hipStream_t st, int32_t *npp_copy = nullptr) {
+                 hipStream_t st, int32_t *npp_copy = nullptr, int32_t *queue = nullptr) {
     std::call_once(g_attr_once, set_kernel_attributes);
     if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
     AlignParams ap;
@@ -333,6 +370,12 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
     ap.tmp = tmp;
     ap.tiles = tiles;
     ap.ntiles_out = ntiles;
+    ap.xsplit = tiles ? queue : nullptr;
+    for (int g = 0; g < 2; ++g) {
+        ap.nwt[g] = tiled_nwt(d, g == 0);
+        ap.xcap[g] = (int)tiled_xcap(pl, ap.nwt[g]);
+    }
+    if (tiles) ap.cus = device_cus();
     ap.tile_rows = pl.tile;
     ap.P = (int)pl.P;
     ap.Kp = (int)pl.Kp;
@@ -420,27 +463,20 @@ void launch_shrink(const Plan &pl, ShrinkParams sp, bool gather, int r, hipStrea
     }
 }
 
-// Weight rows per tile of the LDS-tiled kernel.  256 (16 MFMAs per 8
-// fragment reads per wave) measured fastest for both projections of the
-// GPT-OSS-20B prefill layer even where N is not a multiple of the tile; 128
-// only when N is too small to fill wider tiles.  (Both are whole multiples of
-// the 128-row half tiles the packed weight layout is padded to.)
-int tiled_bw(int N, bool gu) {
-    const int feats = gu ? N * 2 : N;
-    return feats <= 128 ? 128 : 256;
-}
 
 template <int BW, int BT, bool GU, bool WP>
 void launch_tiled(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
-                  hipStream_t st) {
+                  const int32_t *xsplit, hipStream_t st) {
     const int n_wt = (gp.Nout + (GU ? BW / 2 : BW) - 1) / (GU ? BW / 2 : BW);
-    const unsigned total = (unsigned)(n_wt * pl.max_tiles);
-    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU, WP>), dim3(total), dim3(256), 0, st, gp, tiles, ntiles, n_wt);
+    // every XCD may take up to xcap items of the cost-balanced ranges
+    const unsigned total = (unsigned)(8 * tiled_xcap(pl, n_wt));
+    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU, WP>), dim3(total), dim3(256), 0, st, gp, tiles, ntiles, n_wt,
+                       xsplit + (GU ? 0 : 16));
 }
 
 template <bool GU, bool WP>
 void launch_gemm_wp(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
-                    hipStream_t st) {
+                    const int32_t *queue, hipStream_t st) {
     if (pl.kind == 1) {
         const int tile = GU ? kStreamBW / 2 : kStreamBW;
         const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
@@ -450,17 +486,17 @@ void launch_gemm_wp(const Plan &pl, const GemmParams &gp, const int32_t *tiles, 
     }
     const int bw = tiled_bw(gp.Nout, GU);
     if (pl.tile == 128) {
-        if (bw == 256) launch_tiled<256, 128, GU, WP>(pl, gp, tiles, ntiles, st);
-        else launch_tiled<128, 128, GU, WP>(pl, gp, tiles, ntiles, st);
+        if (bw == 256) launch_tiled<256, 128, GU, WP>(pl, gp, tiles, ntiles, queue, st);
+        else launch_tiled<128, 128, GU, WP>(pl, gp, tiles, ntiles, queue, st);
     } else {
-        if (bw == 256) launch_tiled<256, 256, GU, WP>(pl, gp, tiles, ntiles, st);
-        else launch_tiled<128, 256, GU, WP>(pl, gp, tiles, ntiles, st);
+        if (bw == 256) launch_tiled<256, 256, GU, WP>(pl, gp, tiles, ntiles, queue, st);
+        else launch_tiled<128, 256, GU, WP>(pl, gp, tiles, ntiles, queue, st);
     }
 }
 
 template <bool GU>
-void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles, bool wp,
-                 hipStream_t st) {
+void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
+                 const int32_t *queue, bool wp, hipStream_t st) {
     if (gp.Wscale != nullptr) {
         // MXFP8 weights: the streaming kernel only (checked by moe_lora_check_args)
         const int tile = GU ? kStreamBW / 2 : kStreamBW;
@@ -474,8 +510,8 @@ void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, con
         }
         return;
     }
-    if (wp) launch_gemm_wp<GU, true>(pl, gp, tiles, ntiles, st);
-    else launch_gemm_wp<GU, false>(pl, gp, tiles, ntiles, st);
+    if (wp) launch_gemm_wp<GU, true>(pl, gp, tiles, ntiles, queue, st);
+    else launch_gemm_wp<GU, false>(pl, gp, tiles, ntiles, queue, st);
 }
 
 }  // namespace
@@ -732,6 +768,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         if (ev) (void)hipEventRecord((hipEvent_t)ev[slot], st);
     };
     int32_t *tiles = (int32_t *)(ws + p.o_tiles);
+    int32_t *queue = (int32_t *)(ws + p.o_queue);
     mark(2 * MOE_LORA_STAGE_ROUTE);
     if (p.row_shrink) launch_route_shrink(p, d, a, ids, wts, s13, st);
     else launch_route(d, a->router_logits, a->expert_bias, ids, wts, st);
@@ -739,7 +776,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     mark(2 * MOE_LORA_STAGE_ALIGN);
     int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt, items,
                           cnt + 1, tmp,
-                          p.kind == 2 ? tiles : nullptr, cnt + 2, st, a->num_post_pad_out);
+                          p.kind == 2 ? tiles : nullptr, cnt + 2, st, a->num_post_pad_out, queue);
     if (r2 != MOE_LORA_OK) return r2;
     // the tiled GEMM reads x gathered and packed per sorted row; with LoRA
     // the pack shares one launch with the gate_up shrink (stage SHRINK13)
@@ -854,7 +891,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.out = h;
         gp.Kdim = H;
         gp.Nout = I;
-        launch_gemm<true>(p, gp, tiles, cnt + 2, a->weights_packed != 0, st);
+        launch_gemm<true>(p, gp, tiles, cnt + 2, queue, a->weights_packed != 0, st);
         mark(2 * MOE_LORA_STAGE_GATE_UP + 1);
         mark(2 * MOE_LORA_STAGE_SHRINK2);
         if (p.lora) {
@@ -876,7 +913,7 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.Kdim = I;
         gp.Nout = H;
         mark(2 * MOE_LORA_STAGE_DOWN);
-        launch_gemm<false>(p, gp, tiles, cnt + 2, a->weights_packed != 0, st);
+        launch_gemm<false>(p, gp, tiles, cnt + 2, queue, a->weights_packed != 0, st);
         mark(2 * MOE_LORA_STAGE_DOWN + 1);
         mark(2 * MOE_LORA_STAGE_COMBINE);
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((H / kCombineVec<true> + 255) / 256), (unsigned)d->T), dim3(256),

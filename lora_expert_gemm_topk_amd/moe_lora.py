@@ -222,6 +222,15 @@ def moe_lora_packed_weight_bytes(dims: MoeLoraDims, which: int) -> int:
     return int(lib().moe_lora_packed_weight_bytes(ctypes.byref(dims), int(which)))
 
 
+def _layout_dims(Ep: int, H: int, I: int) -> MoeLoraDims:
+    """Dims that describe only the stacked weights' shapes (E+S = Ep expert
+    slices): the routing fields do not affect the packed layouts, so one
+    token and K = 1 stand in, with up to 1024 routed experts and the rest as
+    shared slots (the largest router the layer takes, E = 1024 and S = 64)."""
+    E = min(Ep, 1024)
+    return make_dims(1, H, I, E, 1, Ep - E, 0, 0, 1.0, 1, "bf16")
+
+
 class PackedWeights:
     """w13 and w2 re-laid out once by moe_lora_pack_weights (bf16 only).
 
@@ -236,8 +245,7 @@ class PackedWeights:
         self.I = twoI // 2
         if tuple(w2.shape) != (self.Ep, self.H, self.I):
             raise ValueError(f"w2 shape {tuple(w2.shape)} does not match w13 {tuple(w13.shape)}")
-        # routing fields do not affect the layout: one routed expert, K = 1
-        self.dims = make_dims(1, self.H, self.I, self.Ep, 1, 0, 0, 0, 1.0, 1, "bf16")
+        self.dims = _layout_dims(self.Ep, self.H, self.I)
         n13 = moe_lora_packed_weight_bytes(self.dims, 0)
         n2 = moe_lora_packed_weight_bytes(self.dims, 1)
         if n13 == 0 or n2 == 0:
@@ -288,7 +296,7 @@ class Mxfp8Weights:
     def pack(self) -> "Mxfp8Weights":
         """A copy whose codes are in the packed order of
         moe_lora_pack_mxfp8_weights (same scales, bit-identical results)."""
-        dims = make_dims(1, self.H, self.I, self.Ep, 1)
+        dims = _layout_dims(self.Ep, self.H, self.I)
         n13, n2 = moe_lora_packed_mxfp8_bytes(dims, 0), moe_lora_packed_mxfp8_bytes(dims, 1)
         if not n13 or not n2:
             raise ValueError("no packed MXFP8 form for this shape")

@@ -30,6 +30,9 @@ import numpy as np
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "oracle.c"
 _LIB = _HERE / "liboracle.so"
+# tests/test_oracle_mutations.py points this at a deliberately broken build
+# of oracle.c to check that the pins catch the mistake
+_LIB_OVERRIDE = os.environ.get("MOELORA_ORACLE_LIB")
 _lib = None
 
 F32 = 0
@@ -51,9 +54,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
-        build()
-    lib = ctypes.CDLL(str(_LIB))
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+            build()
+        lib = ctypes.CDLL(str(_LIB))
     i64, i32, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_float
     vp = ctypes.c_void_p
     lib.oracle_route.argtypes = [i64, i64, i64, i64, f32, i32, vp, vp, vp]

@@ -260,3 +260,13 @@ def test_forward_static_rejects_on_host():
     # the workspace fields are ignored: no workspace pointer is needed
     assert L.moe_lora_forward_static(ctypes.byref(d), ctypes.byref(_args(workspace=None, workspace_bytes=0,
                                                                           hidden=None)), None) == ml.MOE_LORA_EINVAL
+
+
+def test_packing_dims_cover_the_largest_router():
+    """Packed layouts depend only on the weight shapes: stacks of more than
+    1024 expert slices (1024 routed + shared slots) have a packed size."""
+    for Ep in (1, 1024, 1025, 1088):
+        d = mm._layout_dims(Ep, 64, 32)
+        assert d.E + d.S == Ep and d.E <= 1024
+        assert mm.moe_lora_packed_weight_bytes(d, 0) == Ep * 16 * 1 * 2 * 1024
+        assert mm.moe_lora_packed_mxfp8_bytes(d, 1) == Ep * (64 // 16) * 1 * 2048

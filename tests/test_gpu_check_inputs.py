@@ -96,6 +96,11 @@ def test_check_inputs_mxfp8(plant):
     want = _expected(inp, mxw)
     assert want == (0 if plant == "none" else ml.MOE_LORA_BAD_MXFP8)
     assert _status(inp, packed=mxw) == want
+    # the packed codes carry the same codes (and zero padding past K, never
+    # flagged): the check reads the packed buffer and reports the same
+    packed = mxw.pack()
+    torch.cuda.synchronize()
+    assert _status(inp, packed=packed) == want
 
 
 def test_check_inputs_empty_batch_writes_zero():

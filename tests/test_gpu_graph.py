@@ -20,15 +20,16 @@ pytestmark = pytest.mark.gpu
 
 
 def _weights(inp, packed):
-    if packed == "mx":
+    if packed in ("mx", "mxp"):
         c13, s13 = synth.mxfp8_quantize(inp.w13.cpu())
         c2, s2 = synth.mxfp8_quantize(inp.w2.cpu())
-        return ml.Mxfp8Weights(c13.cuda(), s13.cuda(), c2.cuda(), s2.cuda())
+        mxw = ml.Mxfp8Weights(c13.cuda(), s13.cuda(), c2.cuda(), s2.cuda())
+        return mxw.pack() if packed == "mxp" else mxw
     return ml.PackedWeights(inp.w13, inp.w2) if packed else None
 
 
 @pytest.mark.parametrize("T,bm,packed", [(48, 0, False), (64, 0, True), (600, 128, True), (1, 0, False),
-                                         (64, 0, "mx"), (7, 32, "mx")])
+                                         (64, 0, "mx"), (7, 32, "mx"), (64, 0, "mxp")])
 def test_graph_replay_equals_eager(T, bm, packed):
     shape = synth.LayerShape(T=T, H=256, I=192, E=8, K=2, S=1, L=3, r=16, rsf=2.5)
     inp = synth.make_inputs(shape, synth.Recipe(adapters="uniform_all"), seed=T, device="cuda")

@@ -123,3 +123,19 @@ def test_forward_alignment_outputs(bm):
     assert int(npp.item()) == o["num_post_pad"]
     assert np.array_equal(sid.cpu().numpy(), o["sorted_ids"])
     assert np.array_equal(bex.cpu().numpy(), o["block_expert"])
+
+
+def test_check_inputs_flags_a_nonfinite_bias():
+    """moe_lora_check_inputs reads the biased router's expert bias with the
+    logits: a NaN or infinite bias value is reported as MOE_LORA_BAD_LOGIT."""
+    shape = synth.LayerShape(T=40, H=128, I=96, E=6, K=2, S=1, L=3, r=16, rsf=2.5)
+    inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=3)
+    for val, want in ((0.5, 0), (float("nan"), ml.MOE_LORA_BAD_LOGIT), (float("inf"), ml.MOE_LORA_BAD_LOGIT)):
+        bias = torch.zeros(shape.E, dtype=torch.float32, device=DEV)
+        bias[shape.E - 1] = val
+        say("check_inputs bias", val)
+        st = ml.moe_lora_check_inputs(inp.x, inp.logits, inp.adapter_ids, inp.w13, inp.w2, inp.a13, inp.b13,
+                                      inp.a2, inp.b2, K=shape.K, S=shape.S, rsf=shape.rsf,
+                                      router="bias_sigmoid", expert_bias=bias)
+        torch.cuda.synchronize()
+        assert int(st.item()) == want
