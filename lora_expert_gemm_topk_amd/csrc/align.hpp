@@ -40,6 +40,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "route.hpp"
 
 namespace moelora {
 
@@ -655,12 +656,18 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignParams p) {
 // per-expert loops of the general form, and the padding, block map and LoRA
 // items are written by independent threads.  The layout is the same as the
 // general form's, bit for bit.
-__host__ __device__ inline int64_t align_small_lds_ints(int NW, int Ep, int La) {
+//
+// ROUTE: the same workgroup routes the tokens first (wave w routes tokens
+// w, w + NW, ...; ids and weights are written out as by the router launch
+// and kept in LDS for the sort), one launch instead of two for the small
+// calls whose gate_up shrink does not run in the router's launch.
+__host__ __device__ inline int64_t align_small_lds_ints(int NW, int Ep, int La, int64_t P) {
     const int64_t NK = (int64_t)Ep * (La + 1);
-    return (int64_t)NW * NK + 3 * (NK + 1) + 2 * (int64_t)Ep + 1 + 80;
+    return (int64_t)NW * NK + 3 * (NK + 1) + 2 * (int64_t)Ep + 1 + 80 + P;
 }
 
-__global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p) {
+template <bool ROUTE, int VPL>
+__global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p, RouteParams rp) {
     extern __shared__ int lds[];
     const int nt = (int)blockDim.x, NW = nt >> 6;
     const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -672,13 +679,21 @@ __global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p) {
     int *offE = itemOff + NK + 1;     // [Ep+1] padded start of each expert
     int *totE = offE + Ep + 1;        // [Ep] pairs per expert
     int *scr = totE + Ep;             // [80] scan scratch
+    int *idsL = scr + 80;             // [P] expert of each pair (ROUTE)
 
+    if constexpr (ROUTE) {
+        for (int t = w; t < rp.T; t += NW) {
+            const int myi = route_one_token<VPL>(rp, t);  // K + S <= 64: every slot is returned
+            if (lane < p.Kp) idsL[t * p.Kp + lane] = myi;
+        }
+    }
     for (int i = tid; i < NW * NK; i += nt) histW[i] = 0;
     const int f = tid;
     const bool valid = f < P;
+    if constexpr (ROUTE) __syncthreads();
     int e = 0, a1 = 0;
     if (valid) {
-        e = clamp_expert(p.topk_ids[f], Ep);
+        e = clamp_expert(ROUTE ? idsL[f] : p.topk_ids[f], Ep);
         if (La > 0) a1 = adapter_key_of(p.adapter_ids[f / p.Kp], La);
     }
     const int key = e * A1 + a1;

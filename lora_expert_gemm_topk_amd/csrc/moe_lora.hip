@@ -64,6 +64,7 @@ struct Plan {
     bool lds_keys = false;   // alignment keys staged in LDS
     bool multi = false;      // multi-workgroup alignment
     bool small_align = false;  // one-pass alignment for small calls without GEMM token tiles
+    bool route_in_align = false;  // small_align: the router runs in the alignment's launch
     int align_small_nw = 4;
     size_t align_small_lds = 0;
     int anb = 0, achunk = 0; // its blocks and pairs per block
@@ -190,10 +191,13 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     p.small_align = !p.multi && p.kind != 2 && p.P <= 1024;
     if (p.small_align) {
         p.align_small_nw = (int)std::max<int64_t>(4, (p.P + 63) / 64);
-        const int64_t ints = align_small_lds_ints(p.align_small_nw, (int)p.Ep, (int)p.La);
+        const int64_t ints = align_small_lds_ints(p.align_small_nw, (int)p.Ep, (int)p.La, p.P);
         if (ints * 4 > 65536) p.small_align = false;
         else p.align_small_lds = (size_t)ints * 4;
     }
+    // small calls whose gate_up shrink does not run in the router's launch
+    // route inside the alignment's launch (every slot fits one wavefront)
+    p.route_in_align = p.small_align && !p.row_shrink && p.Kp <= 64;
     p.tmp_ints = p.P;
     if (p.multi) {
         p.achunk = (int)std::max<int64_t>(256, ((p.P + 63) / 64 + 63) / 64 * 64);
@@ -352,7 +356,8 @@ int64_t tiled_xcap(const Plan &pl, int n_wt) { return 2 * (((int64_t)n_wt * pl.m
 int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
                  int32_t *sorted, int32_t *sorted_adapter, int32_t *bexp, int32_t *npp, int32_t *items,
                  int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles,
-                 hipStream_t st, int32_t *npp_copy = nullptr, int32_t *queue = nullptr) {
+                 hipStream_t st, int32_t *npp_copy = nullptr, int32_t *queue = nullptr,
+                 const RouteParams *rp = nullptr) {
     std::call_once(g_attr_once, set_kernel_attributes);
     if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
     AlignParams ap;
@@ -404,8 +409,17 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
         return MOE_LORA_OK;
     }
     if (pl.small_align && tiles == nullptr) {
-        hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3((unsigned)(pl.align_small_nw * 64)), pl.align_small_lds,
-                           st, ap);
+        const dim3 g1(1), blk((unsigned)(pl.align_small_nw * 64));
+        if (rp == nullptr) {
+            hipLaunchKernelGGL((align_small_kernel<false, 1>), g1, blk, pl.align_small_lds, st, ap, RouteParams{});
+        } else {
+            const int E = rp->E;
+            if (E <= 64) hipLaunchKernelGGL((align_small_kernel<true, 1>), g1, blk, pl.align_small_lds, st, ap, *rp);
+            else if (E <= 128) hipLaunchKernelGGL((align_small_kernel<true, 2>), g1, blk, pl.align_small_lds, st, ap, *rp);
+            else if (E <= 256) hipLaunchKernelGGL((align_small_kernel<true, 4>), g1, blk, pl.align_small_lds, st, ap, *rp);
+            else if (E <= 512) hipLaunchKernelGGL((align_small_kernel<true, 8>), g1, blk, pl.align_small_lds, st, ap, *rp);
+            else hipLaunchKernelGGL((align_small_kernel<true, 16>), g1, blk, pl.align_small_lds, st, ap, *rp);
+        }
         return MOE_LORA_OK;
     }
     const dim3 grid(1), block((unsigned)(pl.align_nw * 64));
@@ -771,12 +785,14 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     int32_t *queue = (int32_t *)(ws + p.o_queue);
     mark(2 * MOE_LORA_STAGE_ROUTE);
     if (p.row_shrink) launch_route_shrink(p, d, a, ids, wts, s13, st);
-    else launch_route(d, a->router_logits, a->expert_bias, ids, wts, st);
+    else if (!p.route_in_align) launch_route(d, a->router_logits, a->expert_bias, ids, wts, st);
     mark(2 * MOE_LORA_STAGE_ROUTE + 1);
+    const RouteParams rp_align = route_params(d, a->router_logits, a->expert_bias, ids, wts);
     mark(2 * MOE_LORA_STAGE_ALIGN);
     int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt, items,
                           cnt + 1, tmp,
-                          p.kind == 2 ? tiles : nullptr, cnt + 2, st, a->num_post_pad_out, queue);
+                          p.kind == 2 ? tiles : nullptr, cnt + 2, st, a->num_post_pad_out, queue,
+                          p.route_in_align ? &rp_align : nullptr);
     if (r2 != MOE_LORA_OK) return r2;
     // the tiled GEMM reads x gathered and packed per sorted row; with LoRA
     // the pack shares one launch with the gate_up shrink (stage SHRINK13)
