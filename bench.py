@@ -291,8 +291,10 @@ def report_mxfp8(name: str, steps: int, warmup: int) -> dict:
     """A bf16 workload with its expert weights given as MXFP8 (E4M3 codes and
     one E8M0 scale per 32 elements, drawn from the same seeded bf16 weights):
     per-iteration median/p10/p90, the layer's HBM fraction with the weights
-    counted at 1 + 1/32 bytes per element, the gate_up and down kernels
-    timed by stage events, and the bf16 layer on the same inputs beside it."""
+    counted at 1 + 1/32 bytes per element and its matrix-core fraction (bf16
+    products on the converted weights), the gate_up and down kernels timed by
+    stage events, and the bf16 layer (packed weights) on the same inputs
+    beside it, its kernels timed the same way."""
     shape, recipe = synth.workload(name)
     inp = synth.make_inputs(shape, recipe, seed=0, device="cuda")
     c13, s13 = synth.mxfp8_quantize(inp.w13.cpu())
@@ -324,12 +326,22 @@ def report_mxfp8(name: str, steps: int, warmup: int) -> dict:
     gu_bytes = wk["bytes_gate_up"] - wk["experts"] * 2 * shape.I * shape.H * (2 - (1 + 1 / 32))
     pw = ml.PackedWeights(inp.w13, inp.w2)
     tb = per_iteration(lambda: ml.forward_inputs(inp, out=out, workspace=ws, packed=pw), steps, warmup)
+    se = StageEvents(steps)
+    for i in range(steps):
+        ml.forward_inputs(inp, out=out, workspace=ws, packed=pw, stage_events=se.arrays[i])
+    torch.cuda.synchronize()
+    stage_b = se.stage_ms()
+    se.close()
+    dims = ml.make_dims(shape.T, shape.H, shape.I, shape.E, shape.K, shape.S, shape.L, shape.r, shape.rsf)
     res = {"tokens_per_s": shape.T / sec, **t, "weights": "mxfp8 (E4M3, E8M0 scale per 32), codes packed",
-           "dtype": "bf16",
+           "dtype": "bf16", "gemm_kind": ml.moe_lora_plan_query(dims)["gemm_kind"],
            "bytes": bytes_layer, "hbm_frac": bytes_layer / sec / HBM_PEAK,
+           "mfma_frac": wk["flops_layer"] / sec / MFMA_BF16_PEAK,
            "gate_up_us": stage["gate_up"] * 1e3, "down_us": stage["down"] * 1e3,
            "gate_up_hbm_frac": gu_bytes / (stage["gate_up"] * 1e-3) / HBM_PEAK,
-           "bf16_packed_median_ms": tb["median_ms"], "speedup_vs_bf16": tb["median_ms"] / t["median_ms"]}
+           "gate_up_mfma_frac": wk["flops_gate_up"] / (stage["gate_up"] * 1e-3) / MFMA_BF16_PEAK,
+           "bf16_packed_median_ms": tb["median_ms"], "speedup_vs_bf16": tb["median_ms"] / t["median_ms"],
+           "bf16_gate_up_us": stage_b["gate_up"] * 1e3, "bf16_down_us": stage_b["down"] * 1e3}
     del inp, mxw, pw
     torch.cuda.empty_cache()
     return res
@@ -496,6 +508,10 @@ def main() -> int:
         print("bench: reported gptoss_decode_T64 with MXFP8 weights", file=sys.stderr, flush=True)
         result["reported"]["gptoss_decode_T64_mxfp8"] = report_mxfp8("gptoss_decode_T64", max(20, args.steps),
                                                                      max(5, args.warmup))
+        if args.prefill:
+            print(f"bench: reported {args.prefill} with MXFP8 weights", file=sys.stderr, flush=True)
+            result["reported"][f"{args.prefill}_mxfp8"] = report_mxfp8(args.prefill, max(5, args.steps // 5),
+                                                                       max(2, args.warmup // 5))
     print(json.dumps(result), flush=True)
     return 0
 

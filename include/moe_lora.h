@@ -173,11 +173,12 @@ typedef struct moe_lora_plan {
  *     2^(scale - 127).  Activations, LoRA stacks and the output stay bf16,
  *     and the products run in bf16 on the exactly converted weights.
  *     Preconditions (not checked on the device): scale bytes in [1, 254],
- *     codes not NaN (0x7F, 0xFF).  Needs dtype bf16,
- *     H and I multiples of 32 and at most 8192, and the streaming GEMM
- *     (plan gemm_kind 1; for many rows per expert pass block_m 16 or 32),
- *     else MOE_LORA_EUNSUPPORTED; NULL or misaligned scales give
- *     MOE_LORA_EINVAL.
+ *     codes not NaN (0x7F, 0xFF).  Needs dtype bf16, H and I multiples
+ *     of 32, and H, I at most 8192 on the streaming GEMM (plan gemm_kind 1)
+ *     or at most 3072 on the LDS-tiled GEMM (gemm_kind 2, which converts
+ *     each weight fragment in registers right before its products; pass
+ *     block_m 16 or 32 for longer rows), else MOE_LORA_EUNSUPPORTED; NULL or
+ *     misaligned scales give MOE_LORA_EINVAL.
  *   expert_bias [E] f32: the per-expert bias of the biased router
  *     (dims.router 1 or 2; NULL = all zero); must be NULL with router 0.
  *   sorted_ids_out [sorted_capacity], block_expert_out [max_blocks],

@@ -72,6 +72,9 @@ constexpr int kTileBK = 32;   // K per LDS stage
 #endif
 constexpr int kStages = MOELORA_TILED_STAGES;  // LDS ring depth
 static_assert(kStages >= 3, "the K loop keeps at least two slabs in flight");
+// MXFP8 weights in the tiled kernel: most 32-element scale blocks per row
+// (K <= 3072), so the tile's scale rows fit in LDS beside the ring
+constexpr int kMxTiledMaxBlocks = 96;
 
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order
 template <typename F, int... I>
@@ -82,6 +85,37 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
+
+// Step plan of the MXFP8 steady-state k-step (MT row tiles, NTL live column
+// tiles, row-tile-major MFMA order: step s runs row tile s / NTL, column
+// tile s % NTL).  The codes of row tile mt for the next k-step are read at
+// ra(mt), one step after this k-step's conversion of mt (at step
+// (mt - 1) NTL) consumed them; row tile 0 of the next k-step is converted at
+// CV0, after this k-step's last use of it; the B fragment reads and then the
+// slab copies take the steps with no code read, in order (B reads beyond
+// them go to the last step, copies beyond them after the k-step).
+template <int MT, int NTL>
+struct MxSched {
+    static constexpr int NMM = MT * NTL;
+    static constexpr int CV0 = NTL > NMM - 2 ? NTL : NMM - 2;
+    static constexpr int ra(int mt) { return mt == 0 ? 0 : (mt - 1) * NTL + 1; }
+    static constexpr bool taken(int st) {
+        for (int m = 0; m < MT; ++m)
+            if (ra(m) == st) return true;
+        return false;
+    }
+    static constexpr int free_step(int k) {
+        int c = 0;
+        for (int st = 0; st < NMM; ++st)
+            if (!taken(st)) {
+                if (c == k) return st;
+                ++c;
+            }
+        return -1;
+    }
+    static constexpr int rb(int nt) { return free_step(nt) >= 0 ? free_step(nt) : NMM - 1; }
+    static constexpr int dstep(int d) { return free_step(NTL + d); }
+};
 
 // 16 bytes of zeros: the source of every load past the end of K
 __device__ __attribute__((aligned(16))) const uint16_t g_zero_chunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -152,7 +186,21 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 // WP: weights in the packed layout of moe_lora_pack_weights (copied block by
 // block like the tokens) instead of row-major.
-template <int BW, int BT, bool GU, bool WP>
+//
+// MX: MXFP8 expert weights (E4M3 codes, one E8M0 scale per 32 elements along
+// K; row-major codes, or with WP the packed codes of
+// moe_lora_pack_mxfp8_weights).  A K slab then carries 32 codes (bytes) per
+// weight row: in each 1 KiB block of the stage's weight area, 32 tile rows,
+// codes 0..15 of row r at 16 r and codes 16..31 at 512 + 16 r, so a lane's
+// eight codes of a 16-wide k-step are one 8-byte LDS read.  The tile's
+// scale rows (K/32 bytes per weight row) are copied to LDS once per tile;
+// each fragment is converted with the hardware's scaled FP8 -> bf16
+// conversion (exact: E4M3 has 3 mantissa bits) right before its first MFMA,
+// and the same bf16 MFMAs run.  The weight area keeps its bf16 size, so the
+// LoRA slabs (bf16 B rows) are unchanged, and every slab issues the same
+// number of stage loads per wave (a K slab's spare weight-side loads copy
+// the zero chunk), which keeps the slab waits exact.
+template <int BW, int BT, bool GU, bool WP, bool MX = false>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int32_t *__restrict__ tiles,
                                                          const int32_t *__restrict__ n_tiles, int n_wtiles,
                                                          const int32_t *__restrict__ xsplit) {
@@ -160,6 +208,15 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     constexpr int ROWS = BW + BT;                       // LDS rows per stage
     constexpr int STAGE_BYTES = ROWS * 64;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * STAGE_BYTES];
+    // MX: the tile's weight scales.  The tile's weight rows are NRUN runs of
+    // consecutive rows (gate_up: its gate rows, then its up rows), so the
+    // scales of a run are one contiguous byte range of K/32 bytes per row;
+    // each run has RUN_BYTES of LDS (layout at the copy below).
+    constexpr int NRUN = GU ? 2 : 1, RUN_ROWS = GU ? BW / 2 : BW;
+    constexpr int RUN_CHUNKS = (RUN_ROWS * kMxTiledMaxBlocks + 15) / 16;  // most whole 16-byte pieces of a run
+    constexpr int RUN_COPIES = (RUN_CHUNKS + 63) / 64;                    // 1 KiB copies per run, at most
+    constexpr int RUN_BYTES = 16 + 1024 * RUN_COPIES + 32;  // + the 8-byte scale reads' overhang
+    __shared__ __attribute__((aligned(16))) unsigned char mx_sc[MX ? NRUN * RUN_BYTES : 16];
 
     // Logical order: expert-major, then weight tile, then the expert's token
     // tiles.  Expert e owns logical [n_wtiles*t0, n_wtiles*(t0+nt)) where t0 is
@@ -218,6 +275,44 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     const int f_row = (tid < BT) ? p.sorted_ids[my_row] : p.P;
     const int a_row = (p.lora && tid < BT) ? p.sorted_adapter[my_row] : -1;
 
+    // ---- MX: the tile's scales, copied to LDS ahead of the ring ------------
+    // Run u covers the weight rows of features i0 .. i0 + vrows - 1 (gate
+    // rows, or up rows at u = 1): bytes [0, len) from rg.  Byte b of the
+    // range lands at LDS run base + 16 + (rg mod 16) + b, which keeps the
+    // 16-byte grid of the scale array (16-byte aligned) on that of LDS, so
+    // the scale of (run row q, K block kb) sits at run base + 16 +
+    // (rg mod 16) + q nb + kb.  The whole 16-byte pieces from rg rounded down
+    // to the end rounded down (all inside the array) go by direct
+    // global->LDS loads issued before the ring's (so every slab wait covers
+    // them; lanes past the last piece copy the zero chunk into the run's
+    // spare bytes); the last (end mod 16) bytes are fetched one per thread
+    // and stored once the first slab wait has seen every copy land.
+    const int nb = (int)(Kd / 32);
+    int mx_off16[NRUN], mx_nch[NRUN], mx_tail[NRUN];
+    uint32_t mx_byte = 0;
+    if constexpr (MX) {
+        const int vrows = max(0, min(RUN_ROWS, N - i0));
+#pragma unroll
+        for (int u = 0; u < NRUN; ++u) {
+            const uint8_t *rg = p.Wscale + ((int64_t)e * rows_per_expert + (u ? N : 0) + i0) * nb;
+            const uint8_t *g16 = rg - ((uintptr_t)rg & 15);
+            const uint8_t *end = rg + vrows * nb;
+            const uint8_t *end0 = end - ((uintptr_t)end & 15);
+            mx_off16[u] = (int)((uintptr_t)rg & 15);
+            mx_nch[u] = (int)((end0 - g16) >> 4);
+            mx_tail[u] = (int)((uintptr_t)end & 15);
+            typedef __attribute__((address_space(3))) unsigned char lds_b;
+            lds_b *run = (lds_b *)mx_sc + u * RUN_BYTES + 16;
+            for (int m = w; m * 64 < mx_nch[u]; m += 4) {
+                const int c = m * 64 + lane;
+                dma16(c < mx_nch[u] ? (const void *)(g16 + 16 * c) : (const void *)g_zero_chunk, run + 1024 * m);
+            }
+            // threads 16u .. 16u + 14: the tail bytes
+            const int k = tid - 16 * u;
+            if (k >= 0 && k < mx_tail[u]) mx_byte = end0[k];
+        }
+    }
+
     // ---- direct-to-LDS stage loads ----------------------------------------
     // Wave w owns the stage's 16-row groups w, w+4, ...: instruction j fills
     // group w + 4j.  Groups below BW/16 hold weight rows, the rest token rows.
@@ -229,6 +324,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     constexpr int LPW = GROUPS / 4;                 // load instructions per wave per stage
     constexpr int LPW_A = BW / 64;                  // of which weight groups
     constexpr bool B_PACKED = true;                 // tokens arrive packed (x packed per sorted row, h)
+    // MX K slabs: 32 codes (bytes) per weight row fill half the weight area,
+    // BW/128 loads per wave; the wave's other weight-side loads are not issued
+    constexpr int MX_REAL = BW / 128;
+    constexpr int LPW_K = MX ? LPW - LPW_A + MX_REAL : LPW;  // loads per wave of a K slab
     const int64_t nslab_in = (Kd + kSlabK - 1) / kSlabK;
     const uint16_t *src[LPW];
     int chunk_of[LPW];  // chunk (0..3) this lane moves, row-major groups
@@ -258,6 +357,38 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     auto src_step = [&](int j) -> int64_t {
         return (j < LPW_A ? WP : B_PACKED) ? (int64_t)kBlockElems : (int64_t)kTileBK;
     };
+    // MX: weight-side load j < BW/128 of a K slab moves 32 tile rows: lane l
+    // takes codes 16q .. 16q+15 (q = l/32) of tile row 32(w+4j) + l%32 to
+    // byte 16l of the stage's 1 KiB block w+4j.  Packed codes: the slab is
+    // 32-code group kt%4 of 128-wide chunk kt/4, whose 2 KiB block per 16 rows
+    // holds half q of row r's group g at 1024q + 256g + 16r.  Rows past N
+    // read the expert's row 0, as the bf16 weights do (their outputs are
+    // dropped).
+    const uint8_t *mx_src[MX_REAL];
+    if constexpr (MX) {
+        const uint8_t *W8 = reinterpret_cast<const uint8_t *>(p.W);
+        const int64_t nch = packed_mx_chunks(Kd);
+#pragma unroll
+        for (int j = 0; j < MX_REAL; ++j) {
+            const int trow = (w + 4 * j) * 32 + (lane & 31), q = lane >> 5;
+            bool ok;
+            const int R = tile_weight_row<GU>(trow, i0, N, ok);
+            const int64_t grow = (int64_t)e * rows_per_expert + (ok ? R : 0);
+            mx_src[j] = WP ? W8 + (grow >> 4) * nch * 2048 + 16 * (64 * q + (grow & 15)) : W8 + grow * Kd + 16 * q;
+        }
+    }
+    // whether load j of a K slab is issued (MX: not the spare weight-side ones)
+    auto k_issued = [](int j) { return !MX || j < MX_REAL || j >= LPW_A; };
+    // source of issued load j of K slab kt (kt < nk)
+    auto ksrc = [&](int j, int kt) -> const void * {
+        if constexpr (MX) {
+            if (j < MX_REAL) {
+                const int64_t off = WP ? (int64_t)(kt >> 2) * 2048 + (kt & 3) * 256 : (int64_t)kt * kTileBK;
+                return mx_src[j] + off;
+            }
+        }
+        return src[j] + kt * src_step(j);
+    };
     const int nk = (int)((Kd + kTileBK - 1) / kTileBK);
     const int rs = (p.r + kTileBK - 1) / kTileBK;  // LoRA slabs per adapter
     typedef __attribute__((address_space(3))) unsigned char lds_t;
@@ -276,8 +407,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             const int64_t k0 = (int64_t)kt * kTileBK;
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
-                const bool kin = (j < LPW_A ? WP : B_PACKED) || k0 + chunk_of[j] * 8 < Kd;
-                dma(kin ? (const void *)(src[j] + kt * src_step(j)) : (const void *)g_zero_chunk, stage, j);
+                if (!k_issued(j)) continue;
+                // MX weights: K is a multiple of 32, every slab is whole
+                const bool kin = (j < LPW_A ? (WP || MX) : B_PACKED) || k0 + chunk_of[j] * 8 < Kd;
+                dma(kin ? ksrc(j, kt) : (const void *)g_zero_chunk, stage, j);
             }
             return;
         }
@@ -317,30 +450,70 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
 
     const int a_row0 = wm * (BW / 2) + l32;        // + mt*32
     const int b_row0 = BW + wn * 32 + l32;         // + nt*64
-    // Fragment reads of one 16-wide k-step (NTL live column tiles) and its MFMAs.
-    auto rd = [&](auto ntl, u32x4 *af, u32x4 *bfr, int stage, int ks) {
+    // MX fragments: lane (l32, lh) of row tile mt reads the eight codes
+    // 16 ks + 8 lh .. + 7 of tile row a_row0 + 32 mt and, at ks = 0, the
+    // row's scale byte of the slab; mx_cvt turns them into the bf16 fragment,
+    // exactly (E4M3 times a power of two fits bf16).  The scale stays a byte
+    // until the conversion, so no instruction waits on its read before then.
+    int mx_soff[MT];     // LDS offset of the row's scale of K block 0
+    uint32_t mx_scl[MT]; // scale byte of the slab last read at ks = 0
+    if constexpr (MX) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int tr = a_row0 + mt * 32;
+            const int u = GU ? ((tr >> 1) & 1) : 0;                   // gate or up run
+            const int q = GU ? 2 * (tr >> 2) + (tr & 1) : tr;        // row within the run
+            mx_soff[mt] = u * RUN_BYTES + 16 + mx_off16[u] + q * nb;
+            mx_scl[mt] = 0u;
+        }
+    }
+    auto mx_rd_raw = [&](uint2 &r, const unsigned char *base, int mt, int ks, int slab) {
+        r = *reinterpret_cast<const uint2 *>(base + ((a_row0 + mt * 32) >> 5) * 1024 + ks * 512 + l32 * 16 + lh * 8);
+        if (ks == 0) mx_scl[mt] = mx_sc[mx_soff[mt] + slab];
+    };
+    // r's codes times 2^(scale - 127), `bits` = scale << 23 (that power of two in fp32)
+    auto mx_cvt_bits = [&](u32x4 &a, uint2 r, uint32_t bits) {
+        const float sc = __uint_as_float(bits);
+        a[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, false));
+        a[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, sc, true));
+        a[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, false));
+        a[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, sc, true));
+    };
+    auto mx_cvt_to = [&](u32x4 &a, uint2 r, int mt) { mx_cvt_bits(a, r, mx_scl[mt] << 23); };
+    // the drain keeps a K slab's codes in dwords 0, 1 of the fragment itself
+    auto mx_rd = [&](u32x4 &a, const unsigned char *base, int mt, int ks, int slab) {
+        uint2 r;
+        mx_rd_raw(r, base, mt, ks, slab);
+        a[0] = r.x;
+        a[1] = r.y;
+    };
+    auto mx_cvt = [&](u32x4 &a, int mt) { mx_cvt_to(a, make_uint2(a[0], a[1]), mt); };
+    // Fragment reads of one 16-wide k-step (NTL live column tiles) of slab
+    // `slab` held in ring stage `stage`, and its MFMAs.
+    auto rd = [&](auto ntl, u32x4 *af, u32x4 *bfr, int stage, int ks, int slab) {
         constexpr int NTL = decltype(ntl)::value;
         const unsigned char *base = lds + stage * STAGE_BYTES;
         const int c = ks * 2 + lh;
+        if (MX && slab < nk) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            af[mt] = *reinterpret_cast<const u32x4 *>(base + lds_off<WP>(a_row0 + mt * 32, c));
+            for (int mt = 0; mt < MT; ++mt) mx_rd(af[mt], base, mt, ks, slab);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                af[mt] = *reinterpret_cast<const u32x4 *>(base + lds_off<WP>(a_row0 + mt * 32, c));
+        }
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt)
             bfr[nt] = *reinterpret_cast<const u32x4 *>(base + lds_off<B_PACKED>(b_row0 + nt * 64, c));
     };
-    auto mm = [&](auto ntl, const u32x4 *af, const u32x4 *bfr) {
+    // mm restricted to the column tiles set in `live` (wave-uniform); `cvt`:
+    // the A fragments still hold MX codes
+    auto mm_live = [&](auto ntl, u32x4 *af, const u32x4 *bfr, int live, bool cvt) {
         constexpr int NTL = decltype(ntl)::value;
+        if (MX && cvt) {
 #pragma unroll
-        for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mt]), as_bf16x8(bfr[nt]),
-                                                                      acc[mt][nt], 0, 0, 0);
-    };
-    // mm restricted to the column tiles set in `live` (wave-uniform)
-    auto mm_live = [&](auto ntl, const u32x4 *af, const u32x4 *bfr, int live) {
-        constexpr int NTL = decltype(ntl)::value;
+            for (int mt = 0; mt < MT; ++mt) mx_cvt(af[mt], mt);
+        }
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
             if (!((live >> nt) & 1)) continue;
@@ -350,8 +523,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
                                                                       acc[mt][nt], 0, 0, 0);
         }
     };
-    // Single steps of the above: fragment read i (A fragments first, then B)
-    // and MFMA i (column tile i / MT, row tile i % MT).
+    // Single steps of the above for K slabs: fragment read i (A fragments
+    // first, then B) and MFMA i (column tile i / MT, row tile i % MT).
     auto rd_one = [&](auto i, u32x4 *af, u32x4 *bfr, const unsigned char *base, int ks) {
         constexpr int I = decltype(i)::value;
         const int c = ks * 2 + lh;
@@ -369,10 +542,12 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // a wait longer, never shorter.
     auto wait_slab = [&](int younger) {
         static_assert(kStages <= 6, "extend the wait ladder");
-        if (younger >= 4) wait_vm_barrier<4 * LPW>();
-        else if (younger == 3) wait_vm_barrier<3 * LPW>();
-        else if (younger == 2) wait_vm_barrier<2 * LPW>();
-        else if (younger == 1) wait_vm_barrier<LPW>();
+        // per younger slab the fewest loads a slab issues (LoRA slabs issue
+        // LPW >= LPW_K): a wait that counts low only waits longer
+        if (younger >= 4) wait_vm_barrier<4 * LPW_K>();
+        else if (younger == 3) wait_vm_barrier<3 * LPW_K>();
+        else if (younger == 2) wait_vm_barrier<2 * LPW_K>();
+        else if (younger == 1) wait_vm_barrier<LPW_K>();
         else wait_vm_barrier<0>();
     };
 
@@ -424,15 +599,25 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     auto mainloop = [&](auto ntl) {
         u32x4 a0[MT], b0[NT], a1[MT], b1[NT];
         wait_slab(min(kStages - 2, nk_tot - 1));
-        rd(ntl, a0, b0, 0, 0);
+        if constexpr (MX) {
+            // every scale copy has landed (older than slab 0): the tail bytes
+#pragma unroll
+            for (int u = 0; u < NRUN; ++u) {
+                const int k = tid - 16 * u;
+                if (k >= 0 && k < mx_tail[u]) mx_sc[u * RUN_BYTES + 16 + 16 * mx_nch[u] + k] = (unsigned char)mx_byte;
+            }
+            lds_barrier();
+        }
+        rd(ntl, a0, b0, 0, 0, 0);
         int kt = 0;
+        constexpr int NTL = decltype(ntl)::value;
+        constexpr int NMM = MT * NTL, NRD = MT + NTL;
+        if constexpr (!MX) {
         // Steady state, one slab per iteration.  Instruction order is fixed by hand (a scheduling barrier after each
         // step): MFMA i of a k-step is followed by fragment read i of the next
         // k-step and, after the barrier, by one slab copy, so the wave keeps
         // its matrix core fed while the reads and copies issue between MFMAs
         // instead of in blocks (measured ~8% faster than blocked issue).
-        constexpr int NTL = decltype(ntl)::value;
-        constexpr int NMM = MT * NTL, NRD = MT + NTL;
         for (; kt + kStages - 1 < nk_full; ++kt) {
             const unsigned char *cur = lds + (kt % kStages) * STAGE_BYTES;
             const unsigned char *nxt = lds + ((kt + 1) % kStages) * STAGE_BYTES;
@@ -451,7 +636,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             static_for<NMM>([&](auto i) {
                 mm_one(i, a1, b1);
                 if constexpr (i < NRD) rd_one(i, a0, b0, nxt, 0);
-                else if constexpr (i - NRD < LPW) dma(src[i - NRD] + kfill * src_step(i - NRD), fill, i - NRD);
+                else if constexpr (i - NRD < LPW) dma(ksrc(i - NRD, kfill), fill, i - NRD);
                 __builtin_amdgcn_sched_barrier(0);
             });
             if constexpr (NMM < NRD) {
@@ -461,9 +646,114 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             if constexpr (DONE < LPW) {
                 static_for<LPW - DONE>([&](auto i) {
                     constexpr int j = DONE + decltype(i)::value;
-                    dma(src[j] + kfill * src_step(j), fill, j);
+                    dma(ksrc(j, kfill), fill, j);
                 });
             }
+        }
+        } else {
+        // MXFP8 steady state: the step plan of MxSched, one set of codes `r`
+        // and one set of converted fragments (a0); each fragment is converted
+        // NTL - 1 MFMAs before its first use, so no conversion stands
+        // between two MFMAs of the matrix core's queue.  Four slabs per
+        // iteration: sc4[mt] holds the scale bytes of the group's four slabs
+        // for row tile mt (byte j: slab g + j), refreshed once per group with
+        // one aligned 8-byte LDS read (one scale-byte read per row tile and
+        // slab measured ~5% slower on the prefill GEMMs).
+        using S = MxSched<MT, NTL>;
+        uint2 r[MT];
+        uint32_t sc4[MT];
+        // scale bytes of slabs g .. g+3 of row tile mt (g a multiple of 4)
+        auto rd_sc4 = [&](int mt, int g) {
+            const int pos = mx_soff[mt] + g;
+            const uint2 v = *reinterpret_cast<const uint2 *>(mx_sc + (pos & ~3));
+            return __builtin_amdgcn_alignbyte(v.y, v.x, (uint32_t)(pos & 3));
+        };
+        auto sbits = [&](int mt, int j) { return ((sc4[mt] >> (8 * j)) & 0xffu) << 23; };
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            r[mt] = make_uint2(a0[mt][0], a0[mt][1]);
+            sc4[mt] = rd_sc4(mt, 0);
+        }
+        if constexpr (NTL > 0) mx_cvt_bits(a0[0], r[0], sbits(0, 0));
+        // issued load d of a K slab: weight-side d < MX_REAL, then the token side
+        auto jd = [](int d) { return d < MX_REAL ? d : d - MX_REAL + LPW_A; };
+        // One k-step of slab g + J on B fragments bc, reading the next k-step
+        // (codes and B fragments bn, at ks / slab) from stage `src`.  Its
+        // fragments convert with scale byte J, the next k-step's row tile 0
+        // with byte JN; SECOND: also the slab copies of slab kfill into
+        // `fill`, and with REFRESH the scale bytes of the next group (slab
+        // `slab`), each read after this k-step's last use of the old ones.
+        auto kstep = [&](auto second, auto refresh, int J, int JN, const u32x4 *bc, u32x4 *bn,
+                         const unsigned char *src, int ks, int slab, lds_t *fill, int kfill) {
+            constexpr bool SECOND = decltype(second)::value, REFRESH = decltype(refresh)::value;
+            static_for<NMM>([&](auto i) {
+                constexpr int I = decltype(i)::value, mt = I / NTL, nt = I % NTL;
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0[mt]), as_bf16x8(bc[nt]),
+                                                                      acc[mt][nt], 0, 0, 0);
+                if constexpr (nt == 0 && mt + 1 < MT) mx_cvt_bits(a0[mt + 1], r[mt + 1], sbits(mt + 1, J));
+                if constexpr (I == S::CV0) mx_cvt_bits(a0[0], r[0], sbits(0, JN));
+                static_for<MT>([&](auto m) {
+                    constexpr int M = decltype(m)::value;
+                    if constexpr (S::ra(M) == I) {
+                        r[M] = *reinterpret_cast<const uint2 *>(src + ((a_row0 + M * 32) >> 5) * 1024 + ks * 512 +
+                                                                l32 * 16 + lh * 8);
+                        if constexpr (REFRESH) sc4[M] = rd_sc4(M, slab);
+                    }
+                });
+                static_for<NTL>([&](auto n) {
+                    constexpr int N_ = decltype(n)::value;
+                    if constexpr (S::rb(N_) == I)
+                        bn[N_] = *reinterpret_cast<const u32x4 *>(src + lds_off<B_PACKED>(b_row0 + N_ * 64, ks * 2 + lh));
+                });
+                if constexpr (SECOND) {
+                    static_for<LPW_K>([&](auto d) {
+                        if constexpr (S::dstep(decltype(d)::value) == I) dma(ksrc(jd(decltype(d)::value), kfill), fill, jd(decltype(d)::value));
+                    });
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (SECOND) {
+                static_for<LPW_K>([&](auto d) {
+                    if constexpr (S::dstep(decltype(d)::value) < 0) dma(ksrc(jd(decltype(d)::value), kfill), fill, jd(decltype(d)::value));
+                });
+            }
+        };
+        for (; kt + 3 + kStages - 1 < nk_full; kt += 4) {
+            static_for<4>([&](auto jj) {
+                constexpr int J = decltype(jj)::value;
+                const int sl = kt + J;
+                const unsigned char *cur = lds + (sl % kStages) * STAGE_BYTES;
+                const unsigned char *nxt = lds + ((sl + 1) % kStages) * STAGE_BYTES;
+                lds_t *fill = lds_base + ((sl + kStages - 1) % kStages) * STAGE_BYTES;
+                kstep(std::false_type{}, std::false_type{}, J, J, b0, b1, cur, 1, sl, fill, 0);
+                wait_vm_barrier<(kStages - 3) * LPW_K>();
+                __builtin_amdgcn_sched_barrier(0);
+                kstep(std::true_type{}, std::integral_constant<bool, J == 3>{}, J, (J + 1) & 3, b1, b0, nxt, 0, sl + 1,
+                      fill, sl + kStages - 1);
+            });
+        }
+        // The last (at most 3) slabs of the steady state, one per iteration:
+        // sc4 already holds their scale bytes (group g), picked at run time.
+        const int g = kt;
+        for (; kt + kStages - 1 < nk_full; ++kt) {
+            const unsigned char *cur = lds + (kt % kStages) * STAGE_BYTES;
+            const unsigned char *nxt = lds + ((kt + 1) % kStages) * STAGE_BYTES;
+            lds_t *fill = lds_base + ((kt + kStages - 1) % kStages) * STAGE_BYTES;
+            const int j = kt - g;
+            kstep(std::false_type{}, std::false_type{}, j, j, b0, b1, cur, 1, kt, fill, 0);
+            wait_vm_barrier<(kStages - 3) * LPW_K>();
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(std::true_type{}, std::false_type{}, j, j + 1, b1, b0, nxt, 0, kt + 1, fill, kt + kStages - 1);
+        }
+        // the drain converts slab kt's codes with its scale byte kt - g
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) mx_scl[mt] = (sc4[mt] >> (8 * (kt - g))) & 0xffu;
+        // the drain reads a K slab's codes from dwords 0, 1 of its fragments
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            a0[mt][0] = r[mt].x;
+            a0[mt][1] = r[mt].y;
+        }
         }
         // The rest: the drain of the ring and the LoRA slabs.  A LoRA slab
         // adds nonzero products only on its adapter's run of rows, so the
@@ -482,15 +772,21 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
                     if (c0 < hi && c0 + 32 > lo) live |= 1 << nt;
                 }
             }
-            rd(ntl, a1, b1, kt % kStages, 1);
-            mm_live(ntl, a0, b0, live);
+            // MX: both fragment sets of a K slab convert with its scale, a0's
+            // and a1's before the reads of the next slab replace it
+            rd(ntl, a1, b1, kt % kStages, 1, kt);
+            mm_live(ntl, a0, b0, live, kt < nk);
+            if (MX && kt < nk) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) mx_cvt(a1[mt], mt);
+            }
             if (kt + 1 < nk_tot) {
                 // issued so far: slabs 0 .. min(kt + kStages - 2, nk_tot - 1)
                 wait_slab(min(kStages - 3, nk_tot - 2 - kt));
                 if (kt + kStages - 1 < nk_tot) issue(kt + kStages - 1);
-                rd(ntl, a0, b0, (kt + 1) % kStages, 0);
+                rd(ntl, a0, b0, (kt + 1) % kStages, 0, kt + 1);
             }
-            mm_live(ntl, a1, b1, live);
+            mm_live(ntl, a1, b1, live, false);
         }
     };
     switch (nt_live) {

@@ -478,14 +478,27 @@ void launch_shrink(const Plan &pl, ShrinkParams sp, bool gather, int r, hipStrea
 }
 
 
-template <int BW, int BT, bool GU, bool WP>
+template <int BW, int BT, bool GU, bool WP, bool MX>
 void launch_tiled(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
                   const int32_t *xsplit, hipStream_t st) {
     const int n_wt = (gp.Nout + (GU ? BW / 2 : BW) - 1) / (GU ? BW / 2 : BW);
     // every XCD may take up to xcap items of the cost-balanced ranges
     const unsigned total = (unsigned)(8 * tiled_xcap(pl, n_wt));
-    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU, WP>), dim3(total), dim3(256), 0, st, gp, tiles, ntiles, n_wt,
-                       xsplit + (GU ? 0 : 16));
+    hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU, WP, MX>), dim3(total), dim3(256), 0, st, gp, tiles, ntiles,
+                       n_wt, xsplit + (GU ? 0 : 16));
+}
+
+template <bool GU, bool WP, bool MX>
+void launch_tiled_shape(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
+                        const int32_t *queue, hipStream_t st) {
+    const int bw = tiled_bw(gp.Nout, GU);
+    if (pl.tile == 128) {
+        if (bw == 256) launch_tiled<256, 128, GU, WP, MX>(pl, gp, tiles, ntiles, queue, st);
+        else launch_tiled<128, 128, GU, WP, MX>(pl, gp, tiles, ntiles, queue, st);
+    } else {
+        if (bw == 256) launch_tiled<256, 256, GU, WP, MX>(pl, gp, tiles, ntiles, queue, st);
+        else launch_tiled<128, 256, GU, WP, MX>(pl, gp, tiles, ntiles, queue, st);
+    }
 }
 
 template <bool GU, bool WP>
@@ -498,21 +511,20 @@ void launch_gemm_wp(const Plan &pl, const GemmParams &gp, const int32_t *tiles, 
         else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, WP>), grid, block, 0, st, gp);
         return;
     }
-    const int bw = tiled_bw(gp.Nout, GU);
-    if (pl.tile == 128) {
-        if (bw == 256) launch_tiled<256, 128, GU, WP>(pl, gp, tiles, ntiles, queue, st);
-        else launch_tiled<128, 128, GU, WP>(pl, gp, tiles, ntiles, queue, st);
-    } else {
-        if (bw == 256) launch_tiled<256, 256, GU, WP>(pl, gp, tiles, ntiles, queue, st);
-        else launch_tiled<128, 256, GU, WP>(pl, gp, tiles, ntiles, queue, st);
-    }
+    launch_tiled_shape<GU, WP, false>(pl, gp, tiles, ntiles, queue, st);
 }
 
 template <bool GU>
 void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
                  const int32_t *queue, bool wp, hipStream_t st) {
+    if (gp.Wscale != nullptr && pl.kind == 2) {
+        // MXFP8 weights, many rows per expert: H, I <= 32 kMxTiledMaxBlocks (checked by moe_lora_check_args)
+        if (wp) launch_tiled_shape<GU, true, true>(pl, gp, tiles, ntiles, queue, st);
+        else launch_tiled_shape<GU, false, true>(pl, gp, tiles, ntiles, queue, st);
+        return;
+    }
     if (gp.Wscale != nullptr) {
-        // MXFP8 weights: the streaming kernel only (checked by moe_lora_check_args)
+        // MXFP8 weights, few rows per expert: the streaming kernel (kind 1; kind 0 is checked out)
         const int tile = GU ? kStreamBW / 2 : kStreamBW;
         const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
         if (wp) {
@@ -583,8 +595,11 @@ int moe_lora_check_args(const moe_lora_dims *d, const moe_lora_args *a) {
     if (a->weights_mxfp8) {
         if (!a->w13_scale || !a->w2_scale || !aligned(a->w13_scale, 16) || !aligned(a->w2_scale, 16))
             return MOE_LORA_EINVAL;
-        if (d->dtype != MOE_LORA_BF16 || d->H % 32 != 0 || d->I % 32 != 0 || p.kind != 1 ||
-            d->H > 32 * kMxMaxBlocks || d->I > 32 * kMxMaxBlocks)
+        // the streaming GEMM holds a row's scales for K <= 32 kMxMaxBlocks, the
+        // tiled one for K <= 32 kMxTiledMaxBlocks
+        const int64_t kmax = 32 * (p.kind == 2 ? kMxTiledMaxBlocks : kMxMaxBlocks);
+        if (d->dtype != MOE_LORA_BF16 || d->H % 32 != 0 || d->I % 32 != 0 || p.kind == 0 || d->H > kmax ||
+            d->I > kmax)
             return MOE_LORA_EUNSUPPORTED;
     }
     return MOE_LORA_OK;

@@ -140,15 +140,21 @@ def test_check_args_mxfp8_flag():
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, w13_scale=0xb000)) == ml.MOE_LORA_EINVAL
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, w13_scale=0xb004, w2_scale=0xc000)) == ml.MOE_LORA_EINVAL
     assert ml.moe_lora_check_args(_dims(H=8224), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
-    # bf16 only, H and I multiples of 32, streaming GEMM only; packed codes allowed
+    # bf16 only, H and I multiples of 32; packed codes allowed
     assert ml.moe_lora_check_args(_dims(dtype="f32"), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
     assert ml.moe_lora_check_args(d, _args(weights_mxfp8=1, weights_packed=1, **sc)) == ml.MOE_LORA_OK
     assert ml.moe_lora_check_args(_dims(H=2888), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
     assert ml.moe_lora_check_args(_dims(I=2888), _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
+    # the LDS-tiled GEMM takes K (H for gate_up, I for down) up to 3072, the
+    # streaming one up to 8192
     big = _dims(T=4096, L=32, r=32)
     assert ml.moe_lora_plan_query(big)["gemm_kind"] == 2
-    assert ml.moe_lora_check_args(big, _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_EUNSUPPORTED
-    assert ml.moe_lora_check_args(_dims(T=4096, L=32, r=32, block_m=32), _args(weights_mxfp8=1, **sc)) == 0
+    assert ml.moe_lora_check_args(big, _args(weights_mxfp8=1, **sc)) == ml.MOE_LORA_OK
+    for H, I in ((3072, 3072), (3104, 2880), (2880, 3104)):
+        want = ml.MOE_LORA_OK if max(H, I) <= 3072 else ml.MOE_LORA_EUNSUPPORTED
+        assert ml.moe_lora_check_args(_dims(T=4096, H=H, I=I, L=32, r=32), _args(weights_mxfp8=1, **sc)) == want
+        assert ml.moe_lora_check_args(_dims(T=4096, H=H, I=I, L=32, r=32, block_m=32),
+                                      _args(weights_mxfp8=1, **sc)) == 0
     # the flag off ignores the scale pointers
     assert ml.moe_lora_check_args(d, _args()) == ml.MOE_LORA_OK
 
