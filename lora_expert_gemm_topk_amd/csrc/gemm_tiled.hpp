@@ -390,55 +390,22 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         return src[j] + kt * src_step(j);
     };
     const int nk = (int)((Kd + kTileBK - 1) / kTileBK);
-    const int rs = (p.r + kTileBK - 1) / kTileBK;  // LoRA slabs per adapter
     typedef __attribute__((address_space(3))) unsigned char lds_t;
     lds_t *lds_base = (lds_t *)lds;
     auto dma = [&](const void *g, lds_t *stage, int j) { dma16(g, stage + (w + 4 * j) * 1024); };
     // Slab kt < nk: K columns [32 kt, 32 kt + 32) of the weights and tokens.
-    // Slab nk + q (LoRA expand, aitrends.kr summary of the AWS multi-LoRA MoE
-    // post, "section details": the LoRA sum folded into the expand step):
-    // rank columns [32 rc, 32 rc + 32) of adapter alist[q / rs], rc = q % rs;
-    // the weight side holds B13/B2 rows of (adapter, expert), the token side
-    // the bf16 shrink rows of the tokens carrying that adapter and zeros for
-    // every other token, so the same MFMAs add exactly the expand term.
     auto issue = [&](int kt) {
         lds_t *stage = lds_base + (kt % kStages) * STAGE_BYTES;
-        if (kt < nk) {
-            const int64_t k0 = (int64_t)kt * kTileBK;
-#pragma unroll
-            for (int j = 0; j < LPW; ++j) {
-                if (!k_issued(j)) continue;
-                // MX weights: K is a multiple of 32, every slab is whole
-                const bool kin = (j < LPW_A ? (WP || MX) : B_PACKED) || k0 + chunk_of[j] * 8 < Kd;
-                dma(kin ? ksrc(j, kt) : (const void *)g_zero_chunk, stage, j);
-            }
-            return;
-        }
-        const int q = kt - nk;
-        const int ai = q / rs;
-        const int kk0 = (q - ai * rs) * kTileBK;
-        const int a = __builtin_amdgcn_readfirstlane(alist[ai]);
-        const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r;
-        const uint16_t *s16 = reinterpret_cast<const uint16_t *>(p.s_part);
+        const int64_t k0 = (int64_t)kt * kTileBK;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            // token groups of a packed-layout stage take lane l as (row l%16,
-            // chunk l/16), the block order the fragment reads expect
-            const bool pk = j < LPW_A ? WP : B_PACKED;
-            const int rr = (w + 4 * j) * 16 + (pk ? (lane & 15) : (lane >> 2));
-            const int kk = kk0 + (pk ? (lane >> 4) : chunk_of[j]) * 8;
-            const void *g = g_zero_chunk;
-            if (j < LPW_A) {
-                bool ok;
-                const int grow = tile_weight_row<GU>(rr, i0, N, ok);
-                if (ok && kk < p.r) g = Bae + (int64_t)grow * p.r + kk;
-            } else {
-                const int j_tok = rr - BW;
-                if (j_tok < nrows && kk < p.r && tok_a[j_tok] == a) g = s16 + (int64_t)(row0 + j_tok) * p.r + kk;
-            }
-            dma(g, stage, j);
+            if (!k_issued(j)) continue;
+            // MX weights: K is a multiple of 32, every slab is whole
+            const bool kin = (j < LPW_A ? (WP || MX) : B_PACKED) || k0 + chunk_of[j] * 8 < Kd;
+            dma(kin ? ksrc(j, kt) : (const void *)g_zero_chunk, stage, j);
         }
     };
+    const int rs = (p.r + kTileBK - 1) / kTileBK;  // 32-rank slabs per adapter
 
     f32x16 acc[MT][NT];
 #pragma unroll
@@ -551,8 +518,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         else wait_vm_barrier<0>();
     };
 
-    // Ring prologue: the K slabs first; the adapter list is built while they
-    // are in flight, then any LoRA slabs the prologue still has to issue.
+    // Ring prologue: the K slabs; the adapter list is built while they are
+    // in flight.
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
         if (s < nk) issue(s);
@@ -580,10 +547,6 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         lds_barrier();
     }
     const int n_adapters = __builtin_amdgcn_readfirstlane(wcnt[4]);
-    const int nk_tot = nk + (p.lora ? n_adapters * rs : 0);
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s >= nk && s < nk_tot) issue(s);
 
     // The whole K loop, specialised on the live column tiles so it has no
     // branches.  Two fragment register sets alternate: while the MFMAs of one
@@ -596,9 +559,133 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // lie wholly inside K, so it needs no slab-kind or end-of-K branches and
     // is one basic block (measured ~15% faster than one loop with them).
     const int nk_full = (int)(Kd / kTileBK);
+
+    // ---- LoRA expand (aitrends.kr summary of the AWS multi-LoRA MoE post,
+    // "section details": the LoRA sum folded into the expand step) ---------
+    // After the K loop, each adapter present in the token tile adds
+    // B[a, e] (its rows of this weight tile) times the bf16 shrink rows of
+    // its tokens, as MFMAs on the same accumulators.  The ring, now free,
+    // streams only the weight side: unit u = (adapter q, 32-rank slab) is
+    // BW rows x 32 ranks, kStages*STAGE_BYTES / (BW*64) units fit, so many
+    // more are in flight than whole slabs would allow.  Each lane holds its
+    // tokens' shrink rows in registers for 64 ranks at a time (read once per
+    // tile) and zeroes those of other adapters before each MFMA; the MFMAs
+    // of column tiles outside the adapter's run of rows (exact zeros) are
+    // skipped.  Units go in adapter order, ranks ascending, so the sums are
+    // those of the same products in the same order as full LoRA slabs.
+    const uint16_t *s16 = reinterpret_cast<const uint16_t *>(p.s_part);
+    auto lora_phase = [&](auto ntl) {
+        constexpr int NTL = decltype(ntl)::value;
+        constexpr int UBYTES = BW * 64;                          // one unit: BW rows x 32 bf16 ranks
+        constexpr int NSLOT = kStages * STAGE_BYTES / UBYTES;    // units the ring holds
+        static_assert(NSLOT >= 3 && NSLOT <= 12, "LoRA unit ring depth");
+        // wait for unit u with `younger` later units still in flight, then barrier
+        auto wait_unit = [&](int younger) {
+            switch (younger) {
+                case 0: wait_vm_barrier<0>(); break;
+                case 1: wait_vm_barrier<LPW_A>(); break;
+                case 2: wait_vm_barrier<2 * LPW_A>(); break;
+                case 3: wait_vm_barrier<3 * LPW_A>(); break;
+                case 4: wait_vm_barrier<4 * LPW_A>(); break;
+                case 5: wait_vm_barrier<5 * LPW_A>(); break;
+                case 6: wait_vm_barrier<6 * LPW_A>(); break;
+                case 7: wait_vm_barrier<7 * LPW_A>(); break;
+                case 8: wait_vm_barrier<8 * LPW_A>(); break;
+                case 9: wait_vm_barrier<9 * LPW_A>(); break;
+                default: wait_vm_barrier<10 * LPW_A>(); break;
+            }
+        };
+        int myad[NTL > 0 ? NTL : 1];  // adapter of this lane's token in column tile nt
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) myad[nt] = tok_a[(2 * nt + wn) * 32 + l32];
+        // every wave is past its last fragment read of the ring's K slabs
+        lds_barrier();
+        for (int c0 = 0; c0 < rs; c0 += 2) {      // ranks [32 c0, 32 c0 + 64)
+            const int uc = min(2, rs - c0);        // 32-rank slabs per adapter in this range
+            const int nu = n_adapters * uc;
+            // weight side of unit u: rows as the weight groups of a slab (the
+            // packed-layout block order with packed weights), ranks 32 rc ..
+            auto issue_unit = [&](int u) {
+                const int q = u / uc, rc = c0 + (u - q * uc);
+                const int a = __builtin_amdgcn_readfirstlane(alist[q]);
+                const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r;
+                lds_t *slot = lds_base + (u % NSLOT) * UBYTES;
+#pragma unroll
+                for (int j = 0; j < LPW_A; ++j) {
+                    const int rr = (w + 4 * j) * 16 + (WP ? (lane & 15) : (lane >> 2));
+                    const int kk = rc * kTileBK + (WP ? (lane >> 4) : chunk_of[j]) * 8;
+                    bool ok;
+                    const int grow = tile_weight_row<GU>(rr, i0, N, ok);
+                    const void *g = (ok && kk < p.r) ? (const void *)(Bae + (int64_t)grow * p.r + kk)
+                                                     : (const void *)g_zero_chunk;
+                    dma(g, slot, j);
+                }
+            };
+            const int npre = min(nu, NSLOT - 1);
+            for (int u = 0; u < npre; ++u) issue_unit(u);
+            // shrink rows: lane (l32, lh) of column tile nt holds ranks
+            // 32 c0 + 16 kq + 8 lh .. + 7 of tile row (2 nt + wn) 32 + l32
+            u32x4 sfr[NTL > 0 ? NTL : 1][4];
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                const int jt = (2 * nt + wn) * 32 + l32;
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) {
+                    const int k = c0 * kTileBK + kq * 16 + lh * 8;
+                    sfr[nt][kq] = ld16(s16 + (int64_t)(row0 + min(jt, nrows - 1)) * p.r + k, jt < nrows && k < p.r);
+                }
+            }
+            // wait for the shrink rows here (with the units issued above),
+            // not at a first use after later unit copies
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) asm volatile("" ::"v"(sfr[nt][kq]));
+            for (int q = 0; q < n_adapters; ++q) {
+                const int a = __builtin_amdgcn_readfirstlane(alist[q]);
+                const int lo = __builtin_amdgcn_readfirstlane(arun[2 * q]);
+                const int hi = __builtin_amdgcn_readfirstlane(arun[2 * q + 1]);
+#pragma unroll
+                for (int rcl = 0; rcl < 2; ++rcl) {
+                    if (rcl >= uc) break;
+                    const int u = q * uc + rcl;
+                    // issued so far: units 0 .. min(u + NSLOT - 2, nu - 1)
+                    wait_unit(min(NSLOT - 2, nu - 1 - u));
+                    // into the slot of unit u - 1, which every wave is done with
+                    if (u + NSLOT - 1 < nu) issue_unit(u + NSLOT - 1);
+                    const unsigned char *slot = lds + (u % NSLOT) * UBYTES;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if ((c0 + rcl) * kTileBK + ks * 16 >= p.r) break;  // ranks past r
+                        u32x4 af[MT];
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            af[mt] = *reinterpret_cast<const u32x4 *>(slot + lds_off<WP>(a_row0 + mt * 32, ks * 2 + lh));
+#pragma unroll
+                        for (int nt = 0; nt < NTL; ++nt) {
+                            const int cr = (2 * nt + wn) * 32;
+                            if (!(cr < hi && cr + 32 > lo)) continue;
+                            const u32x4 sv = sfr[nt][rcl * 2 + ks];
+                            const bool mine = myad[nt] == a;
+                            u32x4 bv;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) bv[i] = mine ? sv[i] : 0u;
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt)
+                                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mt]), as_bf16x8(bv),
+                                                                                      acc[mt][nt], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            // the next rank range (or the epilogue) reuses the ring
+            lds_barrier();
+        }
+    };
+
     auto mainloop = [&](auto ntl) {
         u32x4 a0[MT], b0[NT], a1[MT], b1[NT];
-        wait_slab(min(kStages - 2, nk_tot - 1));
+        wait_slab(min(kStages - 2, nk - 1));
         if constexpr (MX) {
             // every scale copy has landed (older than slab 0): the tail bytes
 #pragma unroll
@@ -755,39 +842,26 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             a0[mt][1] = r[mt].y;
         }
         }
-        // The rest: the drain of the ring and the LoRA slabs.  A LoRA slab
-        // adds nonzero products only on its adapter's run of rows, so the
-        // MFMAs of column tiles outside that run (which would add exact zeros)
-        // are skipped.
-        for (; kt < nk_tot; ++kt) {
-            int live = (1 << NTL) - 1;
-            if (kt >= nk) {
-                const int ai = (kt - nk) / rs;
-                const int lo = __builtin_amdgcn_readfirstlane(arun[2 * ai]);
-                const int hi = __builtin_amdgcn_readfirstlane(arun[2 * ai + 1]);
-                live = 0;
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) {
-                    const int c0 = (2 * nt + wn) * 32;
-                    if (c0 < hi && c0 + 32 > lo) live |= 1 << nt;
-                }
-            }
+        // The rest: the drain of the ring.
+        for (; kt < nk; ++kt) {
+            const int live = (1 << NTL) - 1;
             // MX: both fragment sets of a K slab convert with its scale, a0's
             // and a1's before the reads of the next slab replace it
             rd(ntl, a1, b1, kt % kStages, 1, kt);
-            mm_live(ntl, a0, b0, live, kt < nk);
-            if (MX && kt < nk) {
+            mm_live(ntl, a0, b0, live, true);
+            if constexpr (MX) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) mx_cvt(a1[mt], mt);
             }
-            if (kt + 1 < nk_tot) {
-                // issued so far: slabs 0 .. min(kt + kStages - 2, nk_tot - 1)
-                wait_slab(min(kStages - 3, nk_tot - 2 - kt));
-                if (kt + kStages - 1 < nk_tot) issue(kt + kStages - 1);
+            if (kt + 1 < nk) {
+                // issued so far: slabs 0 .. min(kt + kStages - 2, nk - 1)
+                wait_slab(min(kStages - 3, nk - 2 - kt));
+                if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
                 rd(ntl, a0, b0, (kt + 1) % kStages, 0, kt + 1);
             }
             mm_live(ntl, a1, b1, live, false);
         }
+        if (p.lora && n_adapters > 0) lora_phase(ntl);
     };
     switch (nt_live) {
         case 0: mainloop(std::integral_constant<int, 0>{}); break;
