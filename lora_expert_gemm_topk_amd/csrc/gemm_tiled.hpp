@@ -71,6 +71,10 @@ constexpr int kTileBK = 32;   // K per LDS stage
 #define MOELORA_TILED_STAGES 4
 #endif
 constexpr int kStages = MOELORA_TILED_STAGES;  // LDS ring depth
+#ifndef MOELORA_SKEW_PANEL
+#define MOELORA_SKEW_PANEL 1
+#endif
+constexpr int kSkewPanel = MOELORA_SKEW_PANEL;  // token tiles per XCD panel in the skewed work order
 static_assert(kStages >= 3, "the K loop keeps at least two slabs in flight");
 // MXFP8 weights in the tiled kernel: most 32-element scale blocks per row
 // (K <= 3072), so the tile's scale rows fit in LDS beside the ring
@@ -236,9 +240,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     const bool skewed = 2 * n_tiles[0] < n_tiles[1] * n_tiles[2];
     int wt, ti;
     if (skewed) {
-        if ((int)blockIdx.x >= live) return;
-        wt = (int)blockIdx.x % n_wtiles;
-        ti = (int)blockIdx.x / n_wtiles;
+        // token tiles in panels of kSkewPanel consecutive tiles, the panels
+        // dealt to the XCDs in turn; an XCD runs a panel's items weight tile
+        // by weight tile, so its L2 fetches the panel's token rows once and
+        // each weight tile once per panel (on a Zipf-skewed 128-expert
+        // prefill one tile per panel was fastest: larger panels read less
+        // but leave the XCDs less evenly loaded)
+        const int x = (int)blockIdx.x & 7, k = (int)(blockIdx.x >> 3);
+        const int per = kSkewPanel * n_wtiles;
+        const int j = k / per, kl = k - j * per;
+        ti = (8 * j + x) * kSkewPanel + kl % kSkewPanel;
+        wt = kl / kSkewPanel;
+        if (ti >= n_tiles[0]) return;
     } else {
         const int x = (int)blockIdx.x & 7;
         const int logical = xsplit[x] + (int)(blockIdx.x >> 3);
@@ -598,6 +611,17 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         int myad[NTL > 0 ? NTL : 1];  // adapter of this lane's token in column tile nt
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) myad[nt] = tok_a[(2 * nt + wn) * 32 + l32];
+        // this lane's B row offset (row * r, or -1 for rows past N) and rank
+        // within a 32-rank slab for weight-side copy j
+        int boff[LPW_A], bk[LPW_A];
+#pragma unroll
+        for (int j = 0; j < LPW_A; ++j) {
+            const int rr = (w + 4 * j) * 16 + (WP ? (lane & 15) : (lane >> 2));
+            bool ok;
+            const int grow = tile_weight_row<GU>(rr, i0, N, ok);
+            boff[j] = ok ? grow * p.r : -1;
+            bk[j] = (WP ? (lane >> 4) : chunk_of[j]) * 8;
+        }
         // every wave is past its last fragment read of the ring's K slabs
         lds_barrier();
         for (int c0 = 0; c0 < rs; c0 += 2) {      // ranks [32 c0, 32 c0 + 64)
@@ -608,20 +632,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             auto issue_unit = [&](int u) {
                 const int q = u / uc, rc = c0 + (u - q * uc);
                 const int a = __builtin_amdgcn_readfirstlane(alist[q]);
-                const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r;
+                const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r + rc * kTileBK;
                 lds_t *slot = lds_base + (u % NSLOT) * UBYTES;
 #pragma unroll
                 for (int j = 0; j < LPW_A; ++j) {
-                    const int rr = (w + 4 * j) * 16 + (WP ? (lane & 15) : (lane >> 2));
-                    const int kk = rc * kTileBK + (WP ? (lane >> 4) : chunk_of[j]) * 8;
-                    bool ok;
-                    const int grow = tile_weight_row<GU>(rr, i0, N, ok);
-                    const void *g = (ok && kk < p.r) ? (const void *)(Bae + (int64_t)grow * p.r + kk)
-                                                     : (const void *)g_zero_chunk;
-                    dma(g, slot, j);
+                    const bool in = boff[j] >= 0 && rc * kTileBK + bk[j] < p.r;
+                    dma(in ? (const void *)(Bae + boff[j] + bk[j]) : (const void *)g_zero_chunk, slot, j);
                 }
             };
-            const int npre = min(nu, NSLOT - 1);
+            // units are consumed an adapter (uc units) at a time, one barrier each
+            const int npre = min(nu, NSLOT - uc);
             for (int u = 0; u < npre; ++u) issue_unit(u);
             // shrink rows: lane (l32, lh) of column tile nt holds ranks
             // 32 c0 + 16 kq + 8 lh .. + 7 of tile row (2 nt + wn) 32 + l32
@@ -645,14 +665,15 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
                 const int a = __builtin_amdgcn_readfirstlane(alist[q]);
                 const int lo = __builtin_amdgcn_readfirstlane(arun[2 * q]);
                 const int hi = __builtin_amdgcn_readfirstlane(arun[2 * q + 1]);
+                const int u0 = q * uc;
+                // issued so far: units 0 .. min(u0 + NSLOT - uc, nu) - 1; wait for this adapter's
+                wait_unit(min(nu - u0 - uc, NSLOT - 2 * uc));
+                // into the slots of adapter q - 1, which every wave is done with
+                for (int u = u0 + NSLOT - uc; u < min(nu, u0 + NSLOT); ++u) issue_unit(u);
 #pragma unroll
                 for (int rcl = 0; rcl < 2; ++rcl) {
                     if (rcl >= uc) break;
-                    const int u = q * uc + rcl;
-                    // issued so far: units 0 .. min(u + NSLOT - 2, nu - 1)
-                    wait_unit(min(NSLOT - 2, nu - 1 - u));
-                    // into the slot of unit u - 1, which every wave is done with
-                    if (u + NSLOT - 1 < nu) issue_unit(u + NSLOT - 1);
+                    const int u = u0 + rcl;
                     const unsigned char *slot = lds + (u % NSLOT) * UBYTES;
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {

@@ -482,8 +482,11 @@ template <int BW, int BT, bool GU, bool WP, bool MX>
 void launch_tiled(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
                   const int32_t *xsplit, hipStream_t st) {
     const int n_wt = (gp.Nout + (GU ? BW / 2 : BW) - 1) / (GU ? BW / 2 : BW);
-    // every XCD may take up to xcap items of the cost-balanced ranges
-    const unsigned total = (unsigned)(8 * tiled_xcap(pl, n_wt));
+    // every XCD may take up to xcap items of the cost-balanced ranges, or
+    // (skewed order) its panels of kSkewPanel token tiles x n_wt items
+    const int64_t panels = (pl.max_tiles + kSkewPanel - 1) / kSkewPanel;
+    const int64_t skew_blocks = 8 * ((panels + 7) / 8) * kSkewPanel * n_wt;
+    const unsigned total = (unsigned)std::max<int64_t>(8 * tiled_xcap(pl, n_wt), skew_blocks);
     hipLaunchKernelGGL((gemm_tiled_kernel<BW, BT, GU, WP, MX>), dim3(total), dim3(256), 0, st, gp, tiles, ntiles,
                        n_wt, xsplit + (GU ? 0 : 16));
 }
