@@ -794,4 +794,114 @@ __global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p, RouteP
     }
 }
 
+// ---- tiny calls: one wavefront ------------------------------------------
+// At most 64 pairs and no GEMM token tiles: one wavefront, one lane per pair
+// f, no LDS and no barrier.  Each lane reads every other lane's key (v_readlane
+// in a 64-step loop) to count the pairs before it in (expert, adapter+1, f)
+// order, within its expert and within its key, and the pairs of its expert;
+// a second pass adds the padded sizes of the smaller experts (each counted
+// once, by its first pair).  The lane then stores its pair; the first pair
+// of each expert writes that expert's padding and block map, the first pair
+// of each LoRA key its items.  The layout is the one the other forms write,
+// bit for bit.  ROUTE: the wavefront routes the T <= 64 / (K+S) tokens first,
+// one after another.
+template <bool ROUTE, int VPL>
+__global__ __launch_bounds__(64) void align_tiny_kernel(AlignParams p, RouteParams rp) {
+    const int lane = (int)threadIdx.x;
+    const int La = p.La, Ep = p.Ep, A1 = La + 1, P = p.P;
+    const bool valid = lane < P;
+    int e = 0;
+    if constexpr (ROUTE) {
+        for (int t = 0; t < rp.T; ++t) {
+            const int myi = route_one_token<VPL>(rp, t);  // slot j's expert in lane j
+            const int src = lane - t * p.Kp;
+            const int got = __shfl(myi, max(0, min(src, 63)), 64);
+            if (src >= 0 && src < p.Kp) e = clamp_expert(got, Ep);
+        }
+    } else {
+        if (valid) e = clamp_expert(p.topk_ids[lane], Ep);
+    }
+    const int a1 = (valid && La > 0) ? adapter_key_of(p.adapter_ids[lane / p.Kp], La) : 0;
+    const int key = valid ? e * A1 + a1 : 0x7fffffff;
+    // pass 1: ranks and counts
+    int before_e = 0;   // pairs of this expert before this one
+    int cnt_e = 0;      // pairs of this expert
+    int before_k = 0;   // pairs of this key before this one
+    int cnt_k = 0;      // pairs of this key
+    for (int j = 0; j < P; ++j) {
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        const bool earlier = kj < key || (kj == key && j < lane);
+        cnt_e += ej == e;
+        before_e += (ej == e && earlier) ? 1 : 0;
+        cnt_k += kj == key;
+        before_k += (kj == key && j < lane) ? 1 : 0;
+    }
+    const int pad_e = (cnt_e + p.bm - 1) / p.bm * p.bm;
+    const bool lead_e = valid && before_e == 0;  // first pair of its expert
+    const bool lead_k = valid && before_k == 0;  // first pair of its key
+    const int items_k = (La > 0 && a1 > 0) ? (cnt_k + p.lbm - 1) / p.lbm : 0;
+    // pass 2: expert start (padded sizes of the smaller experts), first item
+    // of this key, and the totals
+    int off_e = 0, item0 = 0, npp = 0, nitems = 0;
+    for (int j = 0; j < P; ++j) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        const int pj = __builtin_amdgcn_readlane(pad_e, j);
+        const int lj = __builtin_amdgcn_readlane(lead_e ? 1 : 0, j);
+        const int ij = __builtin_amdgcn_readlane(lead_k ? items_k : 0, j);
+        if (lj) {
+            npp += pj;
+            if (ej < e) off_e += pj;
+        }
+        nitems += ij;
+        if (kj < key) item0 += ij;
+    }
+    const int pos = off_e + before_e;
+    if (valid) {
+        p.sorted_ids[pos] = lane;
+        if (p.sorted_adapter) p.sorted_adapter[pos] = a1 - 1;
+    }
+    if (lead_e) {
+        for (int q = off_e + cnt_e; q < off_e + pad_e; ++q) {
+            p.sorted_ids[q] = P;
+            if (p.sorted_adapter) p.sorted_adapter[q] = -1;
+        }
+        for (int b = off_e / p.bm; b < (off_e + pad_e) / p.bm; ++b) p.block_expert[b] = e;
+    }
+    for (int q = npp + lane; q < p.cap; q += 64) {
+        p.sorted_ids[q] = P;
+        if (p.sorted_adapter) p.sorted_adapter[q] = -1;
+    }
+    for (int b = npp / p.bm + lane; b < p.max_blocks; b += 64) p.block_expert[b] = -1;
+    const bool with_items = La > 0 && p.items != nullptr;
+    if (with_items) {
+        if (lead_k && items_k > 0) {
+            // the key's run starts where its first pair sits
+            int it = item0;
+            for (int q = 0; q < cnt_k; q += p.lbm) {
+                int4 v;
+                v.x = pos + q;
+                v.y = min(p.lbm, cnt_k - q);
+                v.z = a1 - 1;
+                v.w = e;
+                reinterpret_cast<int4 *>(p.items)[it++] = v;
+            }
+        }
+        for (int q = nitems + lane; q < p.max_items; q += 64) {
+            int4 v;
+            v.x = 0;
+            v.y = 0;
+            v.z = -1;
+            v.w = -1;
+            reinterpret_cast<int4 *>(p.items)[q] = v;
+        }
+    }
+    if (lane == 0) {
+        *p.npp_out = npp;
+        if (p.npp_copy) *p.npp_copy = npp;
+        *p.nitems_out = with_items ? nitems : 0;
+    }
+}
+
 }  // namespace moelora

@@ -49,6 +49,36 @@ __device__ __forceinline__ bool better(const CandT<V> &a, const CandT<V> &b) {
     return a.v > b.v || (a.v == b.v && a.i < b.i);
 }
 
+// One step of a wavefront-wide arg-max over (value, index) candidates: each
+// lane of the rows in ROW_MASK compares with the candidate DPP pattern CTRL
+// brings it (lanes without a source see "none").  The order is total, so the
+// winner does not depend on the pattern.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void cand_dpp_step(Cand &c) {
+    Cand o;
+    o.v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, c.v), CTRL, ROW_MASK, 0xf, false));
+    o.i = __builtin_amdgcn_update_dpp(0x7fffffff, c.i, CTRL, ROW_MASK, 0xf, false);
+    if (better(o, c)) c = o;
+}
+
+// The best candidate of the wavefront, in every lane: exchanges within quads
+// (lane xor 1, xor 2), half-rows and rows (mirrors), then across rows (row
+// broadcasts) leave it in lane 63, which is read out.  Register-to-register
+// steps (DPP) instead of LDS-routed shuffles: the router's K rounds each run
+// one of these.
+__device__ __forceinline__ Cand wave_best(Cand c) {
+    cand_dpp_step<0xb1, 0xf>(c);   // quad_perm [1,0,3,2]
+    cand_dpp_step<0x4e, 0xf>(c);   // quad_perm [2,3,0,1]
+    cand_dpp_step<0x141, 0xf>(c);  // row_half_mirror
+    cand_dpp_step<0x140, 0xf>(c);  // row_mirror
+    cand_dpp_step<0x142, 0xa>(c);  // row_bcast15 into rows 1, 3
+    cand_dpp_step<0x143, 0xc>(c);  // row_bcast31 into rows 2, 3
+    Cand w;
+    w.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.v), 63));
+    w.i = __builtin_amdgcn_readlane(c.i, 63);
+    return w;
+}
+
 // Biased router for token t (see the file comment): returns to lane j the
 // expert id of slot j like route_one_token.
 template <int VPL>
@@ -148,12 +178,7 @@ __device__ int route_one_token(const RouteParams &rp, int t, bool write = true) 
             Cand d{v[j], lane + 64 * j};
             if (live[j] && better(d, c)) c = d;
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            Cand o{__shfl_xor(c.v, off, 64), __shfl_xor(c.i, off, 64)};
-            if (better(o, c)) c = o;
-        }
-        // every lane now holds the same winner
+        c = wave_best(c);  // every lane now holds the same winner
         if ((c.i & 63) == lane) {
 #pragma unroll
             for (int j = 0; j < VPL; ++j)

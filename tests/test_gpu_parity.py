@@ -145,10 +145,13 @@ SMALL = [
     dict(T=40, H=256, I=192, E=6, K=2, S=1, L=3, r=128, rsf=2.5, dtype="bf16", block_m=16),
     dict(T=300, H=256, I=192, E=4, K=2, S=0, L=3, r=128, dtype="bf16", block_m=128),
     dict(T=24, H=128, I=64, E=4, K=2, S=0, L=2, r=128, dtype="f32"),
-    # routed inside the small alignment's launch (no LoRA, or a split shrink): E up to 1000, 64 slots
+    # routed inside the small alignment's launch (no LoRA, or a split shrink;
+    # at most one token per wave): E up to 1000, 64 slots
     dict(T=15, H=64, I=64, E=1000, K=63, S=1, L=0, r=0, rsf=2.0, dtype="bf16"),
-    dict(T=9, H=96, I=64, E=300, K=7, S=0, L=2, r=8, dtype="bf16", split=2),
-    dict(T=30, H=64, I=40, E=130, K=4, S=0, L=0, r=0, dtype="f32"),
+    dict(T=4, H=96, I=64, E=300, K=7, S=0, L=2, r=8, dtype="bf16", split=2),
+    dict(T=3, H=64, I=40, E=130, K=4, S=0, L=0, r=0, dtype="f32"),
+    # one token more than the alignment has waves: routed in its own launch
+    dict(T=5, H=64, I=40, E=130, K=4, S=0, L=0, r=0, dtype="bf16"),
     # a wide, ragged hidden size (12296 = 8 * 1537, not a multiple of 32) on both GEMM kinds
     dict(T=24, H=12296, I=64, E=4, K=2, S=0, L=2, r=16, dtype="bf16", block_m=16),
     dict(T=260, H=12296, I=64, E=4, K=2, S=0, L=2, r=16, dtype="bf16", block_m=128),

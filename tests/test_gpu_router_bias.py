@@ -75,8 +75,9 @@ FWD = [
     # streaming GEMM with the gate_up shrink in the router launch (decode form)
     dict(T=40, H=200, I=72, E=6, K=2, S=0, L=3, r=16, router="bias_sigmoid"),
     dict(T=24, H=136, I=72, E=5, K=2, S=1, L=3, r=16, rsf=2.5, router="bias_softmax"),
-    # no LoRA: the router runs inside the small alignment's launch
-    dict(T=33, H=128, I=96, E=40, K=5, S=1, L=0, r=0, rsf=2.5, router="bias_softmax"),
+    # no LoRA: few tokens route inside the small alignment's launch, more in their own
+    dict(T=3, H=128, I=96, E=40, K=5, S=1, L=0, r=0, rsf=2.5, router="bias_softmax"),
+    dict(T=4, H=128, I=96, E=200, K=6, S=0, L=0, r=0, router="bias_sigmoid"),
     dict(T=70, H=128, I=96, E=200, K=6, S=0, L=0, r=0, router="bias_sigmoid"),
     # LDS-tiled GEMM
     dict(T=300, H=200, I=200, E=4, K=2, S=0, L=3, r=24, router="bias_softmax", block_m=128),
