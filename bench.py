@@ -441,6 +441,8 @@ def main() -> int:
                     help="read w13/w2 row-major instead of packing them once before timing")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--mxfp8-only", default="",
+                    help="only run the MXFP8-weight report on these comma-separated workloads (one JSON line each)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -453,6 +455,10 @@ def main() -> int:
 
     if args.copy_calib_mib:
         copy_calibration(args.copy_calib_mib, args.steps)
+        return 0
+    if args.mxfp8_only:
+        for name in args.mxfp8_only.split(","):
+            print(json.dumps({"workload": name, "mxfp8": report_mxfp8(name, args.steps, args.warmup)}), flush=True)
         return 0
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     m = measure(args.workload, args.steps, args.warmup, packed=not args.row_major)

@@ -284,10 +284,6 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // sorts an expert's rows by adapter, so each is one run of rows); arun:
     // the first and one-past-last row of each adapter's run.
     __shared__ int tok_f[BT], tok_a[BT], alist[BT], arun[2 * BT], wcnt[5];
-    const int my_row = row0 + min(tid, nrows - 1);
-    const int f_row = (tid < BT) ? p.sorted_ids[my_row] : p.P;
-    const int a_row = (p.lora && tid < BT) ? p.sorted_adapter[my_row] : -1;
-
     // ---- MX: the tile's scales, copied to LDS ahead of the ring ------------
     // Run u covers the weight rows of features i0 .. i0 + vrows - 1 (gate
     // rows, or up rows at u = 1): bytes [0, len) from rg.  Byte b of the
@@ -325,6 +321,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
             if (k >= 0 && k < mx_tail[u]) mx_byte = end0[k];
         }
     }
+
+    const int my_row = row0 + min(tid, nrows - 1);
+    const int f_row = (tid < BT) ? p.sorted_ids[my_row] : p.P;
+    const int a_row = (p.lora && tid < BT) ? p.sorted_adapter[my_row] : -1;
 
     // ---- direct-to-LDS stage loads ----------------------------------------
     // Wave w owns the stage's 16-row groups w, w+4, ...: instruction j fills
@@ -540,6 +540,11 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         tok_f[tid] = tid < nrows ? f_row : p.P;
         tok_a[tid] = (tid < nrows && a_row < p.L) ? a_row : -1;
     }
+    // Every value loaded above is used here on all paths (the MX tail byte
+    // is loaded first): a load whose only use is conditional would leave the
+    // compiler a wait for it pending into the K loop, where it would put a
+    // full vmcnt(0) wait in every iteration.
+    asm volatile("" ::"v"(f_row), "v"(a_row), "v"(mx_byte));
     lds_barrier();
     {
         const int a = tid < BT ? tok_a[tid] : -1;
