@@ -516,8 +516,8 @@ def main() -> int:
                                                                      max(5, args.warmup))
         if args.prefill:
             print(f"bench: reported {args.prefill} with MXFP8 weights", file=sys.stderr, flush=True)
-            result["reported"][f"{args.prefill}_mxfp8"] = report_mxfp8(args.prefill, max(5, args.steps // 5),
-                                                                       max(2, args.warmup // 5))
+            result["reported"][f"{args.prefill}_mxfp8"] = report_mxfp8(args.prefill, max(20, args.steps // 2),
+                                                                       max(5, args.warmup // 2))
     print(json.dumps(result), flush=True)
     return 0
 

@@ -89,8 +89,9 @@ extern "C" {
  *   dtype  MOE_LORA_BF16 (bf16 tensors, fp32 accumulation) or MOE_LORA_F32
  *   block_m  token rows per GEMM tile; 0 = library choice from the
  *      average rows per expert.  16 or 32: streaming GEMM, experts padded to
- *      block_m rows.  128 or 256 (bf16 only): LDS-tiled GEMM, experts padded
- *      to 32 rows and cut into tiles of at most block_m rows
+ *      block_m rows.  128 or 256 (bf16 layers only, MOE_LORA_EUNSUPPORTED for
+ *      fp32): LDS-tiled GEMM, experts padded to 32 rows and cut into tiles
+ *      of at most block_m rows; it takes MXFP8 weights with H, I <= 3072
  *   lora_block_m  rows per LoRA shrink work item; 0 = library choice, else
  *      16 or 32 (32 needs r <= 64)
  *   router  MOE_LORA_ROUTER_TOPK (0): top-K of the logits, weights as under
