@@ -803,92 +803,106 @@ __global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p, RouteP
 // once, by its first pair).  The lane then stores its pair; the first pair
 // of each expert writes that expert's padding and block map, the first pair
 // of each LoRA key its items.  The layout is the one the other forms write,
-// bit for bit.  ROUTE: the wavefront routes the T <= 64 / (K+S) tokens first,
-// one after another.
-template <bool ROUTE, int VPL>
-__global__ __launch_bounds__(64) void align_tiny_kernel(AlignParams p, RouteParams rp) {
-    const int lane = (int)threadIdx.x;
-    const int La = p.La, Ep = p.Ep, A1 = La + 1, P = p.P;
-    const bool valid = lane < P;
-    int e = 0;
-    if constexpr (ROUTE) {
-        for (int t = 0; t < rp.T; ++t) {
-            const int myi = route_one_token<VPL>(rp, t);  // slot j's expert in lane j
-            const int src = lane - t * p.Kp;
-            const int got = __shfl(myi, max(0, min(src, 63)), 64);
-            if (src >= 0 && src < p.Kp) e = clamp_expert(got, Ep);
-        }
-    } else {
-        if (valid) e = clamp_expert(p.topk_ids[lane], Ep);
-    }
-    const int a1 = (valid && La > 0) ? adapter_key_of(p.adapter_ids[lane / p.Kp], La) : 0;
-    const int key = valid ? e * A1 + a1 : 0x7fffffff;
+// bit for bit.
+
+// Lane f's place in the layout (lanes >= P hold no pair).
+struct TinyRank {
+    int e, a1, key;
+    int pos;            // sorted position of the pair
+    int off_e, cnt_e, pad_e;  // its expert's first position, pairs and padded size
+    int cnt_k, items_k, item0;  // its key's pairs, LoRA items and first item
+    int npp, nitems;    // totals (every lane)
+    bool valid, lead_e, lead_k;  // holds a pair; first pair of its expert / key
+};
+
+// `e`: lane f's expert (any value on lanes >= P).  Wave-uniform control flow.
+__device__ __forceinline__ TinyRank tiny_align_rank(const AlignParams &p, int e) {
+    TinyRank r;
+    const int lane = lane_id();
+    const int La = p.La, A1 = La + 1, P = p.P;
+    r.valid = lane < P;
+    r.e = e;
+    r.a1 = (r.valid && La > 0) ? adapter_key_of(p.adapter_ids[lane / p.Kp], La) : 0;
+    r.key = r.valid ? e * A1 + r.a1 : 0x7fffffff;
     // pass 1: ranks and counts
     int before_e = 0;   // pairs of this expert before this one
     int cnt_e = 0;      // pairs of this expert
     int before_k = 0;   // pairs of this key before this one
     int cnt_k = 0;      // pairs of this key
     for (int j = 0; j < P; ++j) {
-        const int kj = __builtin_amdgcn_readlane(key, j);
+        const int kj = __builtin_amdgcn_readlane(r.key, j);
         const int ej = __builtin_amdgcn_readlane(e, j);
-        const bool earlier = kj < key || (kj == key && j < lane);
+        const bool earlier = kj < r.key || (kj == r.key && j < lane);
         cnt_e += ej == e;
         before_e += (ej == e && earlier) ? 1 : 0;
-        cnt_k += kj == key;
-        before_k += (kj == key && j < lane) ? 1 : 0;
+        cnt_k += kj == r.key;
+        before_k += (kj == r.key && j < lane) ? 1 : 0;
     }
-    const int pad_e = (cnt_e + p.bm - 1) / p.bm * p.bm;
-    const bool lead_e = valid && before_e == 0;  // first pair of its expert
-    const bool lead_k = valid && before_k == 0;  // first pair of its key
-    const int items_k = (La > 0 && a1 > 0) ? (cnt_k + p.lbm - 1) / p.lbm : 0;
+    r.cnt_e = cnt_e;
+    r.cnt_k = cnt_k;
+    r.pad_e = (cnt_e + p.bm - 1) / p.bm * p.bm;
+    r.lead_e = r.valid && before_e == 0;
+    r.lead_k = r.valid && before_k == 0;
+    r.items_k = (La > 0 && r.a1 > 0) ? (cnt_k + p.lbm - 1) / p.lbm : 0;
     // pass 2: expert start (padded sizes of the smaller experts), first item
     // of this key, and the totals
     int off_e = 0, item0 = 0, npp = 0, nitems = 0;
     for (int j = 0; j < P; ++j) {
         const int ej = __builtin_amdgcn_readlane(e, j);
-        const int kj = __builtin_amdgcn_readlane(key, j);
-        const int pj = __builtin_amdgcn_readlane(pad_e, j);
-        const int lj = __builtin_amdgcn_readlane(lead_e ? 1 : 0, j);
-        const int ij = __builtin_amdgcn_readlane(lead_k ? items_k : 0, j);
+        const int kj = __builtin_amdgcn_readlane(r.key, j);
+        const int pj = __builtin_amdgcn_readlane(r.pad_e, j);
+        const int lj = __builtin_amdgcn_readlane(r.lead_e ? 1 : 0, j);
+        const int ij = __builtin_amdgcn_readlane(r.lead_k ? r.items_k : 0, j);
         if (lj) {
             npp += pj;
             if (ej < e) off_e += pj;
         }
         nitems += ij;
-        if (kj < key) item0 += ij;
+        if (kj < r.key) item0 += ij;
     }
-    const int pos = off_e + before_e;
-    if (valid) {
-        p.sorted_ids[pos] = lane;
-        if (p.sorted_adapter) p.sorted_adapter[pos] = a1 - 1;
+    r.off_e = off_e;
+    r.item0 = item0;
+    r.npp = npp;
+    r.nitems = nitems;
+    r.pos = off_e + before_e;
+    return r;
+}
+
+// Store the layout ranked by tiny_align_rank (the whole wavefront calls it).
+__device__ __forceinline__ void tiny_align_store(const AlignParams &p, const TinyRank &r) {
+    const int lane = lane_id();
+    const int P = p.P;
+    if (r.valid) {
+        p.sorted_ids[r.pos] = lane;
+        if (p.sorted_adapter) p.sorted_adapter[r.pos] = r.a1 - 1;
     }
-    if (lead_e) {
-        for (int q = off_e + cnt_e; q < off_e + pad_e; ++q) {
+    if (r.lead_e) {
+        for (int q = r.off_e + r.cnt_e; q < r.off_e + r.pad_e; ++q) {
             p.sorted_ids[q] = P;
             if (p.sorted_adapter) p.sorted_adapter[q] = -1;
         }
-        for (int b = off_e / p.bm; b < (off_e + pad_e) / p.bm; ++b) p.block_expert[b] = e;
+        for (int b = r.off_e / p.bm; b < (r.off_e + r.pad_e) / p.bm; ++b) p.block_expert[b] = r.e;
     }
-    for (int q = npp + lane; q < p.cap; q += 64) {
+    for (int q = r.npp + lane; q < p.cap; q += 64) {
         p.sorted_ids[q] = P;
         if (p.sorted_adapter) p.sorted_adapter[q] = -1;
     }
-    for (int b = npp / p.bm + lane; b < p.max_blocks; b += 64) p.block_expert[b] = -1;
-    const bool with_items = La > 0 && p.items != nullptr;
+    for (int b = r.npp / p.bm + lane; b < p.max_blocks; b += 64) p.block_expert[b] = -1;
+    const bool with_items = p.La > 0 && p.items != nullptr;
     if (with_items) {
-        if (lead_k && items_k > 0) {
+        if (r.lead_k && r.items_k > 0) {
             // the key's run starts where its first pair sits
-            int it = item0;
-            for (int q = 0; q < cnt_k; q += p.lbm) {
+            int it = r.item0;
+            for (int q = 0; q < r.cnt_k; q += p.lbm) {
                 int4 v;
-                v.x = pos + q;
-                v.y = min(p.lbm, cnt_k - q);
-                v.z = a1 - 1;
-                v.w = e;
+                v.x = r.pos + q;
+                v.y = min(p.lbm, r.cnt_k - q);
+                v.z = r.a1 - 1;
+                v.w = r.e;
                 reinterpret_cast<int4 *>(p.items)[it++] = v;
             }
         }
-        for (int q = nitems + lane; q < p.max_items; q += 64) {
+        for (int q = r.nitems + lane; q < p.max_items; q += 64) {
             int4 v;
             v.x = 0;
             v.y = 0;
@@ -898,10 +912,64 @@ __global__ __launch_bounds__(64) void align_tiny_kernel(AlignParams p, RoutePara
         }
     }
     if (lane == 0) {
-        *p.npp_out = npp;
-        if (p.npp_copy) *p.npp_copy = npp;
-        *p.nitems_out = with_items ? nitems : 0;
+        *p.npp_out = r.npp;
+        if (p.npp_copy) *p.npp_copy = r.npp;
+        *p.nitems_out = with_items ? r.nitems : 0;
     }
+}
+
+// Routing and alignment of a tiny call inside another kernel's workgroup of
+// 256 threads, for a kernel whose workgroups each need one block of the
+// layout: wave w < T routes token w, then wave 0 ranks the pairs.  Only the
+// `writer` workgroup stores the routing and the layout (as the standalone
+// kernels do, for the kernels launched after this one); every workgroup
+// keeps in LDS the padded row count (s_blk[0]), the expert of its block b
+// (s_blk[1]) and the pair of each of the block's BT rows (s_rows).
+// Requires T <= 4, T*(K+S) <= 64, E <= 64*VPL and ap.bm == BT.
+struct FusedRoute {
+    AlignParams ap;
+    RouteParams rp;
+};
+
+template <int BT, int VPL>
+__device__ __forceinline__ void route_align_in_block(const FusedRoute &fr, int b, bool writer, int *s_e,
+                                                     int *s_rows, int *s_blk) {
+    const AlignParams &ap = fr.ap;
+    const int w = (int)(threadIdx.x >> 6), lane = lane_id();
+    if (w < fr.rp.T) {
+        const int myi = route_one_token<VPL>(fr.rp, w, writer);  // slot j's expert in lane j
+        if (lane < ap.Kp) s_e[w * ap.Kp + lane] = clamp_expert(myi, ap.Ep);
+    }
+    if ((int)threadIdx.x < BT) s_rows[threadIdx.x] = ap.P;
+    if (threadIdx.x == 0) s_blk[1] = 0;
+    __syncthreads();
+    if (w == 0) {
+        const TinyRank r = tiny_align_rank(ap, lane < ap.P ? s_e[lane] : 0);
+        if (writer) tiny_align_store(ap, r);
+        if (r.valid && r.pos >= b * BT && r.pos < (b + 1) * BT) s_rows[r.pos - b * BT] = lane;
+        if (r.lead_e && r.off_e <= b * BT && b * BT < r.off_e + r.pad_e) s_blk[1] = r.e;
+        if (lane == 0) s_blk[0] = r.npp;
+    }
+    __syncthreads();
+}
+
+// ROUTE: the wavefront routes the T <= 64 / (K+S) tokens first, one after
+// another.
+template <bool ROUTE, int VPL>
+__global__ __launch_bounds__(64) void align_tiny_kernel(AlignParams p, RouteParams rp) {
+    const int lane = (int)threadIdx.x;
+    int e = 0;
+    if constexpr (ROUTE) {
+        for (int t = 0; t < rp.T; ++t) {
+            const int myi = route_one_token<VPL>(rp, t);  // slot j's expert in lane j
+            const int src = lane - t * p.Kp;
+            const int got = __shfl(myi, max(0, min(src, 63)), 64);
+            if (src >= 0 && src < p.Kp) e = clamp_expert(got, p.Ep);
+        }
+    } else {
+        if (lane < p.P) e = clamp_expert(p.topk_ids[lane], p.Ep);
+    }
+    tiny_align_store(p, tiny_align_rank(p, e));
 }
 
 }  // namespace moelora

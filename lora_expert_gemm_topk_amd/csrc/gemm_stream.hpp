@@ -24,6 +24,7 @@
 // Blocks past the padded row count exit at once.
 #pragma once
 
+#include "align.hpp"
 #include "common.hpp"
 #include "pack.hpp"
 
@@ -94,18 +95,38 @@ __device__ __forceinline__ void lora_expand_add(const GemmParams &p, int e, int 
 // the hardware's scaled FP8 -> bf16 conversion (exact: E4M3 has 3 mantissa
 // bits) and feeds the same bf16 MFMAs; the matching 32 activations are that
 // lane's 64 bytes of x.  Weight bytes per layer call halve.
-template <int BW, int BT, bool GU, bool WP, bool MX = false>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
+//
+// ROUTE (gate_up of tiny calls without LoRA): the workgroup routes the
+// tokens and aligns the pairs itself (route_align_in_block) instead of
+// reading a layout written by earlier launches; workgroup (0, 0) stores the
+// routing and the layout for the down GEMM and the combine.
+template <int BW, int BT, bool GU, bool WP, bool MX, bool ROUTE>
+__device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const FusedRoute *fr) {
     constexpr int MS = BW / 16, NS = BT / 16;
     constexpr int LDW = BW + 4;
     __shared__ float buf[2][BT][LDW];
     // MXFP8: the scale bytes of the tile's BW weight rows, staged once
     __shared__ __attribute__((aligned(16))) uint8_t mx_sc[MX ? BW * kMxMaxBlocks : 16];
+    // ROUTE: the slots' experts, the block's pairs, padded row count and expert
+    __shared__ int r_e[ROUTE ? 64 : 1], r_rows[ROUTE ? BT : 1], r_blk[2];
 
     const int b = blockIdx.y;
-    const int npp = p.counters[0];
+    int npp, e;
+    if constexpr (ROUTE) {
+        route_align_in_block<BT, 4>(*fr, b, blockIdx.x == 0 && b == 0, r_e, r_rows, r_blk);
+        npp = r_blk[0];
+        e = r_blk[1];
+    } else {
+        npp = p.counters[0];
+        e = 0;
+    }
     if (b * BT >= npp) return;
-    const int e = p.block_expert[b];
+    if constexpr (!ROUTE) e = p.block_expert[b];
+    // the pair at sorted row prow of this block (P: padding)
+    auto sorted_at = [&](int prow) -> int {
+        if constexpr (ROUTE) return r_rows[prow - b * BT];
+        else return p.sorted_ids[prow];
+    };
     const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
     const int g = lane >> 4, l16 = lane & 15;
     const int64_t Kd = p.Kdim;
@@ -159,7 +180,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
         const int prow = b * BT + ns * 16 + l16;
-        const int f = p.sorted_ids[prow];
+        const int f = sorted_at(prow);
         xok[ns] = f < p.P;
         int64_t row = 0;
         if (xok[ns]) row = GU ? (f / p.Kp) : prow;
@@ -334,7 +355,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
             const int prow = b * BT + j;
             const int col0 = i0 + 4 * qp;
             if (col0 >= N) continue;
-            const int f = p.sorted_ids[prow];
+            const int f = sorted_at(prow);
             uint2 packed = make_uint2(0u, 0u);
             if (f < p.P) {
                 float v[8];  // gate col0..col0+3, up col0..col0+3
@@ -373,7 +394,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
             const int prow = b * BT + j;
             const int col0 = i0 + cg * 4;
             if (col0 >= N) continue;
-            const int f = p.sorted_ids[prow];
+            const int f = sorted_at(prow);
             uint2 packed = make_uint2(0u, 0u);
             if (f < p.P) {
                 float v[8];
@@ -410,7 +431,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
             const int prow = b * BT + j;
             const int col0 = i0 + cg * 4;
             if (col0 >= N) continue;
-            const int f = p.sorted_ids[prow];
+            const int f = sorted_at(prow);
             if (f >= p.P) continue;
             float v[4];
 #pragma unroll
@@ -428,6 +449,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
                 make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
     }
+}
+
+template <int BW, int BT, bool GU, bool WP, bool MX = false>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
+    gemm_stream_body<BW, BT, GU, WP, MX, false>(p, nullptr);
+}
+
+template <int BW, int BT, bool WP, bool MX>
+__global__ __launch_bounds__(256) void gemm_stream_route_kernel(GemmParams p, FusedRoute fr) {
+    gemm_stream_body<BW, BT, true, WP, MX, true>(p, &fr);
 }
 
 }  // namespace moelora

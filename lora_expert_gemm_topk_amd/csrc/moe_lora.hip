@@ -65,6 +65,7 @@ struct Plan {
     bool multi = false;      // multi-workgroup alignment
     bool small_align = false;  // one-pass alignment for small calls without GEMM token tiles
     bool route_in_align = false;  // small_align: the router runs in the alignment's launch
+    bool route_in_gemm = false;   // the gate_up launch routes and aligns (tiny calls without LoRA)
     int align_small_nw = 4;
     size_t align_small_lds = 0;
     int anb = 0, achunk = 0; // its blocks and pairs per block
@@ -201,6 +202,11 @@ int make_plan(const moe_lora_dims *d, Plan *pl) {
     // one after another in a wave costs more than the launch it saves
     // (measured: T = 32 with 64 experts, 57 us against 19 us in two launches)
     p.route_in_align = p.small_align && !p.row_shrink && p.Kp <= 64 && d->T <= p.align_small_nw;
+    // tiny calls without LoRA on the streaming GEMM: every gate_up workgroup
+    // routes the tokens and aligns the pairs itself (a wave per token, then
+    // one wave ranks them), so the call runs in three launches
+    p.route_in_gemm = p.small_align && p.kind == 1 && !p.lora && p.P <= 64 && d->T >= 1 && d->T <= 4 &&
+                      d->E <= 256;
     p.tmp_ints = p.P;
     if (p.multi) {
         p.achunk = (int)std::max<int64_t>(256, ((p.P + 63) / 64 + 63) / 64 * 64);
@@ -356,13 +362,10 @@ int tiled_nwt(const moe_lora_dims *d, bool gu) {
 int64_t tiled_xcap(const Plan &pl, int n_wt) { return 2 * (((int64_t)n_wt * pl.max_tiles + 7) / 8); }
 
 // Alignment: one workgroup below the multi-workgroup threshold, else four launches.
-int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
-                 int32_t *sorted, int32_t *sorted_adapter, int32_t *bexp, int32_t *npp, int32_t *items,
-                 int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles,
-                 hipStream_t st, int32_t *npp_copy = nullptr, int32_t *queue = nullptr,
-                 const RouteParams *rp = nullptr) {
-    std::call_once(g_attr_once, set_kernel_attributes);
-    if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
+AlignParams align_params(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
+                         int32_t *sorted, int32_t *sorted_adapter, int32_t *bexp, int32_t *npp, int32_t *items,
+                         int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles, int32_t *npp_copy,
+                         int32_t *queue) {
     AlignParams ap;
     ap.T = (int)d->T;
     ap.lds_keys = pl.lds_keys ? 1 : 0;
@@ -402,6 +405,19 @@ int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, con
     ap.chunk = pl.achunk;
     ap.hist = tmp;
     ap.ktot = tmp + (int64_t)pl.anb * NK;
+    return ap;
+}
+
+int launch_align(const Plan &pl, const moe_lora_dims *d, const int32_t *ids, const int32_t *adapter_ids,
+                 int32_t *sorted, int32_t *sorted_adapter, int32_t *bexp, int32_t *npp, int32_t *items,
+                 int32_t *nitems, int32_t *tmp, int32_t *tiles, int32_t *ntiles,
+                 hipStream_t st, int32_t *npp_copy = nullptr, int32_t *queue = nullptr,
+                 const RouteParams *rp = nullptr) {
+    std::call_once(g_attr_once, set_kernel_attributes);
+    if (g_attr_err != hipSuccess) return hip_fail(g_attr_err, "hipFuncSetAttribute(align)");
+    const AlignParams ap = align_params(pl, d, ids, adapter_ids, sorted, sorted_adapter, bexp, npp, items, nitems,
+                                        tmp, tiles, ntiles, npp_copy, queue);
+    const int NK = (int)(pl.Ep * (pl.La + 1));
     if (pl.multi) {
         const size_t klds = sizeof(int) * (size_t)NK;
         hipLaunchKernelGGL(align_hist_kernel, dim3((unsigned)pl.anb), dim3(256), klds, st, ap);
@@ -522,43 +538,49 @@ void launch_tiled_shape(const Plan &pl, const GemmParams &gp, const int32_t *til
     }
 }
 
-template <bool GU, bool WP>
-void launch_gemm_wp(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
-                    const int32_t *queue, hipStream_t st) {
-    if (pl.kind == 1) {
-        const int tile = GU ? kStreamBW / 2 : kStreamBW;
-        const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
-        if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, WP>), grid, block, 0, st, gp);
-        else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, WP>), grid, block, 0, st, gp);
-        return;
+// The streaming GEMM (few rows per expert).  fr: gate_up routes and aligns
+// inside its workgroups.
+template <bool GU, bool WP, bool MX>
+void launch_stream(const Plan &pl, const GemmParams &gp, const FusedRoute *fr, hipStream_t st) {
+    const int tile = GU ? kStreamBW / 2 : kStreamBW;
+    const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
+    if constexpr (GU) {
+        if (fr != nullptr) {
+            if (pl.bm == 16)
+                hipLaunchKernelGGL((gemm_stream_route_kernel<kStreamBW, 16, WP, MX>), grid, block, 0, st, gp, *fr);
+            else
+                hipLaunchKernelGGL((gemm_stream_route_kernel<kStreamBW, 32, WP, MX>), grid, block, 0, st, gp, *fr);
+            return;
+        }
     }
-    launch_tiled_shape<GU, WP, false>(pl, gp, tiles, ntiles, queue, st);
+    if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, WP, MX>), grid, block, 0, st, gp);
+    else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, WP, MX>), grid, block, 0, st, gp);
+}
+
+template <bool GU, bool MX>
+void launch_stream_wp(const Plan &pl, const GemmParams &gp, const FusedRoute *fr, bool wp, hipStream_t st) {
+    if (wp) launch_stream<GU, true, MX>(pl, gp, fr, st);
+    else launch_stream<GU, false, MX>(pl, gp, fr, st);
 }
 
 template <bool GU>
 void launch_gemm(const Plan &pl, const GemmParams &gp, const int32_t *tiles, const int32_t *ntiles,
-                 const int32_t *queue, bool wp, hipStream_t st) {
-    if (gp.Wscale != nullptr && pl.kind == 2) {
-        // MXFP8 weights, many rows per expert: H, I <= 32 kMxTiledMaxBlocks (checked by moe_lora_check_args)
-        if (wp) launch_tiled_shape<GU, true, true>(pl, gp, tiles, ntiles, queue, st);
-        else launch_tiled_shape<GU, false, true>(pl, gp, tiles, ntiles, queue, st);
-        return;
-    }
-    if (gp.Wscale != nullptr) {
-        // MXFP8 weights, few rows per expert: the streaming kernel (kind 1; kind 0 is checked out)
-        const int tile = GU ? kStreamBW / 2 : kStreamBW;
-        const dim3 grid((unsigned)((gp.Nout + tile - 1) / tile), (unsigned)pl.max_blocks), block(256);
-        if (wp) {
-            if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, true, true>), grid, block, 0, st, gp);
-            else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, true, true>), grid, block, 0, st, gp);
+                 const int32_t *queue, bool wp, hipStream_t st, const FusedRoute *fr = nullptr) {
+    const bool mx = gp.Wscale != nullptr;
+    if (pl.kind == 2) {
+        // MXFP8 weights: H, I <= 32 kMxTiledMaxBlocks (checked by moe_lora_check_args)
+        if (mx) {
+            if (wp) launch_tiled_shape<GU, true, true>(pl, gp, tiles, ntiles, queue, st);
+            else launch_tiled_shape<GU, false, true>(pl, gp, tiles, ntiles, queue, st);
         } else {
-            if (pl.bm == 16) hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 16, GU, false, true>), grid, block, 0, st, gp);
-            else hipLaunchKernelGGL((gemm_stream_kernel<kStreamBW, 32, GU, false, true>), grid, block, 0, st, gp);
+            if (wp) launch_tiled_shape<GU, true, false>(pl, gp, tiles, ntiles, queue, st);
+            else launch_tiled_shape<GU, false, false>(pl, gp, tiles, ntiles, queue, st);
         }
         return;
     }
-    if (wp) launch_gemm_wp<GU, true>(pl, gp, tiles, ntiles, queue, st);
-    else launch_gemm_wp<GU, false>(pl, gp, tiles, ntiles, queue, st);
+    // kind 1 (kind 0, the fp32 path, does not come here; MXFP8 with kind 0 is checked out)
+    if (mx) launch_stream_wp<GU, true>(pl, gp, fr, wp, st);
+    else launch_stream_wp<GU, false>(pl, gp, fr, wp, st);
 }
 
 }  // namespace
@@ -819,17 +841,24 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
     };
     int32_t *tiles = (int32_t *)(ws + p.o_tiles);
     int32_t *queue = (int32_t *)(ws + p.o_queue);
+    // with route_in_gemm the gate_up launch routes and aligns (both stages empty)
     mark(2 * MOE_LORA_STAGE_ROUTE);
     if (p.row_shrink) launch_route_shrink(p, d, a, ids, wts, s13, st);
-    else if (!p.route_in_align) launch_route(d, a->router_logits, a->expert_bias, ids, wts, st);
+    else if (!p.route_in_align && !p.route_in_gemm) launch_route(d, a->router_logits, a->expert_bias, ids, wts, st);
     mark(2 * MOE_LORA_STAGE_ROUTE + 1);
     const RouteParams rp_align = route_params(d, a->router_logits, a->expert_bias, ids, wts);
     mark(2 * MOE_LORA_STAGE_ALIGN);
-    int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt, items,
-                          cnt + 1, tmp,
-                          p.kind == 2 ? tiles : nullptr, cnt + 2, st, a->num_post_pad_out, queue,
-                          p.route_in_align ? &rp_align : nullptr);
-    if (r2 != MOE_LORA_OK) return r2;
+    FusedRoute fused;
+    if (p.route_in_gemm) {
+        fused.ap = align_params(p, d, ids, a->adapter_ids, sorted, nullptr, bexp, cnt, items, cnt + 1, tmp, nullptr,
+                                cnt + 2, a->num_post_pad_out, queue);
+        fused.rp = rp_align;
+    } else {
+        const int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt,
+                                    items, cnt + 1, tmp, p.kind == 2 ? tiles : nullptr, cnt + 2, st,
+                                    a->num_post_pad_out, queue, p.route_in_align ? &rp_align : nullptr);
+        if (r2 != MOE_LORA_OK) return r2;
+    }
     // the tiled GEMM reads x gathered and packed per sorted row; with LoRA
     // the pack shares one launch with the gate_up shrink (stage SHRINK13)
     PackXParams xp;
@@ -943,7 +972,8 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         gp.out = h;
         gp.Kdim = H;
         gp.Nout = I;
-        launch_gemm<true>(p, gp, tiles, cnt + 2, queue, a->weights_packed != 0, st);
+        launch_gemm<true>(p, gp, tiles, cnt + 2, queue, a->weights_packed != 0, st,
+                          p.route_in_gemm ? &fused : nullptr);
         mark(2 * MOE_LORA_STAGE_GATE_UP + 1);
         mark(2 * MOE_LORA_STAGE_SHRINK2);
         if (p.lora) {

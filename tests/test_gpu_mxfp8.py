@@ -29,6 +29,7 @@ CASES = [
     dict(T=7, H=64, I=64, E=4, K=1, S=0, L=2, r=8, block_m=16),   # one 128-wide chunk of K at most
     dict(T=9, H=8192, I=64, E=4, K=2, S=0, L=2, r=16),    # gate_up at the largest K (256 scale blocks per row)
     dict(T=9, H=64, I=8192, E=4, K=2, S=1, L=2, r=8),     # down at the largest K
+    dict(T=3, H=128, I=96, E=40, K=5, S=1, L=0, r=0, rsf=2.5),  # routed inside gate_up
 ]
 
 

@@ -75,10 +75,12 @@ FWD = [
     # streaming GEMM with the gate_up shrink in the router launch (decode form)
     dict(T=40, H=200, I=72, E=6, K=2, S=0, L=3, r=16, router="bias_sigmoid"),
     dict(T=24, H=136, I=72, E=5, K=2, S=1, L=3, r=16, rsf=2.5, router="bias_softmax"),
-    # no LoRA: few tokens route inside the small alignment's launch, more in their own
+    # no LoRA: up to 4 tokens route inside each gate_up workgroup, more in their own launch
     dict(T=3, H=128, I=96, E=40, K=5, S=1, L=0, r=0, rsf=2.5, router="bias_softmax"),
     dict(T=4, H=128, I=96, E=200, K=6, S=0, L=0, r=0, router="bias_sigmoid"),
     dict(T=70, H=128, I=96, E=200, K=6, S=0, L=0, r=0, router="bias_sigmoid"),
+    # LoRA with a split shrink: few tokens route inside the small alignment's launch
+    dict(T=4, H=128, I=96, E=200, K=6, S=0, L=2, r=8, router="bias_softmax", split=2),
     # LDS-tiled GEMM
     dict(T=300, H=200, I=200, E=4, K=2, S=0, L=3, r=24, router="bias_softmax", block_m=128),
     dict(T=500, H=256, I=384, E=6, K=2, S=1, L=4, r=32, rsf=2.5, router="bias_sigmoid", block_m=128),
@@ -94,8 +96,8 @@ def test_forward_biased_router(c):
     say("forward biased router", c)
     ids = torch.empty((shape.T, shape.Kp), dtype=torch.int32, device=DEV)
     w = torch.empty((shape.T, shape.Kp), dtype=torch.float32, device=DEV)
-    out = ml.forward_inputs(inp, routing_out=(ids, w), block_m=c.get("block_m", 0), router=c["router"],
-                            expert_bias=bias)
+    out = ml.forward_inputs(inp, routing_out=(ids, w), block_m=c.get("block_m", 0), split_k=c.get("split", 0),
+                            router=c["router"], expert_bias=bias)
     torch.cuda.synchronize()
     sc = SCORING[c["router"]]
     oids, ow = oracle.route_bias(inp.logits.cpu().numpy(), shape.K, shape.S, shape.rsf, 1, sc, bias.cpu().numpy())
@@ -104,12 +106,14 @@ def test_forward_biased_router(c):
     assert_close(out, oracle.forward_inputs(inp, scoring=sc, bias=bias.cpu()), shape.dtype, f"biased {c}")
 
 
-@pytest.mark.parametrize("bm", [0, 128])
-def test_forward_alignment_outputs(bm):
+@pytest.mark.parametrize("bm,tiny", [(0, False), (128, False), (0, True)])
+def test_forward_alignment_outputs(bm, tiny):
     """sorted_ids, block_expert and num_post_pad written by the forward to the
     caller's buffers equal the oracle's alignment, and the layer output is
-    the same as with the alignment kept in the workspace."""
-    shape = synth.LayerShape(T=300, H=128, I=96, E=8, K=3, S=1, L=4, r=16, rsf=2.5)
+    the same as with the alignment kept in the workspace (tiny: a call
+    without LoRA whose gate_up launch routes and aligns)."""
+    shape = (synth.LayerShape(T=3, H=128, I=96, E=40, K=5, S=1, L=0, r=0, rsf=2.5) if tiny else
+             synth.LayerShape(T=300, H=128, I=96, E=8, K=3, S=1, L=4, r=16, rsf=2.5))
     inp = inputs(shape, synth.Recipe(adapters="uniform_all"), seed=13)
     dims = ml.make_dims(shape.T, shape.H, shape.I, shape.E, shape.K, shape.S, shape.L, shape.r, shape.rsf,
                         block_m=bm)
