@@ -49,38 +49,10 @@ struct GemmParams {
     const uint8_t *Wscale = nullptr;  // MXFP8 weights: E8M0 scale of each 32-element block, [rows][Kdim/32]
 };
 
-// Add the LoRA expand term sum_k s[p,k] * B[a,e,row,k] to `v` for NC output
-// rows starting at `rows[c]` (rows[c] < 0: skipped).  s is the fixed-order sum
-// of the split-K partials; `prow` is the row of s (the sorted row, or the
-// pair index when s is kept by pair).  r is a multiple of 8.
-template <int NC>
-__device__ __forceinline__ void lora_expand_add(const GemmParams &p, int e, int a, int prow, const int *rows,
-                                                int rows_per_expert, float *v) {
-    const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r;
-    for (int k0 = 0; k0 < p.r; k0 += 8) {
-        float s[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s[i] = 0.f;
-        for (int sp = 0; sp < p.split; ++sp) {
-            const float4 *sv = reinterpret_cast<const float4 *>(p.s_part + ((int64_t)sp * p.cap + prow) * p.r + k0);
-            const float4 lo = sv[0], hi = sv[1];
-            s[0] += lo.x; s[1] += lo.y; s[2] += lo.z; s[3] += lo.w;
-            s[4] += hi.x; s[5] += hi.y; s[6] += hi.z; s[7] += hi.w;
-        }
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            if (rows[c] < 0) continue;
-            const u32x4 bv = *reinterpret_cast<const u32x4 *>(Bae + (int64_t)rows[c] * p.r + k0);
-            float acc = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc += s[2 * i] * bf16_to_f32((uint16_t)(bv[i] & 0xffffu));
-                acc += s[2 * i + 1] * bf16_to_f32((uint16_t)(bv[i] >> 16));
-            }
-            v[c] += acc;
-        }
-    }
-}
+// LoRA expand in the epilogue: ranks per staged chunk and bf16 elements of
+// B rows staged at once (16 KiB)
+constexpr int kLoraRC = 32;
+constexpr int kLoraStage = 8192;
 
 // WP: weights in the packed layout of moe_lora_pack_weights.  A weight
 // fragment is then one 16-row group (for gate_up the gate and up rows of 8
@@ -109,6 +81,12 @@ __device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const Fuse
     __shared__ __attribute__((aligned(16))) uint8_t mx_sc[MX ? BW * kMxMaxBlocks : 16];
     // ROUTE: the slots' experts, the block's pairs, padded row count and expert
     __shared__ int r_e[ROUTE ? 64 : 1], r_rows[ROUTE ? BT : 1], r_blk[2];
+    // LoRA expand staging: B rows of a batch of adapters [q][tile column][kc],
+    // the rows' s values, and per row its adapter, adapter slot and s row
+    constexpr bool LORA = !ROUTE;
+    __shared__ __attribute__((aligned(16))) uint16_t l_b[LORA ? kLoraStage : 8];
+    __shared__ __attribute__((aligned(16))) float l_s[LORA ? BT : 1][kLoraRC];
+    __shared__ int l_a[BT], l_q[BT], l_srow[BT], l_list[BT + 1];
 
     const int b = blockIdx.y;
     int npp, e;
@@ -177,6 +155,9 @@ __device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const Fuse
     }
     const uint16_t *xrow[NS];
     bool xok[NS];
+    // LoRA: pair and adapter of rows ns*16 + l16, fetched now for the
+    // epilogue (the loads retire long before the main loop's)
+    int row_f[NS], row_a[NS];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
         const int prow = b * BT + ns * 16 + l16;
@@ -185,6 +166,8 @@ __device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const Fuse
         int64_t row = 0;
         if (xok[ns]) row = GU ? (f / p.Kp) : prow;
         xrow[ns] = p.in + row * Kd;
+        row_f[ns] = f;
+        row_a[ns] = (p.lora && xok[ns]) ? p.adapter_ids[f / p.Kp] : -1;
     }
 
     f32x4 acc[MS][NS];
@@ -344,6 +327,123 @@ __device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const Fuse
     }
     __syncthreads();
 
+    // LoRA expand on the finished tile: buf[1][j][c] += sum_k s[j][k] *
+    // B[a_j, e, row(c), k] for the block's rows j with an adapter.  The B
+    // rows of the adapters present (in batches that fit kLoraStage) and the
+    // rows' s values (split-K partials summed in order) are staged in LDS with
+    // all their loads in flight at once, ranks kLoraRC at a time; each column
+    // then adds its 8-rank partial dot products in rank order.
+    if constexpr (LORA) {
+        if (p.lora) {
+            // weight row (within the expert) of tile column c, or -1 past N
+            auto col_row = [&](int c) -> int {
+                if constexpr (GU && WP && !MX) {
+                    // packed quads: gate f, gate f+1, up f, up f+1, gate f+2, ...
+                    const int m = c & 7, feat = i0 + 4 * (c >> 3) + (m >> 2) * 2 + (m & 1);
+                    return feat < N ? (((m >> 1) & 1) ? N + feat : feat) : -1;
+                } else if constexpr (GU) {
+                    const bool up = c >= BW / 2;
+                    const int feat = i0 + (up ? c - BW / 2 : c);
+                    return feat < N ? (up ? N + feat : feat) : -1;
+                } else {
+                    const int feat = i0 + c;
+                    return feat < N ? feat : -1;
+                }
+            };
+            if (w == 0 && l16 == lane) {
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) {
+                    const int j = ns * 16 + l16, a = row_a[ns];
+                    l_a[j] = (a >= 0 && a < p.L) ? a : -1;
+                    l_srow[j] = p.s_by_pair ? row_f[ns] : b * BT + j;
+                }
+            }
+            __syncthreads();
+            // adapter slots in order of first appearance among the rows
+            if (w == 0) {
+                const int a = lane < BT ? l_a[lane] : -1;
+                int first = lane;
+                for (int i = 0; i < BT; ++i)
+                    if (i < first && l_a[i] == a) first = i;
+                const bool lead = a >= 0 && first == lane;
+                const uint64_t m = __ballot(lead);
+                if (lane < BT) l_q[lane] = a >= 0 ? __popcll(m & ((1ull << first) - 1)) : -1;
+                if (lead) l_list[__popcll(m & ((1ull << lane) - 1))] = a;
+                if (lane == 0) l_list[BT] = __popcll(m);
+            }
+            __syncthreads();
+            const int nad = l_list[BT];
+            const int tid = (int)threadIdx.x;
+            for (int k0 = 0; k0 < p.r; k0 += kLoraRC) {
+                const int kc = min(kLoraRC, p.r - k0), kp8 = kc / 8;
+                const int nab = kLoraStage / (BW * kc);  // adapters per batch
+                for (int q0 = 0; q0 < nad; q0 += nab) {
+                    const int nb = min(nab, nad - q0);
+                    // B pieces (16 bytes = 8 ranks): (slot, column, piece)
+                    const int npc = nb * BW * kp8;
+                    u32x4 bv[kLoraStage / (8 * 256)];
+#pragma unroll
+                    for (int i = 0; i < kLoraStage / (8 * 256); ++i) {
+                        const int u = tid + 256 * i;
+                        bv[i] = u32x4{0u, 0u, 0u, 0u};
+                        if (u < npc) {
+                            const int qq = u / (BW * kp8), rem = u - qq * (BW * kp8);
+                            const int c = rem / kp8, kq = rem - c * kp8;
+                            const int grow = col_row(c);
+                            const int a = l_list[q0 + qq];
+                            const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r;
+                            if (grow >= 0) bv[i] = *reinterpret_cast<const u32x4 *>(Bae + (int64_t)grow * p.r + k0 + 8 * kq);
+                        }
+                    }
+                    // s values of the batch's rows, 4 ranks per thread
+                    float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
+                    const int k4n = kc / 4;
+                    const int sj = tid / k4n, sk = tid - sj * k4n;
+                    const bool s_in = sj < BT && l_q[sj] >= q0 && l_q[sj] < q0 + nb;
+                    if (s_in) {
+                        for (int sp = 0; sp < p.split; ++sp) {
+                            const float4 x4 = *reinterpret_cast<const float4 *>(
+                                p.s_part + ((int64_t)sp * p.cap + l_srow[sj]) * p.r + k0 + 4 * sk);
+                            sv.x += x4.x; sv.y += x4.y; sv.z += x4.z; sv.w += x4.w;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < kLoraStage / (8 * 256); ++i) {
+                        const int u = tid + 256 * i;
+                        if (u < npc) *reinterpret_cast<u32x4 *>(l_b + (int64_t)u * 8) = bv[i];
+                    }
+                    if (s_in) *reinterpret_cast<float4 *>(&l_s[sj][4 * sk]) = sv;
+                    __syncthreads();
+                    // each (row, 4-column group): the 8-rank partial sums in rank order
+                    for (int u = tid; u < BT * (BW / 4); u += 256) {
+                        const int j = u / (BW / 4), c4 = u - j * (BW / 4);
+                        const int q = l_q[j] - q0;
+                        if (l_a[j] < 0 || q < 0 || q >= nb) continue;
+#pragma unroll
+                        for (int cc = 0; cc < 4; ++cc) {
+                            const int c = 4 * c4 + cc;
+                            if (col_row(c) < 0) continue;
+                            float v = buf[1][j][c];
+                            for (int g8 = 0; g8 < kp8; ++g8) {
+                                const u32x4 bb = *reinterpret_cast<const u32x4 *>(l_b + ((int64_t)(q * BW + c) * kp8 + g8) * 8);
+                                const float *s8 = &l_s[j][8 * g8];
+                                float acc = 0.f;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    acc += s8[2 * i] * bf16_to_f32((uint16_t)(bb[i] & 0xffffu));
+                                    acc += s8[2 * i + 1] * bf16_to_f32((uint16_t)(bb[i] >> 16));
+                                }
+                                v += acc;
+                            }
+                            buf[1][j][c] = v;
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+        }
+    }
+
     // Epilogue on the finished tile buf[1][token][feature].
     if (GU && WP && !MX) {
         // tile rows 8qp .. 8qp+7 = gate f, gate f+1, up f, up f+1, gate f+2,
@@ -365,18 +465,6 @@ __device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const Fuse
                     v[2 * h2 + 1] = buf[1][j][8 * qp + 4 * h2 + 1];
                     v[4 + 2 * h2 + 0] = buf[1][j][8 * qp + 4 * h2 + 2];
                     v[4 + 2 * h2 + 1] = buf[1][j][8 * qp + 4 * h2 + 3];
-                }
-                if (p.lora) {
-                    const int a = p.adapter_ids[f / p.Kp];
-                    if (a >= 0 && a < p.L) {
-                        int rows[8];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            rows[i] = col0 + i;
-                            rows[4 + i] = N + col0 + i;
-                        }
-                        lora_expand_add<8>(p, e, a, p.s_by_pair ? f : prow, rows, rows_per_expert, v);
-                    }
                 }
                 float hv[4];
 #pragma unroll
@@ -403,18 +491,6 @@ __device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const Fuse
                     v[i] = buf[1][j][cg * 4 + i];
                     v[4 + i] = buf[1][j][BW / 2 + cg * 4 + i];
                 }
-                if (p.lora) {
-                    const int a = p.adapter_ids[f / p.Kp];
-                    if (a >= 0 && a < p.L) {
-                        int rows[8];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            rows[i] = col0 + i;
-                            rows[4 + i] = N + col0 + i;
-                        }
-                        lora_expand_add<8>(p, e, a, p.s_by_pair ? f : prow, rows, rows_per_expert, v);
-                    }
-                }
                 float hv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) hv[i] = silu(v[i]) * v[4 + i];
@@ -436,28 +512,25 @@ __device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const Fuse
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = buf[1][j][cg * 4 + i];
-            if (p.lora) {
-                const int a = p.adapter_ids[f / p.Kp];
-                if (a >= 0 && a < p.L) {
-                    int rows[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) rows[i] = col0 + i;
-                    lora_expand_add<4>(p, e, a, p.s_by_pair ? f : prow, rows, rows_per_expert, v);
-                }
-            }
             *reinterpret_cast<uint2 *>(yout + (int64_t)f * N + col0) =
                 make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
     }
 }
 
+// Three workgroups per CU at 16 rows per block (two at 32): the register
+// budget that keeps that many resident.
+template <int BT> constexpr int stream_waves_per_eu() { return BT == 16 ? 3 : 2; }
+
 template <int BW, int BT, bool GU, bool WP, bool MX = false>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<BT>())))
+void gemm_stream_kernel(GemmParams p) {
     gemm_stream_body<BW, BT, GU, WP, MX, false>(p, nullptr);
 }
 
 template <int BW, int BT, bool WP, bool MX>
-__global__ __launch_bounds__(256) void gemm_stream_route_kernel(GemmParams p, FusedRoute fr) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<BT>())))
+void gemm_stream_route_kernel(GemmParams p, FusedRoute fr) {
     gemm_stream_body<BW, BT, true, WP, MX, true>(p, &fr);
 }
 
