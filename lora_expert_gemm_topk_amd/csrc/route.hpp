@@ -35,6 +35,18 @@ struct RouteParams {
     const float *bias = nullptr;  // [E] (biased router only; nullptr = zero bias)
 };
 
+// The value of `v` in lane j, j the same in every lane: v_readlane (a
+// scalar read) rather than a permute through the LDS crossbar.
+__device__ __forceinline__ float lane_value(float v, int j) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+}
+__device__ __forceinline__ double lane_value(double v, int j) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, j);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), j);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 template <typename V>
 struct CandT {
     V v;
@@ -79,6 +91,39 @@ __device__ __forceinline__ Cand wave_best(Cand c) {
     return w;
 }
 
+// The same arg-max for the biased router's fp64 keys, carrying the
+// candidate's unbiased score `s` along.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_int(int x, int none) {
+    return __builtin_amdgcn_update_dpp(none, x, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_double(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)dpp_int<CTRL, ROW_MASK>((int)(uint32_t)b, 0);
+    const uint32_t hi = (uint32_t)dpp_int<CTRL, ROW_MASK>((int)(uint32_t)(b >> 32), 0);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void cand_dpp_step(CandT<double> &c, double &s) {
+    const CandT<double> o{dpp_double<CTRL, ROW_MASK>(c.v), dpp_int<CTRL, ROW_MASK>(c.i, 0x7fffffff)};
+    const double os = dpp_double<CTRL, ROW_MASK>(s);
+    if (better(o, c)) {
+        c = o;
+        s = os;
+    }
+}
+__device__ __forceinline__ CandT<double> wave_best(CandT<double> c, double &s) {
+    cand_dpp_step<0xb1, 0xf>(c, s);
+    cand_dpp_step<0x4e, 0xf>(c, s);
+    cand_dpp_step<0x141, 0xf>(c, s);
+    cand_dpp_step<0x140, 0xf>(c, s);
+    cand_dpp_step<0x142, 0xa>(c, s);
+    cand_dpp_step<0x143, 0xc>(c, s);
+    s = lane_value(s, 63);
+    return CandT<double>{lane_value(c.v, 63), __builtin_amdgcn_readlane(c.i, 63)};
+}
+
 // Biased router for token t (see the file comment): returns to lane j the
 // expert id of slot j like route_one_token.
 template <int VPL>
@@ -118,15 +163,7 @@ __device__ int route_one_token_bias(const RouteParams &rp, int t, bool write) {
                 cs = sc[j];
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            CandT<double> o{__shfl_xor(c.v, off, 64), __shfl_xor(c.i, off, 64)};
-            const double os = __shfl_xor(cs, off, 64);
-            if (better(o, c)) {
-                c = o;
-                cs = os;
-            }
-        }
+        c = wave_best(c, cs);  // every lane now holds the same winner and its score
         if ((c.i & 63) == lane) {
 #pragma unroll
             for (int j = 0; j < VPL; ++j)
@@ -138,7 +175,7 @@ __device__ int route_one_token_bias(const RouteParams &rp, int t, bool write) {
         }
     }
     double sum = 0.0;
-    for (int j = 0; j < K; ++j) sum += __shfl(mys, j, 64);
+    for (int j = 0; j < K; ++j) sum += lane_value(mys, j);
     const int Kp = K + S;
     if (write && lane < K) {
         rp.ids[(int64_t)t * Kp + lane] = myi;
@@ -189,11 +226,11 @@ __device__ int route_one_token(const RouteParams &rp, int t, bool write = true) 
             myi = c.i;
         }
     }
-    const double m = (double)__shfl(myv, 0, 64);
+    const double m = (double)lane_value(myv, 0);
     const double ex = (lane < K) ? exp((double)myv - m) : 0.0;
     double sum = 0.0;
     if (rp.renorm) {
-        for (int j = 0; j < K; ++j) sum += __shfl(ex, j, 64);
+        for (int j = 0; j < K; ++j) sum += lane_value(ex, j);
     } else {
         for (int e = 0; e < E; ++e) sum += exp((double)l[e] - m);
     }

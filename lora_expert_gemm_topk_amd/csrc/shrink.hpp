@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void route_shrink_kernel(RouteParams rp, RowSh
     __shared__ int e_slot;
     if (threadIdx.x < 64) {
         const int myi = route_one_token<VPL>(rp, t, j == 0);
-        const int e = __shfl(myi, j, 64);
+        const int e = __builtin_amdgcn_readlane(myi, j);
         if (threadIdx.x == 0) e_slot = e;
     }
     const int a = sp.adapter_ids[t];
