@@ -496,7 +496,7 @@ def main() -> int:
     torch.cuda.empty_cache()
     if args.prefill:
         print(f"bench: {args.prefill}", file=sys.stderr, flush=True)
-        p = measure(args.prefill, max(5, args.steps // 5), max(2, args.warmup // 5), packed=not args.row_major)
+        p = measure(args.prefill, max(20, args.steps // 2), max(5, args.warmup // 2), packed=not args.row_major)
         ps = p["shape"]
         result["prefill"] = {"workload": args.prefill, "tokens_per_s": ps.T / (p["ms"] * 1e-3),
                              "ms_per_step": p["ms"], "roofline": roofline_obj(p, "mfma"),
