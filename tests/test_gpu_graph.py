@@ -28,10 +28,12 @@ def _weights(inp, packed):
     return ml.PackedWeights(inp.w13, inp.w2) if packed else None
 
 
-@pytest.mark.parametrize("T,bm,packed", [(48, 0, False), (64, 0, True), (600, 128, True), (1, 0, False),
-                                         (64, 0, "mx"), (7, 32, "mx"), (64, 0, "mxp")])
-def test_graph_replay_equals_eager(T, bm, packed):
-    shape = synth.LayerShape(T=T, H=256, I=192, E=8, K=2, S=1, L=3, r=16, rsf=2.5)
+# L = 0 with T <= 4: the gate_up launch routes and aligns (three launches)
+@pytest.mark.parametrize("T,bm,packed,L", [(48, 0, False, 3), (64, 0, True, 3), (600, 128, True, 3), (1, 0, False, 3),
+                                           (64, 0, "mx", 3), (7, 32, "mx", 3), (64, 0, "mxp", 3),
+                                           (1, 0, True, 0), (3, 32, "mxp", 0)])
+def test_graph_replay_equals_eager(T, bm, packed, L):
+    shape = synth.LayerShape(T=T, H=256, I=192, E=8, K=2, S=1, L=L, r=16 if L else 0, rsf=2.5)
     inp = synth.make_inputs(shape, synth.Recipe(adapters="uniform_all"), seed=T, device="cuda")
     pw = _weights(inp, packed)
     ws = ml.Workspace()

@@ -159,6 +159,8 @@ SMALL = [
     dict(T=4, H=64, I=72, E=256, K=15, S=1, L=0, r=0, rsf=2.0, dtype="bf16", block_m=32),
     dict(T=2, H=200, I=40, E=3, K=3, S=0, L=0, r=0, dtype="bf16"),
     dict(T=4, H=64, I=40, E=257, K=4, S=0, L=0, r=0, dtype="bf16"),
+    dict(T=1, H=64, I=40, E=1, K=1, S=0, L=0, r=0, dtype="bf16"),
+    dict(T=1, H=64, I=40, E=1, K=1, S=1, L=0, r=0, rsf=2.0, dtype="bf16"),
     # a wide, ragged hidden size (12296 = 8 * 1537, not a multiple of 32) on both GEMM kinds
     dict(T=24, H=12296, I=64, E=4, K=2, S=0, L=2, r=16, dtype="bf16", block_m=16),
     dict(T=260, H=12296, I=64, E=4, K=2, S=0, L=2, r=16, dtype="bf16", block_m=128),
