@@ -929,6 +929,9 @@ __device__ __forceinline__ void tiny_align_store(const AlignParams &p, const Tin
 struct FusedRoute {
     AlignParams ap;
     RouteParams rp;
+    // the host kernel's weights to touch while routing (see its use); per-expert byte strides
+    const unsigned char *touch13 = nullptr, *touch2 = nullptr;
+    int64_t stride13 = 0, stride2 = 0;
 };
 
 template <int BT, int VPL>

@@ -91,9 +91,39 @@ __device__ __forceinline__ void gemm_stream_body(const GemmParams &p, const Fuse
     const int b = blockIdx.y;
     int npp, e;
     if constexpr (ROUTE) {
+        // While the routing's loads are in flight, wave 3 (which routes only
+        // at T = 4) reads one dword of every expert's gate_up weights at this
+        // workgroup's share of them and one of its down weights: the address
+        // translations (and those lines) of the weights this call will stream
+        // are then warm when the expert is known, instead of missing after
+        // the routing.  The values are folded into nothing but a register.
+        constexpr int kTouch = 5;  // experts in chunks of 64 (Ep <= 256 + 64)
+        uint32_t touch[kTouch][2];
+        const int Ep = fr->ap.Ep;
+        const bool toucher = (threadIdx.x >> 6) == 3;
+        if (toucher) {
+            const int64_t o13 = (fr->stride13 / gridDim.x * blockIdx.x) & ~(int64_t)63;
+            const int64_t o2 = (fr->stride2 / ((int64_t)gridDim.x * gridDim.y) * (blockIdx.y * gridDim.x + blockIdx.x)) &
+                               ~(int64_t)63;
+#pragma unroll
+            for (int j = 0; j < kTouch; ++j) {
+                const int ee = 64 * j + lane_id();
+                touch[j][0] = touch[j][1] = 0u;
+                if (ee < Ep) {
+                    touch[j][0] = *reinterpret_cast<const uint32_t *>(fr->touch13 + ee * fr->stride13 + o13);
+                    touch[j][1] = *reinterpret_cast<const uint32_t *>(fr->touch2 + ee * fr->stride2 + o2);
+                }
+            }
+        }
         route_align_in_block<BT, 4>(*fr, b, blockIdx.x == 0 && b == 0, r_e, r_rows, r_blk);
         npp = r_blk[0];
         e = r_blk[1];
+        if (toucher) {
+            uint32_t s = 0;
+#pragma unroll
+            for (int j = 0; j < kTouch; ++j) s ^= touch[j][0] ^ touch[j][1];
+            asm volatile("" ::"v"(s));
+        }
     } else {
         npp = p.counters[0];
         e = 0;

@@ -853,6 +853,18 @@ int moe_lora_forward(const moe_lora_dims *d, const moe_lora_args *a, void *strea
         fused.ap = align_params(p, d, ids, a->adapter_ids, sorted, nullptr, bexp, cnt, items, cnt + 1, tmp, nullptr,
                                 cnt + 2, a->num_post_pad_out, queue);
         fused.rp = rp_align;
+        const int64_t Ep = p.Ep, H = d->H, I = d->I;
+        const int64_t es = a->weights_mxfp8 ? 1 : 2;  // bytes per weight element (MXFP8 codes: 1)
+        const int64_t b13 = a->weights_packed ? (int64_t)(a->weights_mxfp8 ? moe_lora_packed_mxfp8_bytes(d, 0)
+                                                                            : moe_lora_packed_weight_bytes(d, 0))
+                                              : Ep * 2 * I * H * es;
+        const int64_t b2 = a->weights_packed ? (int64_t)(a->weights_mxfp8 ? moe_lora_packed_mxfp8_bytes(d, 1)
+                                                                           : moe_lora_packed_weight_bytes(d, 1))
+                                             : Ep * H * I * es;
+        fused.touch13 = (const unsigned char *)a->w13;
+        fused.touch2 = (const unsigned char *)a->w2;
+        fused.stride13 = b13 / Ep;
+        fused.stride2 = b2 / Ep;
     } else {
         const int r2 = launch_align(p, d, ids, a->adapter_ids, sorted, p.kind == 2 ? sadp : nullptr, bexp, cnt,
                                     items, cnt + 1, tmp, p.kind == 2 ? tiles : nullptr, cnt + 2, st,
