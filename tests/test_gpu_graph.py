@@ -4,8 +4,8 @@ The forward neither synchronises the host nor allocates, and clears its
 counters with kernels (no memset nodes), so a captured call can be replayed.
 Each replay is checked bit for bit against an eager call on the same inputs,
 with eager work and host synchronisation between the replays, for the
-streaming and the LDS-tiled plans, with packed weights and with MXFP8
-weights.  The input check is captured too and replayed over changing
+streaming and the LDS-tiled plans, with packed weights, with MXFP8
+weights, for calls routed inside gate_up, and for the fp32 layer.  The input check is captured too and replayed over changing
 buffer contents.
 """
 from __future__ import annotations
@@ -58,6 +58,32 @@ def test_graph_replay_equals_eager(T, bm, packed, L):
         eager = ml.forward_inputs(inp, block_m=bm, packed=pw, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(eager.view(torch.int16), ref.view(torch.int16)), f"eager after replay {i}"
+
+
+def test_graph_replay_equals_eager_fp32():
+    """The fp32 layer (its own GEMM kernels) captured and replayed the same way."""
+    shape = synth.LayerShape(T=16, H=128, I=256, E=4, K=2, S=1, L=2, r=8, rsf=2.5, dtype=synth.F32)
+    inp = synth.make_inputs(shape, synth.Recipe(adapters="uniform_all"), seed=3, device="cuda")
+    ws = ml.Workspace()
+    out = torch.empty((shape.T, shape.H), dtype=torch.float32, device="cuda")
+    ref = ml.forward_inputs(inp).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ml.forward_inputs(inp, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ml.forward_inputs(inp, out=out, workspace=ws)
+    for i in range(4):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {i}"
+        eager = ml.forward_inputs(inp, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int32), ref.view(torch.int32)), f"eager after replay {i}"
 
 
 def test_graph_replay_of_the_input_check():
