@@ -60,11 +60,16 @@ extern "C" {
 #define MOE_LORA_BF16 1
 
 /* Stages of moe_lora_forward, in launch order (for moe_lora_args.stage_events).
- * With the LDS-tiled GEMM (gemm_kind 2) x is gathered and packed into
- * sorted-row order: in the same launch as the gate_up shrink (stage SHRINK13)
- * when LoRA is active, else as a second launch of stage ALIGN.  ALIGN is one
- * launch below 8192 (token, slot) pairs and four from there on; each other
- * stage is one kernel. */
+ * A stage launches nothing when its work runs in another stage's launch:
+ * with the streaming GEMM (gemm_kind 1) and LoRA the gate_up shrink runs in
+ * the router's launch (SHRINK13 empty); small calls otherwise route inside
+ * the alignment's launch (ROUTE empty); tiny calls without LoRA (T <= 4, at
+ * most 64 (token, slot) pairs, E <= 256) route and align inside the gate_up
+ * launch (ROUTE and ALIGN empty).  With the LDS-tiled GEMM (gemm_kind 2) x
+ * is gathered and packed into sorted-row order: in the same launch as the
+ * gate_up shrink (stage SHRINK13) when LoRA is active, else as a second
+ * launch of stage ALIGN.  ALIGN is one launch below 8192 pairs and four from
+ * there on; every other stage is at most one kernel. */
 #define MOE_LORA_STAGE_ROUTE 0
 #define MOE_LORA_STAGE_ALIGN 1
 #define MOE_LORA_STAGE_SHRINK13 2
