@@ -97,6 +97,9 @@ ALIGN_CASES = [
     # a few pairs over many mostly empty experts, and a key count whose LDS
     # need just exceeds what the one-pass form takes
     dict(T=16, E=1024, K=4, S=0, L=0, r=0), dict(T=12, E=700, K=3, S=1, L=2, r=8),
+    # 65 to 256 pairs (just past one wavefront, mid-range, the top): the one-workgroup form
+    dict(T=65, E=9, K=1, S=0, L=0, r=0), dict(T=33, E=12, K=3, S=1, L=5, r=8),
+    dict(T=50, E=300, K=5, S=0, L=3, r=8, bm=32), dict(T=32, E=8, K=7, S=1, L=2, r=8, lbm=32),
 ]
 
 
