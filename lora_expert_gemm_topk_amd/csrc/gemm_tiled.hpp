@@ -177,6 +177,21 @@ __device__ __forceinline__ void dma16(const void *g, __attribute__((address_spac
         : "s"(m0v), "v"(g));
 }
 
+// dma16 from a wave-uniform base plus this lane's byte offset (the copy's
+// scalar-base form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16s(const void *base, uint32_t off,
+                                       __attribute__((address_space(3))) unsigned char *dst) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0v), "v"(off), "s"((uint64_t)(uintptr_t)base));
+}
+
 // Barrier for LDS data only: waits for this wave's LDS accesses, not for its
 // loads in flight.  (__syncthreads also waits for every outstanding global
 // load, and placed before the K loop it leads the compiler to drain all slab
@@ -583,9 +598,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     // After the K loop, each adapter present in the token tile adds
     // B[a, e] (its rows of this weight tile) times the bf16 shrink rows of
     // its tokens, as MFMAs on the same accumulators.  The ring, now free,
-    // streams only the weight side: unit u = (adapter q, 32-rank slab) is
-    // BW rows x 32 ranks, kStages*STAGE_BYTES / (BW*64) units fit, so many
-    // more are in flight than whole slabs would allow.  Each lane holds its
+    // streams only the weight side in units of BW x 32 ranks: an adapter's
+    // 32-rank slab, or, where the rank range holds 64 ranks, one of its two
+    // row halves (each copy instruction then reads whole 128-byte row
+    // pieces); kStages*STAGE_BYTES / (BW*64) units fit, so many more are in
+    // flight than whole slabs would allow.  Each unit's copies take a
+    // wave-uniform base and per-lane offsets fixed for the tile, so issuing
+    // them costs no vector instructions.  Each lane holds its
     // tokens' shrink rows in registers for 64 ranks at a time (read once per
     // tile) and zeroes those of other adapters before each MFMA; the MFMAs
     // of column tiles outside the adapter's run of rows (exact zeros) are
@@ -594,9 +613,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
     const uint16_t *s16 = reinterpret_cast<const uint16_t *>(p.s_part);
     auto lora_phase = [&](auto ntl) {
         constexpr int NTL = decltype(ntl)::value;
-        constexpr int UBYTES = BW * 64;                          // one unit: BW rows x 32 bf16 ranks
+        constexpr int UBYTES = BW * 64;                          // one unit: BW x 32 bf16 values
         constexpr int NSLOT = kStages * STAGE_BYTES / UBYTES;    // units the ring holds
-        static_assert(NSLOT >= 3 && NSLOT <= 12, "LoRA unit ring depth");
+        static_assert(NSLOT >= 4 && NSLOT <= 12 && NSLOT % 2 == 0, "LoRA unit ring depth");
         // wait for unit u with `younger` later units still in flight, then barrier
         auto wait_unit = [&](int younger) {
             switch (younger) {
@@ -616,38 +635,91 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
         int myad[NTL > 0 ? NTL : 1];  // adapter of this lane's token in column tile nt
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) myad[nt] = tok_a[(2 * nt + wn) * 32 + l32];
-        // this lane's B row offset (row * r, or -1 for rows past N) and rank
-        // within a 32-rank slab for weight-side copy j
-        int boff[LPW_A], bk[LPW_A];
+        // Both unit forms place row tile mt of wave row wm at 4096 mt + (a
+        // part fixed per lane), so a fragment read is (lane base ^ X) +
+        // 4096 mt + slot with X and the slot the same for the whole wave.
+        // 32-rank units: 1 KiB group g of the wave row's row tile mt (tile
+        // rows (BW/2) wm + 32 mt + 16 g ..) sits at block 4 mt + 2 wm + g,
+        // in the K slabs' group layout (packed or swizzled row-major).
+        // Wide units (a whole 64-rank range): unit (adapter, row half h) holds
+        // the 64 ranks of tile rows [h BW/2, (h+1) BW/2), the rows of wave row
+        // h, in 1 KiB blocks of 8 rows x 64 ranks, so every copy instruction
+        // reads 8 whole 128-byte row pieces (a 32-rank unit reads 16 half
+        // lines when r >= 64).  Lane l of block b moves row l/8, rank chunk
+        // (l%8) ^ (l/8) ^ (b%2) to 16-byte slot l%8 of its row: the fragment
+        // reads of 16 consecutive rows then hit 16 different bank groups.
+        // Rank chunk (of 8) lane l moves in copy j of a 32-rank / wide unit:
+        auto nchunk = [&](int j) { return WP ? lane >> 4 : swz_slot((w + 4 * j) * 16 + (lane >> 2), lane & 3); };
+        auto wchunk = [&](int j) { return (lane & 7) ^ (lane >> 3) ^ ((w + 4 * j) & 1); };
+        // byte offsets of those 16 bytes from the unit's base (adapter,
+        // expert, first rank of the range); rows past N read row 0 instead
+        // (their accumulator rows are never stored)
+        uint32_t noff[LPW_A], woff[2][LPW_A];
 #pragma unroll
         for (int j = 0; j < LPW_A; ++j) {
-            const int rr = (w + 4 * j) * 16 + (WP ? (lane & 15) : (lane >> 2));
+            const int b = w + 4 * j;
+            const int grp = ((b >> 1) & 1) * (BW / 32) + (b >> 2) * 2 + (b & 1);
             bool ok;
-            const int grow = tile_weight_row<GU>(rr, i0, N, ok);
-            boff[j] = ok ? grow * p.r : -1;
-            bk[j] = (WP ? (lane >> 4) : chunk_of[j]) * 8;
+            int grow = tile_weight_row<GU>(grp * 16 + (WP ? (lane & 15) : (lane >> 2)), i0, N, ok);
+            noff[j] = (uint32_t)(((ok ? grow : 0) * p.r + nchunk(j) * 8) * 2);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                grow = tile_weight_row<GU>(h * (BW / 2) + b * 8 + (lane >> 3), i0, N, ok);
+                woff[h][j] = (uint32_t)(((ok ? grow : 0) * p.r + wchunk(j) * 8) * 2);
+            }
         }
+        // lane bases: row l32 of row tile 0 at rank chunk lh (chunk 2 ks + lh
+        // of a 32-rank unit, 4 rcl + 2 ks + lh of a wide one: X flips the
+        // bits of ks and rcl)
+        const int nbase = (2 * wm + (l32 >> 4)) * 1024 +
+                          (WP ? lh * 256 + (l32 & 15) * 16 : (l32 & 15) * 64 + ((lh ^ swz_slot(l32, 0)) << 4));
+        const int wbase = (l32 >> 3) * 1024 + (l32 & 7) * 128 + ((lh ^ (l32 & 7) ^ ((l32 >> 3) & 1)) << 4);
         // every wave is past its last fragment read of the ring's K slabs
         lds_barrier();
         for (int c0 = 0; c0 < rs; c0 += 2) {      // ranks [32 c0, 32 c0 + 64)
             const int uc = min(2, rs - c0);        // 32-rank slabs per adapter in this range
             const int nu = n_adapters * uc;
-            // weight side of unit u: rows as the weight groups of a slab (the
-            // packed-layout block order with packed weights), ranks 32 rc ..
-            auto issue_unit = [&](int u) {
-                const int q = u / uc, rc = c0 + (u - q * uc);
-                const int a = __builtin_amdgcn_readfirstlane(alist[q]);
-                const uint16_t *Bae = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r + rc * kTileBK;
-                lds_t *slot = lds_base + (u % NSLOT) * UBYTES;
+            const bool wide = uc == 2;             // units of 64 ranks x half the rows
+            const bool full = (c0 + uc) * kTileBK <= p.r;  // no rank of the range past r
+            const int lbase = wide ? wbase : nbase;
+            uint32_t off0[LPW_A];
 #pragma unroll
-                for (int j = 0; j < LPW_A; ++j) {
-                    const bool in = boff[j] >= 0 && rc * kTileBK + bk[j] < p.r;
-                    dma(in ? (const void *)(Bae + boff[j] + bk[j]) : (const void *)g_zero_chunk, slot, j);
+            for (int j = 0; j < LPW_A; ++j) off0[j] = wide ? woff[0][j] : noff[j];
+            // adapter q's units q uc .. q uc + uc - 1: the weight rows of a
+            // slab (32 ranks) or of a row half (wide), ranks from 32 c0
+            auto issue_adapter = [&](int q) {
+                const int a = __builtin_amdgcn_readfirstlane(alist[q]);
+                const uint16_t *base = p.B + ((int64_t)a * p.Ep + e) * (int64_t)rows_per_expert * p.r + c0 * kTileBK;
+                lds_t *s0 = lds_base + ((q * uc) % NSLOT) * UBYTES;
+                lds_t *s1 = lds_base + ((q * uc + 1) % NSLOT) * UBYTES;
+                if (full) {
+#pragma unroll
+                    for (int j = 0; j < LPW_A; ++j) dma16s(base, off0[j], s0 + (w + 4 * j) * 1024);
+                    if (wide) {
+#pragma unroll
+                        for (int j = 0; j < LPW_A; ++j) dma16s(base, woff[1][j], s1 + (w + 4 * j) * 1024);
+                    }
+                } else {
+                    // rank chunks past r read zeros
+                    const char *cb = reinterpret_cast<const char *>(base);
+#pragma unroll
+                    for (int j = 0; j < LPW_A; ++j) {
+                        const bool in = c0 * kTileBK + (wide ? wchunk(j) : nchunk(j)) * 8 < p.r;
+                        dma(in ? (const void *)(cb + off0[j]) : (const void *)g_zero_chunk, s0, j);
+                    }
+                    if (wide) {
+#pragma unroll
+                        for (int j = 0; j < LPW_A; ++j) {
+                            const bool in = c0 * kTileBK + wchunk(j) * 8 < p.r;
+                            dma(in ? (const void *)(cb + woff[1][j]) : (const void *)g_zero_chunk, s1, j);
+                        }
+                    }
                 }
             };
-            // units are consumed an adapter (uc units) at a time, one barrier each
-            const int npre = min(nu, NSLOT - uc);
-            for (int u = 0; u < npre; ++u) issue_unit(u);
+            // units are consumed an adapter (uc units) at a time, one barrier
+            // each; the ring holds NSLOT / uc adapters
+            const int apr = wide ? NSLOT / 2 : NSLOT;
+            for (int q = 0; q < min(n_adapters, apr - 1); ++q) issue_adapter(q);
             // shrink rows: lane (l32, lh) of column tile nt holds ranks
             // 32 c0 + 16 kq + 8 lh .. + 7 of tile row (2 nt + wn) 32 + l32
             u32x4 sfr[NTL > 0 ? NTL : 1][4];
@@ -674,19 +746,20 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, const int
                 // issued so far: units 0 .. min(u0 + NSLOT - uc, nu) - 1; wait for this adapter's
                 wait_unit(min(nu - u0 - uc, NSLOT - 2 * uc));
                 // into the slots of adapter q - 1, which every wave is done with
-                for (int u = u0 + NSLOT - uc; u < min(nu, u0 + NSLOT); ++u) issue_unit(u);
+                if (q + apr - 1 < n_adapters) issue_adapter(q + apr - 1);
 #pragma unroll
                 for (int rcl = 0; rcl < 2; ++rcl) {
                     if (rcl >= uc) break;
-                    const int u = u0 + rcl;
+                    const int u = u0 + (wide ? wm : rcl);
                     const unsigned char *slot = lds + (u % NSLOT) * UBYTES;
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         if ((c0 + rcl) * kTileBK + ks * 16 >= p.r) break;  // ranks past r
+                        const int x = wide ? (4 * rcl + 2 * ks) << 4 : ks * (WP ? 512 : 32);
+                        const unsigned char *fr = slot + (lbase ^ x);
                         u32x4 af[MT];
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            af[mt] = *reinterpret_cast<const u32x4 *>(slot + lds_off<WP>(a_row0 + mt * 32, ks * 2 + lh));
+                        for (int mt = 0; mt < MT; ++mt) af[mt] = *reinterpret_cast<const u32x4 *>(fr + mt * 4096);
 #pragma unroll
                         for (int nt = 0; nt < NTL; ++nt) {
                             const int cr = (2 * nt + wn) * 32;

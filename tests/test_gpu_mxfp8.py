@@ -93,6 +93,7 @@ def test_mxfp8_gptoss_decode_full_size():
 TILED = [
     dict(T=512, H=256, I=192, E=4, K=2, S=0, L=3, r=16, block_m=128),
     dict(T=600, H=96, I=160, E=3, K=2, S=1, L=2, r=32, rsf=2.5, block_m=256),
+    dict(T=400, H=128, I=96, E=3, K=2, S=0, L=3, r=64, block_m=128),
     dict(T=700, H=160, I=64, E=4, K=3, S=0, L=0, r=0, block_m=128),
     dict(T=300, H=3072, I=64, E=2, K=1, S=0, L=2, r=8, block_m=128),
     dict(T=300, H=64, I=3072, E=2, K=2, S=1, L=2, r=8, block_m=256),

@@ -77,6 +77,8 @@ SMALL = [
     dict(T=500, H=256, I=384, E=6, K=2, S=1, L=4, r=32, rsf=2.5, block_m=256),
     dict(T=260, H=136, I=96, E=3, K=2, S=0, L=2, r=16, block_m=256),    # tiled, H not a slab multiple
     dict(T=200, H=128, I=128, E=5, K=3, S=0, L=0, r=0, block_m=128),    # tiled, no LoRA
+    dict(T=300, H=192, I=136, E=4, K=2, S=1, L=3, r=64, rsf=2.0, block_m=256),  # tiled, 64-rank units
+    dict(T=260, H=128, I=96, E=3, K=2, S=0, L=2, r=96, block_m=128),    # tiled, 64 + 32 ranks
     dict(T=50, H=96, I=64, E=7, K=1, S=0, L=0, r=0),                    # streaming, no LoRA
     dict(T=1, H=96, I=64, E=64, K=8, S=1, L=0, r=0, rsf=2.5),           # routed inside gate_up
 ]

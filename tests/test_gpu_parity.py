@@ -139,6 +139,10 @@ SMALL = [
     dict(T=500, H=256, I=384, E=6, K=2, S=1, L=4, r=32, rsf=2.5, dtype="bf16", block_m=128),
     dict(T=260, H=192, I=96, E=3, K=2, S=0, L=2, r=16, dtype="bf16", block_m=256, split=2),
     dict(T=200, H=128, I=128, E=5, K=3, S=0, L=0, r=0, dtype="bf16", block_m=128),
+    # tiled LoRA expand in 64-rank units: r=48 (ranks 48..63 of the unit
+    # zero), r=96 (one 64-rank range, then a 32-rank one), ragged gate tiles
+    dict(T=300, H=192, I=160, E=4, K=2, S=1, L=3, r=48, rsf=2.0, dtype="bf16", block_m=128),
+    dict(T=260, H=128, I=136, E=3, K=2, S=0, L=3, r=96, dtype="bf16", block_m=256),
     # 64 slots per token: the most the router launch takes the gate_up shrink for
     dict(T=8, H=64, I=64, E=100, K=63, S=1, L=3, r=8, rsf=2.0, dtype="bf16"),
     # K = E: every pair of a token on a different expert, all experts on every token
