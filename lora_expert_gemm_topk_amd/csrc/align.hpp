@@ -105,6 +105,19 @@ __host__ __device__ inline int64_t align_lds_ints(int NW, int Ep, int La, int64_
 
 // In-place exclusive scan of arr[0, n) in LDS by the whole workgroup.
 // Returns the total to every thread.  scr holds >= 17 ints.
+// Inclusive prefix sum over the 64 lanes (all active), by DPP: shifts by
+// 1, 2, 4, 8 lanes inside each row of 16, then rows 1 and 3 add the last
+// lane of the row before them and rows 2 and 3 add lane 31.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += dpp_int<0x111, 0xf>(x, 0);  // row_shr:1
+    x += dpp_int<0x112, 0xf>(x, 0);  // row_shr:2
+    x += dpp_int<0x114, 0xf>(x, 0);  // row_shr:4
+    x += dpp_int<0x118, 0xf>(x, 0);  // row_shr:8
+    x += dpp_int<0x142, 0xa>(x, 0);  // row_bcast15 into rows 1, 3
+    x += dpp_int<0x143, 0xc>(x, 0);  // row_bcast31 into rows 2, 3
+    return x;
+}
+
 __device__ inline int block_excl_scan(int *arr, int n, int *scr) {
     const int nt = (int)blockDim.x, tid = (int)threadIdx.x;
     const int nw = nt >> 6, lane = tid & 63, w = tid >> 6;
@@ -113,22 +126,15 @@ __device__ inline int block_excl_scan(int *arr, int n, int *scr) {
     const int e = min(n, b + per);
     int local = 0;
     for (int i = b; i < e; ++i) local += arr[i];
-    int x = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    const int x = wave_incl_scan(local);
     if (lane == 63) scr[w] = x;
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < nw; ++i) {
-            const int t = scr[i];
-            scr[i] = run;
-            run += t;
-        }
-        scr[nw] = run;
+    if (w == 0) {
+        // the wave totals (at most 16) scanned by wave 0
+        const int t = lane < nw ? scr[lane] : 0;
+        const int y = wave_incl_scan(t);
+        if (lane < nw) scr[lane] = y - t;
+        if (lane == nw - 1) scr[nw] = y;
     }
     __syncthreads();
     int run = scr[w] + x - local;
@@ -150,10 +156,11 @@ __device__ __forceinline__ uint16_t *align_keys(int *lds, int NW, int Ep, int La
 // Everything after the scatter: padding rows, the tail, the block -> expert
 // map, the GEMM token tiles, the LoRA items and the counts.  Needs offE[Ep+1]
 // and totE[Ep] (expert offsets and pair counts) and, with LoRA, cnt2[NK]
-// (pairs per (expert, adapter+1) key) in LDS; tk, scr and itemOff are LDS
-// scratch.  Run by one whole workgroup.
+// (pairs per (expert, adapter+1) key, overwritten here with each key's first
+// row) in LDS; tk, scr and itemOff are LDS scratch.  Run by one whole
+// workgroup.
 __device__ void align_finish(const AlignParams &p, const int *offE, const int *totE, int *tk, int *scr,
-                             const int *cnt2, int *itemOff, int npp, int *cst) {
+                             int *cnt2, int *itemOff, int npp, int *cst) {
     const int NW = (int)(blockDim.x >> 6);
     const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -318,24 +325,36 @@ __device__ void align_finish(const AlignParams &p, const int *offE, const int *t
         }
         __syncthreads();
         nitems = block_excl_scan(itemOff, NK, scr);
+        // the key counts become each key's first row: its expert's offset
+        // plus the counts of the expert's earlier keys
         for (int e = tid; e < Ep; e += nt) {
             int run = offE[e];
             for (int a1 = 0; a1 < A1; ++a1) {
-                const int k = e * A1 + a1;
-                const int c = cnt2[k];
-                if (a1 > 0) {
-                    int it = itemOff[k];
-                    for (int q = 0; q < c; q += p.lbm) {
-                        int4 v;
-                        v.x = run + q;
-                        v.y = min(p.lbm, c - q);
-                        v.z = a1 - 1;
-                        v.w = e;
-                        reinterpret_cast<int4 *>(p.items)[it++] = v;
-                    }
-                }
+                const int c = cnt2[e * A1 + a1];
+                cnt2[e * A1 + a1] = run;
                 run += c;
             }
+        }
+        __syncthreads();
+        // item i belongs to the last key k with itemOff[k] <= i (keys
+        // without items share the offset of the key after them)
+        for (int i = tid; i < nitems; i += nt) {
+            int lo = 0, hi = NK - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (itemOff[mid] <= i) lo = mid;
+                else hi = mid - 1;
+            }
+            const int k = lo, e = k / A1, a1 = k - e * A1;
+            const int first = cnt2[k];
+            const int c = (a1 + 1 < A1 ? cnt2[k + 1] : offE[e] + totE[e]) - first;
+            const int q = (i - itemOff[k]) * p.lbm;
+            int4 v;
+            v.x = first + q;
+            v.y = min(p.lbm, c - q);
+            v.z = a1 - 1;
+            v.w = e;
+            reinterpret_cast<int4 *>(p.items)[i] = v;
         }
         for (int q = nitems + tid; q < p.max_items; q += nt) {
             int4 v;
@@ -563,7 +582,14 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
     int *tk = totE + Ep;             // [TK]
     int *scr = tk + TK;              // [80]
     int *cst = scr + 80;             // [Ep+1] tile cost prefix of align_finish
-    for (int k = tid; k < NK; k += nt) cnt2[k] = p.ktot[k];
+    for (int k0 = tid; k0 < NK; k0 += 8 * nt) {  // eight loads in flight per thread (clamped: no branches)
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p.ktot[min(k0 + u * nt, NK - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u * nt < NK) cnt2[k0 + u * nt] = v[u];
+    }
     __syncthreads();
     for (int e = tid; e < Ep; e += nt) {
         int run = 0;
@@ -592,6 +618,10 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
 // in windows of kScatterWin pairs per lane whose keys are loaded up front so
 // their loads overlap.  Past the one workgroup barrier only wave 0 runs, and
 // its LDS accesses execute in program order, so no further barrier is needed.
+// Each workgroup runs this code once on a CU whose instruction cache is
+// cold, so the loads are branch-free (clamped addresses, masked values: one
+// wait for the whole batch) and the walk is a rolled loop, the window's keys
+// shifting through registers, instead of kScatterWin unrolled copies.
 constexpr int kScatterWin = 16;
 __global__ __launch_bounds__(256) void align_scatter_kernel(AlignParams p) {
     extern __shared__ int cur[];
@@ -602,8 +632,8 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(AlignParams p) {
         int v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int k = k0 + u * 256 + tid;
-            v[u] = k < NK ? p.ktot[k] + row[k] : 0;
+            const int k = min(k0 + u * 256 + tid, NK - 1);
+            v[u] = p.ktot[k] + row[k];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -615,26 +645,36 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(AlignParams p) {
     if (tid >= 64) return;
     const int f0 = blockIdx.x * p.chunk, f1 = min(p.P, f0 + p.chunk);
     for (int w0 = f0; w0 < f1; w0 += 64 * kScatterWin) {
-        int key[kScatterWin];
+        // the window's expert ids, then its adapter ids, each batch in flight at once
+        int key[kScatterWin], av[kScatterWin];
 #pragma unroll
-        for (int u = 0; u < kScatterWin; ++u) {
-            const int f = w0 + 64 * u + lane;
-            key[u] = f < f1 ? align_key_of(p, f) : -1;
+        for (int u = 0; u < kScatterWin; ++u) key[u] = p.topk_ids[min(w0 + 64 * u + lane, f1 - 1)];
+        if (p.La > 0) {
+#pragma unroll
+            for (int u = 0; u < kScatterWin; ++u) av[u] = p.adapter_ids[min(w0 + 64 * u + lane, f1 - 1) / p.Kp];
         }
 #pragma unroll
         for (int u = 0; u < kScatterWin; ++u) {
+            const int k = clamp_expert(key[u], p.Ep) * (p.La + 1) + (p.La > 0 ? adapter_key_of(av[u], p.La) : 0);
+            key[u] = w0 + 64 * u + lane < f1 ? k : -1;
+        }
+#pragma unroll 1
+        for (int u = 0; u < kScatterWin; ++u) {
             const int f = w0 + 64 * u + lane;
             if (w0 + 64 * u >= f1) break;  // uniform
-            const bool valid = key[u] >= 0;
-            const uint64_t m = match_key((uint32_t)(valid ? key[u] : 0), valid, p.nbits_k);
+            const int ku = key[0];
+#pragma unroll
+            for (int i = 0; i + 1 < kScatterWin; ++i) key[i] = key[i + 1];
+            const bool valid = ku >= 0;
+            const uint64_t m = match_key((uint32_t)(valid ? ku : 0), valid, p.nbits_k);
             const uint64_t lt = m & lanemask_lt();
             if (valid) {
-                const int pos = cur[key[u]] + __popcll(lt);
+                const int pos = cur[ku] + __popcll(lt);
                 p.sorted_ids[pos] = f;
-                if (p.sorted_adapter) p.sorted_adapter[pos] = key[u] % (p.La + 1) - 1;
+                if (p.sorted_adapter) p.sorted_adapter[pos] = ku % (p.La + 1) - 1;
             }
             __builtin_amdgcn_wave_barrier();
-            if (valid && lt == 0) cur[key[u]] += __popcll(m);
+            if (valid && lt == 0) cur[ku] += __popcll(m);
             __builtin_amdgcn_wave_barrier();
         }
     }
