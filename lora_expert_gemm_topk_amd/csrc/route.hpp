@@ -52,7 +52,6 @@ struct CandT {
     V v;
     int i;  // expert index; INT_MAX = none
 };
-typedef CandT<float> Cand;
 
 template <typename V>
 __device__ __forceinline__ bool better(const CandT<V> &a, const CandT<V> &b) {
@@ -61,16 +60,32 @@ __device__ __forceinline__ bool better(const CandT<V> &a, const CandT<V> &b) {
     return a.v > b.v || (a.v == b.v && a.i < b.i);
 }
 
-// One step of a wavefront-wide arg-max over (value, index) candidates: each
-// lane of the rows in ROW_MASK compares with the candidate DPP pattern CTRL
-// brings it (lanes without a source see "none").  The order is total, so the
+// The plain router's candidates as one 64-bit integer: the high half an
+// order-preserving key of the value (larger value, larger key; -0 taken as
+// +0 so that equal values tie), the low half the complement of the expert
+// index, so a larger integer is the better candidate under (value desc,
+// index asc) and 0 is "none" (every finite value's key is at least 2^23).
+__device__ __forceinline__ uint32_t order_key(float x) {
+    const uint32_t b = x == 0.0f ? 0u : __float_as_uint(x);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+__device__ __forceinline__ uint64_t pack_cand(float v, int e) {
+    return ((uint64_t)order_key(v) << 32) | (uint32_t)~e;
+}
+
+// One step of a wavefront-wide arg-max over packed candidates: each lane of
+// the rows in ROW_MASK compares with the candidate DPP pattern CTRL brings
+// it (lanes without a source see 0, "none").  The order is total, so the
 // winner does not depend on the pattern.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void cand_dpp_step(Cand &c) {
-    Cand o;
-    o.v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, c.v), CTRL, ROW_MASK, 0xf, false));
-    o.i = __builtin_amdgcn_update_dpp(0x7fffffff, c.i, CTRL, ROW_MASK, 0xf, false);
-    if (better(o, c)) c = o;
+__device__ __forceinline__ void cand_dpp_step(uint64_t &c) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)c, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(c >> 32), CTRL, ROW_MASK, 0xf, false);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    if (o > c) c = o;
 }
 
 // The best candidate of the wavefront, in every lane: exchanges within quads
@@ -78,17 +93,16 @@ __device__ __forceinline__ void cand_dpp_step(Cand &c) {
 // broadcasts) leave it in lane 63, which is read out.  Register-to-register
 // steps (DPP) instead of LDS-routed shuffles: the router's K rounds each run
 // one of these.
-__device__ __forceinline__ Cand wave_best(Cand c) {
+__device__ __forceinline__ uint64_t wave_best(uint64_t c) {
     cand_dpp_step<0xb1, 0xf>(c);   // quad_perm [1,0,3,2]
     cand_dpp_step<0x4e, 0xf>(c);   // quad_perm [2,3,0,1]
     cand_dpp_step<0x141, 0xf>(c);  // row_half_mirror
     cand_dpp_step<0x140, 0xf>(c);  // row_mirror
     cand_dpp_step<0x142, 0xa>(c);  // row_bcast15 into rows 1, 3
     cand_dpp_step<0x143, 0xc>(c);  // row_bcast31 into rows 2, 3
-    Cand w;
-    w.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c.v), 63));
-    w.i = __builtin_amdgcn_readlane(c.i, 63);
-    return w;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // The same arg-max for the biased router's fp64 keys, carrying the
@@ -206,24 +220,26 @@ __device__ int route_one_token(const RouteParams &rp, int t, bool write = true) 
         live[j] = e < E;
         v[j] = live[j] ? l[e] : 0.0f;
     }
+    uint64_t cand[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) cand[j] = pack_cand(v[j], lane + 64 * j);
     float myv = 0.0f;
     int myi = -1;
     for (int s = 0; s < K; ++s) {
-        Cand c{0.0f, 0x7fffffff};
+        uint64_t c = 0;
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-            Cand d{v[j], lane + 64 * j};
-            if (live[j] && better(d, c)) c = d;
-        }
+        for (int j = 0; j < VPL; ++j)
+            if (live[j] && cand[j] > c) c = cand[j];
         c = wave_best(c);  // every lane now holds the same winner
-        if ((c.i & 63) == lane) {
+        const int ci = (int)~(uint32_t)c;
+        if ((ci & 63) == lane) {
 #pragma unroll
             for (int j = 0; j < VPL; ++j)
-                if (j == (c.i >> 6)) live[j] = false;
+                if (j == (ci >> 6)) live[j] = false;
         }
         if (lane == s) {
-            myv = c.v;
-            myi = c.i;
+            myv = order_key_value((uint32_t)(c >> 32));  // a zero comes back as +0: same exp below
+            myi = ci;
         }
     }
     const double m = (double)lane_value(myv, 0);
@@ -232,7 +248,13 @@ __device__ int route_one_token(const RouteParams &rp, int t, bool write = true) 
     if (rp.renorm) {
         for (int j = 0; j < K; ++j) sum += lane_value(ex, j);
     } else {
-        for (int e = 0; e < E; ++e) sum += exp((double)l[e] - m);
+        // softmax over all E: each lane's exps of its own logits, summed in
+        // expert order
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const double xj = lane + 64 * j < E ? exp((double)v[j] - m) : 0.0;
+            for (int q = 0; q < 64 && 64 * j + q < E; ++q) sum += lane_value(xj, q);
+        }
     }
     const int Kp = K + S;
     if (write && lane < K) {
