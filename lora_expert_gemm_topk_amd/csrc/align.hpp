@@ -783,16 +783,16 @@ __global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p, RouteP
         }
         return lo;
     };
-    for (int q = tid; q < p.cap; q += nt) {
-        bool pad = q >= npp;
-        if (!pad) {
-            const int x = expert_at(q);
-            pad = q >= offE[x] + totE[x];
-        }
-        if (pad) {
+    // padding rows: each expert's [offE + totE, next offE), then the tail
+    for (int x = w; x < Ep; x += NW) {
+        for (int q = offE[x] + totE[x] + lane; q < offE[x + 1]; q += 64) {
             p.sorted_ids[q] = P;
             if (p.sorted_adapter) p.sorted_adapter[q] = -1;
         }
+    }
+    for (int q = npp + tid; q < p.cap; q += nt) {
+        p.sorted_ids[q] = P;
+        if (p.sorted_adapter) p.sorted_adapter[q] = -1;
     }
     for (int b = tid; b < p.max_blocks; b += nt) {
         const int pos = b * p.bm;
