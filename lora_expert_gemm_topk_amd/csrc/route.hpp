@@ -47,19 +47,6 @@ __device__ __forceinline__ double lane_value(double v, int j) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-template <typename V>
-struct CandT {
-    V v;
-    int i;  // expert index; INT_MAX = none
-};
-
-template <typename V>
-__device__ __forceinline__ bool better(const CandT<V> &a, const CandT<V> &b) {
-    if (b.i == 0x7fffffff) return a.i != 0x7fffffff;
-    if (a.i == 0x7fffffff) return false;
-    return a.v > b.v || (a.v == b.v && a.i < b.i);
-}
-
 // The plain router's candidates as one 64-bit integer: the high half an
 // order-preserving key of the value (larger value, larger key; -0 taken as
 // +0 so that equal values tie), the low half the complement of the expert
@@ -111,31 +98,49 @@ template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ int dpp_int(int x, int none) {
     return __builtin_amdgcn_update_dpp(none, x, CTRL, ROW_MASK, 0xf, false);
 }
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_double(double x) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = (uint32_t)dpp_int<CTRL, ROW_MASK>((int)(uint32_t)b, 0);
-    const uint32_t hi = (uint32_t)dpp_int<CTRL, ROW_MASK>((int)(uint32_t)(b >> 32), 0);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+// Candidates with fp64 keys: an order-preserving 64-bit key of the value
+// (-0 taken as +0; 0 is "none", below every finite value) and the
+// complemented expert index, compared as one 96-bit unsigned integer.
+struct Cand64 {
+    uint64_t k;
+    uint32_t i;
+};
+__device__ __forceinline__ uint64_t order_key(double x) {
+    const uint64_t b = x == 0.0 ? 0ull : __builtin_bit_cast(uint64_t, x);
+    return (b >> 63) ? ~b : (b | (1ull << 63));
 }
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void cand_dpp_step(CandT<double> &c, double &s) {
-    const CandT<double> o{dpp_double<CTRL, ROW_MASK>(c.v), dpp_int<CTRL, ROW_MASK>(c.i, 0x7fffffff)};
-    const double os = dpp_double<CTRL, ROW_MASK>(s);
-    if (better(o, c)) {
-        c = o;
-        s = os;
-    }
+__device__ __forceinline__ void cand_dpp_step(Cand64 &c) {
+    const uint32_t klo = (uint32_t)dpp_int<CTRL, ROW_MASK>((int)(uint32_t)c.k, 0);
+    const uint32_t khi = (uint32_t)dpp_int<CTRL, ROW_MASK>((int)(uint32_t)(c.k >> 32), 0);
+    const uint32_t oi = (uint32_t)dpp_int<CTRL, ROW_MASK>((int)c.i, 0);
+    const uint64_t ok = ((uint64_t)khi << 32) | klo;
+    const bool take = ok > c.k || (ok == c.k && oi > c.i);
+    c.k = take ? ok : c.k;
+    c.i = take ? oi : c.i;
 }
-__device__ __forceinline__ CandT<double> wave_best(CandT<double> c, double &s) {
-    cand_dpp_step<0xb1, 0xf>(c, s);
-    cand_dpp_step<0x4e, 0xf>(c, s);
-    cand_dpp_step<0x141, 0xf>(c, s);
-    cand_dpp_step<0x140, 0xf>(c, s);
-    cand_dpp_step<0x142, 0xa>(c, s);
-    cand_dpp_step<0x143, 0xc>(c, s);
-    s = lane_value(s, 63);
-    return CandT<double>{lane_value(c.v, 63), __builtin_amdgcn_readlane(c.i, 63)};
+__device__ __forceinline__ Cand64 wave_best(Cand64 c) {
+    cand_dpp_step<0xb1, 0xf>(c);
+    cand_dpp_step<0x4e, 0xf>(c);
+    cand_dpp_step<0x141, 0xf>(c);
+    cand_dpp_step<0x140, 0xf>(c);
+    cand_dpp_step<0x142, 0xa>(c);
+    cand_dpp_step<0x143, 0xc>(c);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c.k, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c.k >> 32), 63);
+    return Cand64{((uint64_t)hi << 32) | lo, (uint32_t)__builtin_amdgcn_readlane((int)c.i, 63)};
+}
+
+// The largest of the wavefront's values, in every lane (a maximum is exact
+// in any order).  Lanes without a value pass -inf.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, __builtin_bit_cast(float, dpp_int<0xb1, 0xf>(__builtin_bit_cast(int, x), (int)0xff800000u)));
+    x = fmaxf(x, __builtin_bit_cast(float, dpp_int<0x4e, 0xf>(__builtin_bit_cast(int, x), (int)0xff800000u)));
+    x = fmaxf(x, __builtin_bit_cast(float, dpp_int<0x141, 0xf>(__builtin_bit_cast(int, x), (int)0xff800000u)));
+    x = fmaxf(x, __builtin_bit_cast(float, dpp_int<0x140, 0xf>(__builtin_bit_cast(int, x), (int)0xff800000u)));
+    x = fmaxf(x, __builtin_bit_cast(float, dpp_int<0x142, 0xa>(__builtin_bit_cast(int, x), (int)0xff800000u)));
+    x = fmaxf(x, __builtin_bit_cast(float, dpp_int<0x143, 0xc>(__builtin_bit_cast(int, x), (int)0xff800000u)));
+    return lane_value(x, 63);
 }
 
 // Biased router for token t (see the file comment): returns to lane j the
@@ -147,45 +152,64 @@ __device__ int route_one_token_bias(const RouteParams &rp, int t, bool write) {
     const float *l = rp.logits + (int64_t)t * E;
     double sc[VPL], key[VPL];
     bool live[VPL];
-    double m = 0.0, den = 1.0;
-    if (rp.scoring == 0) {
-        // largest logit (exact), then the index-order sum every lane takes alike
-        float mx = -__builtin_huge_valf();
-        for (int e = 0; e < E; ++e) mx = fmaxf(mx, l[e]);
-        m = (double)mx;
-        den = 0.0;
-        for (int e = 0; e < E; ++e) den += exp((double)l[e] - m);
-    }
+    float lf[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
         const int e = lane + 64 * j;
         live[j] = e < E;
-        const double lv = live[j] ? (double)l[e] : 0.0;
-        sc[j] = rp.scoring == 0 ? exp(lv - m) / den : 1.0 / (1.0 + exp(-lv));
+        lf[j] = live[j] ? l[e] : -__builtin_huge_valf();
+    }
+    if (rp.scoring == 0) {
+        // largest logit (exact), then the exps of each lane's own logits,
+        // summed in expert order
+        float mx = lf[0];
+#pragma unroll
+        for (int j = 1; j < VPL; ++j) mx = fmaxf(mx, lf[j]);
+        const double m = (double)wave_max(mx);
+        double den = 0.0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            sc[j] = live[j] ? exp((double)lf[j] - m) : 0.0;
+            for (int q = 0; q < 64 && 64 * j + q < E; ++q) den += lane_value(sc[j], q);
+        }
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) sc[j] = sc[j] / den;
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) sc[j] = 1.0 / (1.0 + exp(-(live[j] ? (double)lf[j] : 0.0)));
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int e = lane + 64 * j;
         key[j] = sc[j] + ((live[j] && rp.bias) ? (double)rp.bias[e] : 0.0);
     }
+    uint64_t kk[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) kk[j] = order_key(key[j]);
     double mys = 0.0;
     int myi = -1;
     for (int s = 0; s < K; ++s) {
-        CandT<double> c{0.0, 0x7fffffff};
-        double cs = 0.0;
+        Cand64 c{0ull, 0u};
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            CandT<double> d{key[j], lane + 64 * j};
-            if (live[j] && better(d, c)) {
-                c = d;
-                cs = sc[j];
-            }
+            const uint32_t di = ~(uint32_t)(lane + 64 * j);
+            if (live[j] && (kk[j] > c.k || (kk[j] == c.k && di > c.i))) c = Cand64{kk[j], di};
         }
-        c = wave_best(c, cs);  // every lane now holds the same winner and its score
-        if ((c.i & 63) == lane) {
+        c = wave_best(c);  // every lane now holds the same winner
+        const int ci = (int)~c.i;
+        // the winner's unbiased score, from its lane
+        double cs = 0.0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+            if (j == (ci >> 6)) cs = lane_value(sc[j], ci & 63);
+        if ((ci & 63) == lane) {
 #pragma unroll
             for (int j = 0; j < VPL; ++j)
-                if (j == (c.i >> 6)) live[j] = false;
+                if (j == (ci >> 6)) live[j] = false;
         }
         if (lane == s) {
             mys = cs;
-            myi = c.i;
+            myi = ci;
         }
     }
     double sum = 0.0;
