@@ -92,15 +92,16 @@ __device__ __forceinline__ uint64_t wave_best(uint64_t c) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// The same arg-max for the biased router's fp64 keys, carrying the
-// candidate's unbiased score `s` along.
+// DPP move of one 32-bit word (lanes without a source, or outside ROW_MASK,
+// get `none`).
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ int dpp_int(int x, int none) {
     return __builtin_amdgcn_update_dpp(none, x, CTRL, ROW_MASK, 0xf, false);
 }
-// Candidates with fp64 keys: an order-preserving 64-bit key of the value
-// (-0 taken as +0; 0 is "none", below every finite value) and the
-// complemented expert index, compared as one 96-bit unsigned integer.
+// The biased router's candidates: an order-preserving 64-bit key of its fp64
+// key (-0 taken as +0; 0 is "none", below every finite value) and the
+// complemented expert index, compared as one 96-bit unsigned integer; the
+// winner's unbiased score is read from its lane afterwards.
 struct Cand64 {
     uint64_t k;
     uint32_t i;
