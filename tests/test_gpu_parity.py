@@ -63,6 +63,23 @@ def test_route_ties_bitexact():
     assert np.array_equal(_bits(w), ow.view(np.int32))
 
 
+def test_route_signed_zero_ties_bitexact():
+    """+0 and -0 mixed inside rows (they tie and the lower index goes first),
+    two logits per lane (E = 100), with and without renormalisation."""
+    g = torch.Generator().manual_seed(17)
+    lg = torch.randint(-2, 3, (200, 100), generator=g).float() * 0.5
+    neg = torch.rand(200, 100, generator=g) < 0.5
+    lg[(lg == 0) & neg] = -0.0
+    assert bool((torch.signbit(lg) & (lg == 0)).any()) and bool((~torch.signbit(lg) & (lg == 0)).any())
+    for rn in (1, 0):
+        say("route signed zeros", rn)
+        ids, w = ml.moe_lora_route(lg.to(DEV), 7, 1, 2.5, rn)
+        torch.cuda.synchronize()
+        oids, ow = oracle.route(lg.numpy(), 7, 1, 2.5, rn)
+        assert np.array_equal(ids.cpu().numpy(), oids)
+        assert np.array_equal(_bits(w), ow.view(np.int32))
+
+
 # --------------------------------------------------------------------- align
 
 def _align_case(T, E, K, S, L, r, seed, bm=0, lbm=0, adapters="uniform_all", logits="normal", one_expert=False):

@@ -71,6 +71,25 @@ def test_route_bias_ties_bitexact():
         assert np.array_equal(_bits(w), ow.view(np.int32))
 
 
+@pytest.mark.parametrize("E", [100, 300])
+def test_route_bias_signed_zero_ties_bitexact(E):
+    """+0 and -0 mixed inside rows and in the bias (equal keys: the lower
+    index goes first), several logits per lane, both scorings."""
+    g = torch.Generator().manual_seed(E)
+    lg = torch.randint(-2, 3, (120, E), generator=g).float() * 0.5
+    lg[(lg == 0) & (torch.rand(120, E, generator=g) < 0.5)] = -0.0
+    bias = torch.randint(-1, 2, (E,), generator=g).float() * 0.25
+    bias[(bias == 0) & (torch.rand(E, generator=g) < 0.5)] = -0.0
+    for router in ("bias_sigmoid", "bias_softmax"):
+        for rn in (1, 0):
+            say("route bias signed zeros", E, router, rn)
+            ids, w = ml.moe_lora_route(lg.to(DEV), 8, 1, 2.0, rn, router=router, expert_bias=bias.to(DEV))
+            torch.cuda.synchronize()
+            oids, ow = oracle.route_bias(lg.numpy(), 8, 1, 2.0, rn, SCORING[router], bias.numpy())
+            assert np.array_equal(ids.cpu().numpy(), oids)
+            assert np.array_equal(_bits(w), ow.view(np.int32))
+
+
 FWD = [
     # streaming GEMM with the gate_up shrink in the router launch (decode form)
     dict(T=40, H=200, I=72, E=6, K=2, S=0, L=3, r=16, router="bias_sigmoid"),
