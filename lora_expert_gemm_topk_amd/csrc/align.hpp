@@ -618,10 +618,10 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
 // in windows of kScatterWin pairs per lane whose keys are loaded up front so
 // their loads overlap.  Past the one workgroup barrier only wave 0 runs, and
 // its LDS accesses execute in program order, so no further barrier is needed.
-// Each workgroup runs this code once on a CU whose instruction cache is
-// cold, so the loads are branch-free (clamped addresses, masked values: one
-// wait for the whole batch) and the walk is a rolled loop, the window's keys
-// shifting through registers, instead of kScatterWin unrolled copies.
+// The loads are branch-free (clamped addresses, masked values), so each
+// batch waits once instead of once per load, and the walk is a rolled loop
+// (the window's keys shift through registers) rather than kScatterWin
+// unrolled copies.
 constexpr int kScatterWin = 16;
 __global__ __launch_bounds__(256) void align_scatter_kernel(AlignParams p) {
     extern __shared__ int cur[];
